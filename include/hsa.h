@@ -1,0 +1,134 @@
+/*
+ * hsa.h -- C ABI of the MI355X (gfx950) Hierarchical Sparse Attention forward.
+ *
+ * The operation is the HSA step of "Every Token Counts: Generalizing 16M
+ * Ultra-Long Context in LLMs" (agent-atlas explainer, section "How It Works
+ * (Technically)", Steps 1-4, and the hsa_step sketch under "The algorithm,
+ * simplified"):
+ *
+ *   Step 1  the KV history is cut into chunks of 64 tokens; chunk i owns
+ *           tokens [64 i, 64 i + 64) and one landmark vector.
+ *   Step 2  score  s[t,i] = (q_ret[t] . landmark[i]) * ret_scale  for every chunk
+ *           that lies entirely before the query's own chunk; keep the top_k
+ *           chunks (ties go to the lower chunk index).
+ *   Step 3  for each kept chunk, softmax attention of every q head of the kv
+ *           group over the chunk's 64 keys, with query-key L2 normalisation
+ *           when HSA_FLAG_QK_L2NORM is set:  O[t,i] = softmax(qhat khat^T *
+ *           attn_scale) V[i],  xhat = x / max(||x||_2, 1e-6).
+ *   Step 4  w[t,i] = softmax of s over the kept chunks;  out[t] = sum_i w O.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout: dense row-major, no strides.  B = batch, Lq = q_len, Lkv = kv_len,
+ * Hq/Hkv = q/kv heads, G = Hq/Hkv (q head h uses kv head h/G), d = head_dim,
+ * K = top_k, Nc = floor(Lkv/64).
+ *     q_ret      [B, Lq,  Hkv, d]   dtype      retrieval query, one per kv head
+ *     landmarks  [B, Hkv, Nc,  d]   dtype      one per complete chunk
+ *     q_attn     [B, Lq,  Hq,  d]   dtype      attention query
+ *     k, v       [B, Hkv, Lkv, d]   dtype
+ *     out        [B, Lq,  Hq,  d]   dtype
+ *     topk_idx   [B, Lq,  Hkv, K]   int32      chunk indices, best first
+ *     topk_score [B, Lq,  Hkv, K]   float32    s of each kept chunk
+ * Query row r has absolute position p = q_pos0 + r; its eligible chunks are
+ * 0 .. min(floor(p/64), Nc) - 1.  Slots beyond the number of eligible chunks
+ * hold index -1 and score -inf; a row with no eligible chunk outputs 0.
+ *
+ * Ownership: every pointer is a caller-owned device pointer on the current HIP
+ * device, 16-byte aligned; outputs must not alias inputs.  The library keeps
+ * no state and allocates nothing: scratch memory is the caller's workspace
+ * (at least hsa_workspace_size() bytes, 256-byte aligned), which may be reused
+ * by calls on the same stream.  `stream` is a hipStream_t (NULL: the default
+ * stream); calls only enqueue work.  Concurrent calls on different streams need
+ * different workspaces.
+ *
+ * Errors: all argument checks run on the host before any launch.  On any error
+ * nothing is launched and no output is written.  HSA_ERR_DEVICE reports a
+ * failed launch.  Results are bit-identical from run to run (no floating-point
+ * atomics).
+ */
+#ifndef HSA_H_
+#define HSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSA_OK = 0,
+  HSA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  HSA_ERR_BAD_SHAPE = 2,           /* sizes inconsistent or out of range */
+  HSA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (d, G, K, dtype, flags) */
+  HSA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < hsa_workspace_size() */
+  HSA_ERR_DEVICE = 5,              /* a HIP launch or runtime call failed */
+  HSA_ERR_MISALIGNED = 6           /* a pointer breaks the alignment rule */
+} hsa_status_t;
+
+typedef enum { HSA_DTYPE_F32 = 0, HSA_DTYPE_BF16 = 1 } hsa_dtype_t;
+
+/* Query-key L2 normalisation of Step 3 (the paper's stability ingredient). */
+#define HSA_FLAG_QK_L2NORM 0x1u
+
+#define HSA_CHUNK_TOKENS 64 /* Step 1: fixed chunk size */
+#define HSA_MAX_TOP_K 64
+
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t q_len;       /* Lq >= 1 */
+  int64_t kv_len;      /* Lkv >= 0 */
+  int64_t q_pos0;      /* absolute position of query row 0, >= 0 */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv; G = Hq/Hkv must be 1, 2, 4, 8 or 16 */
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t top_k;       /* K: 1 .. 64 */
+  float ret_scale;     /* Step 2 scale; <= 0 means 1/sqrt(d) */
+  float attn_scale;    /* Step 3 scale; <= 0 means 1/sqrt(d) */
+  uint32_t flags;      /* HSA_FLAG_* */
+  int32_t dtype;       /* hsa_dtype_t of q_ret, landmarks, q_attn, k, v and out */
+} hsa_shape_t;
+
+/* Validates `shape` and stores in *bytes the workspace size that
+ * hsa_forward, hsa_retrieve_topk and hsa_chunk_attend_blend need for it.
+ * hsa_forward and hsa_retrieve_topk also require
+ * floor((q_pos0 + Lq - 1)/64) <= Nc: no row may need a chunk the history does
+ * not hold (HSA_ERR_BAD_SHAPE otherwise). */
+hsa_status_t hsa_workspace_size(const hsa_shape_t* shape, size_t* bytes);
+
+/* Steps 1-2 (landmark scoring, causal eligibility, top-K).
+ * Inputs q_ret, landmarks; outputs topk_idx, topk_score (both required).
+ * Ranking uses the fp32 dot product before scaling; the order is
+ * (dot product descending, chunk index ascending); -0.0 ranks equal to +0.0. */
+hsa_status_t hsa_retrieve_topk(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                               int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Steps 3-4 for a given selection (e.g. from hsa_retrieve_topk, or a caller's
+ * own ranking).  Slot k of row (b, r, g) is used when 0 <= topk_idx < Nc;
+ * other slots are skipped; a row with no used slot outputs 0.  topk_score
+ * need not be sorted.  q_pos0 is not used (no causal check on a given
+ * selection). */
+hsa_status_t hsa_chunk_attend_blend(const hsa_shape_t* shape, const void* q_attn, const void* k,
+                                    const void* v, const int32_t* topk_idx,
+                                    const float* topk_score, void* out, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/* Steps 1-4.  topk_idx / topk_score may be NULL (the selection then stays in
+ * the workspace) or receive the selection as hsa_retrieve_topk writes it. */
+hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                         const void* q_attn, const void* k, const void* v, void* out,
+                         int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Static description of a status code. */
+const char* hsa_status_string(hsa_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t hsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_H_ */

@@ -1,0 +1,138 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/hsa.h declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ultra_long_context_amd as h
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "hsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hsa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return h.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == sorted(h.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.check_output(["nm", "-D", "--defined-only", h.library_path()], text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing else of ours leaks out of the library
+    assert not {e for e in exported if e.startswith("hsa_")} - set(header_functions())
+
+
+def test_status_strings_and_version(lib):
+    for code in range(7):
+        assert lib.hsa_status_string(code)
+    assert lib.hsa_status_string(99) == b"unknown status"
+    assert lib.hsa_version() == 100
+
+
+def base(**kw):
+    d = dict(batch=1, q_len=128, kv_len=1024, q_pos0=896, n_q_heads=8, n_kv_heads=1, head_dim=128,
+             top_k=8, dtype=h.DTYPE_BF16)
+    d.update(kw)
+    return h.make_shape(**d)
+
+
+def ws_size(shape):
+    n = ctypes.c_size_t(0)
+    st = h.load_library().hsa_workspace_size(ctypes.byref(shape), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 2), (dict(q_len=0), 2), (dict(kv_len=-1), 2), (dict(q_pos0=-5), 2),
+    (dict(n_q_heads=7, n_kv_heads=2), 2), (dict(n_q_heads=3, n_kv_heads=1), 3), (dict(n_q_heads=64), 3),
+    (dict(head_dim=96), 3), (dict(top_k=0), 2), (dict(top_k=65), 3), (dict(dtype=7), 3),
+])
+def test_shape_validation(kw, status):
+    st, _ = ws_size(base(**kw))
+    assert st == status
+
+
+def test_bad_flags_and_scales():
+    s = base()
+    s.flags = 0x2
+    assert ws_size(s)[0] == 3
+    s = base()
+    s.ret_scale = float("inf")
+    assert ws_size(s)[0] == 2
+
+
+def test_workspace_size_layout():
+    st, n = ws_size(base())
+    assert st == 0 and n > 0 and n % 256 == 0
+    # decode-like shape: split scan lists + per-slot partials
+    st, n2 = ws_size(base(q_len=16, kv_len=1 << 24, q_pos0=1 << 24, top_k=32))
+    assert st == 0 and n2 > 0 and n2 % 256 == 0
+
+
+class FakeBuf:
+    """Host memory standing in for device pointers: validation never dereferences them."""
+
+    def __init__(self, nbytes=1 << 16, offset=0):
+        self.raw = ctypes.create_string_buffer(nbytes + 512)
+        a = ctypes.addressof(self.raw)
+        self.ptr = ctypes.c_void_p((a + 255) // 256 * 256 + offset)
+
+
+def call_forward(shape, *, q=None, ws_bytes=None, ws_off=0, out=None, idx="none"):
+    lib = h.load_library()
+    bufs = [FakeBuf() for _ in range(6)]
+    ws = FakeBuf(offset=ws_off)
+    p = [b.ptr for b in bufs]
+    if q is not None:
+        p[0] = q
+    if out is not None:
+        p[5] = out
+    i = s = None
+    if idx == "half":
+        i = FakeBuf().ptr
+    need = ws_size(shape)[1]
+    return lib.hsa_forward(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], p[5], i, s, ws.ptr,
+                           need if ws_bytes is None else ws_bytes, None)
+
+
+def test_forward_rejects_before_launch():
+    s = base()
+    assert call_forward(s, q=ctypes.c_void_p(0)) == 1                 # NULL input
+    assert call_forward(s, out=ctypes.c_void_p(0)) == 1               # NULL output
+    assert call_forward(s, ws_bytes=ws_size(s)[1] - 1) == 4           # workspace too small
+    assert call_forward(s, ws_off=16) == 6                            # workspace not 256-aligned
+    q = FakeBuf().ptr
+    assert call_forward(s, q=ctypes.c_void_p(q.value + 2)) == 6       # input not 16-aligned
+    assert call_forward(s, idx="half") == 1                           # idx without score
+    assert call_forward(base(q_pos0=1024 + 64)) == 2                  # rows past the history
+    assert h.load_library().hsa_forward(None, *([None] * 9), 0, None) == 1
+
+
+def test_attend_entry_ignores_positions():
+    """hsa_chunk_attend_blend takes the selection as given: row positions are not checked."""
+    s = base(q_len=5000, q_pos0=0, kv_len=128)
+    st, n = ws_size(s)
+    assert st == 0 and n > 0
+
+
+def test_torch_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        h.forward(x, torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16), x, torch.zeros(1, 1, 64, 128),
+                  torch.zeros(1, 1, 64, 128), q_pos0=0, top_k=1)

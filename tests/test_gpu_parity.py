@@ -1,0 +1,245 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances: selected chunk sets bit-exact (with the fp32 error-band rule for
+continuous scores, exact order and scores in grid mode); output max-abs error
+<= 1e-5 for fp32 inputs and <= 2e-2 for bf16 inputs (fp32 accumulation).
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from workloads import HsaConfig
+
+from hsa_check import check_output, check_selection, inputs_to_device, out_to_f64, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def hsa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ultra_long_context_amd as h
+    h.load_library()
+    return h
+
+
+def sample_rows(cfg, n, seed=0):
+    total = cfg.batch * cfg.q_len
+    if total <= n:
+        return np.arange(total)
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(total, size=n - 4, replace=False).tolist())
+    rows |= {0, total - 1, cfg.q_len - 1, min(total - 1, 64)}
+    return np.array(sorted(rows))
+
+
+def run_forward(hsa, inp, **kw):
+    import torch
+    cfg = inp.cfg
+    dev = inputs_to_device(inp)
+    print("case %s B=%d Lq=%d Lkv=%d Hq=%d Hkv=%d d=%d K=%d %s" % (
+        cfg.name, cfg.batch, cfg.q_len, cfg.kv_len, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+        cfg.top_k, cfg.dtype), flush=True)
+    out, idx, score = hsa.forward(*dev, q_pos0=cfg.q_pos0, top_k=cfg.top_k, qk_norm=cfg.qk_norm,
+                                  return_topk=True, **kw)
+    torch.cuda.synchronize()
+    return out, idx, score
+
+
+def parity(hsa, inp, rows=None, exact=False, ret_scale=None, attn_scale=None):
+    cfg = inp.cfg
+    out, idx, score = run_forward(hsa, inp, ret_scale=ret_scale, attn_scale=attn_scale)
+    rows = np.arange(cfg.batch * cfg.q_len) if rows is None else np.asarray(rows)
+    oi, os_, _, oo = oracle.forward(inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v,
+                                    q_pos0=cfg.q_pos0, top_k=cfg.top_k, qk_norm=cfg.qk_norm,
+                                    ret_scale=ret_scale, attn_scale=attn_scale, rows=rows)
+    B, Lq = cfg.batch, cfg.q_len
+    gi = idx.cpu().numpy().reshape(B * Lq, cfg.n_kv_heads, cfg.top_k)[rows]
+    gs = score.cpu().numpy().reshape(B * Lq, cfg.n_kv_heads, cfg.top_k)[rows]
+    go = out_to_f64(out).reshape(B * Lq, cfg.n_q_heads, cfg.head_dim)[rows]
+    rs = oracle.default_scale(cfg.head_dim) if ret_scale is None else ret_scale
+    rep = check_selection(inp, rows, gi, gs, oi, os_, ret_scale=rs, exact=exact)
+    err = check_output(inp, rows, go, oo, atol=TOL[cfg.dtype], rep=rep, gpu_idx=gi,
+                       qk_norm=cfg.qk_norm, attn_scale=attn_scale, ret_scale=ret_scale)
+    print("  %s  max-abs err %.3e" % (rep, err), flush=True)
+    return rep, err, (out, idx, score)
+
+
+def small(**kw):
+    base = dict(name="small", batch=1, q_len=1024, q_pos0=0, kv_len=1024, n_q_heads=8, n_kv_heads=1,
+                head_dim=128, top_k=8, dtype="bf16", noise_std=0.5, n_needles=4, seed=31)
+    base.update(kw)
+    return HsaConfig(**base)
+
+
+# ----------------------------------------------------------------------------
+# workload-shaped cases at oracle-friendly sizes
+# ----------------------------------------------------------------------------
+
+def test_tiny_fp32_full(hsa):
+    parity(hsa, W.generate(W.CONFIGS[0]))
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_tiny_fp32_seeds(hsa, seed):
+    parity(hsa, W.generate(W.CONFIGS[0], seed=seed))
+
+
+def test_tiny_grid_exact(hsa):
+    parity(hsa, W.generate(W.CONFIGS[0], mode="grid"), exact=True, ret_scale=0.125)
+
+
+def test_prefill_32k_shape_cut_to_4k(hsa):
+    cfg = W.shrink(W.CONFIGS[1], q_len=4096, kv_len=4096)
+    parity(hsa, W.generate(cfg))
+
+
+def test_prefill_grid_small_ties_exact(hsa):
+    cfg = W.shrink(W.CONFIGS[1], q_len=2048, kv_len=2048, top_k=16)
+    parity(hsa, W.generate(cfg, mode="grid_small"), exact=True, ret_scale=0.125)
+
+
+def test_prefill_128k_shape_cut(hsa):
+    cfg = W.shrink(W.CONFIGS[2], q_len=2048, kv_len=2048)
+    inp = W.generate(cfg)
+    parity(hsa, inp, rows=sample_rows(cfg, 700))
+
+
+def test_decode_shape_split_merge(hsa):
+    """Few rows over a long history: the scan splits the chunks and merges."""
+    cfg = W.shrink(W.CONFIGS[3], kv_len=1 << 20)
+    parity(hsa, W.generate(cfg))
+
+
+def test_chunked_prefill_shape_cut(hsa):
+    cfg = W.shrink(W.CONFIGS[4], q_len=512, kv_len=65536 + 512)
+    inp = W.generate(cfg)
+    parity(hsa, inp, rows=sample_rows(cfg, 300))
+
+
+# ----------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------
+
+def test_softmax_exercised_without_qk_norm(hsa):
+    cfg = small(qk_norm=False, q_len=512, kv_len=512)
+    parity(hsa, W.generate(cfg), attn_scale=0.2)
+
+
+def test_sharp_softmax_with_qk_norm(hsa):
+    parity(hsa, W.generate(small(q_len=512, kv_len=512)), attn_scale=8.0)
+
+
+@pytest.mark.parametrize("K", [1, 5, 64])
+def test_top_k_extremes(hsa, K):
+    parity(hsa, W.generate(small(top_k=K, q_len=1024, kv_len=1024 * 5, q_pos0=1024 * 4)))
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 2), (2, 2), (4, 1), (16, 1)])
+def test_group_sizes(hsa, G, Hkv):
+    parity(hsa, W.generate(small(n_q_heads=G * Hkv, n_kv_heads=Hkv, batch=2, q_len=256, kv_len=256)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_dim_64(hsa, dtype):
+    parity(hsa, W.generate(small(head_dim=64, dtype=dtype, q_len=512, kv_len=512)))
+
+
+def test_head_dim_128_fp32(hsa):
+    parity(hsa, W.generate(small(dtype="f32", q_len=512, kv_len=512)))
+
+
+def test_ragged_history_and_rows(hsa):
+    """Lkv % 64 != 0 (partial last chunk never eligible), Lq % 16 != 0."""
+    cfg = small(q_len=77, kv_len=1000 + 37, q_pos0=1000 + 37 - 77 + 10)
+    cfg = replace(cfg, q_pos0=min(cfg.q_pos0, (cfg.kv_len // 64) * 64 + 63 - 76))
+    parity(hsa, W.generate(cfg))
+
+
+def test_rows_without_chunks_output_zero(hsa):
+    cfg = small(q_len=100, kv_len=100)
+    _, _, (out, idx, _) = parity(hsa, W.generate(cfg))
+    o = out_to_f64(out)
+    assert np.all(o[0, :64] == 0.0)
+    assert np.all(idx.cpu().numpy()[0, :64] == -1)
+
+
+def test_uniform_scores_select_first_chunks(hsa):
+    cfg = small(q_len=256, kv_len=4096, q_pos0=3840, top_k=7)
+    inp = W.generate(cfg)
+    inp.q_ret[:] = 0
+    _, _, (_, idx, _) = parity(hsa, inp, exact=False)
+    assert np.all(idx.cpu().numpy()[..., :] == np.arange(7))
+
+
+def test_negative_zero_ties(hsa):
+    cfg = small(q_len=64, kv_len=1024, q_pos0=960, top_k=6, dtype="f32")
+    inp = W.generate(cfg)
+    inp.q_ret[:] = 0.0
+    inp.landmarks[:, :, ::2] = -np.abs(inp.landmarks[:, :, ::2]) - 1
+    _, _, (_, idx, score) = parity(hsa, inp)
+    assert np.all(idx.cpu().numpy() == np.arange(6))
+    assert np.all(score.cpu().numpy() == 0.0)
+
+
+def test_buffer_compaction_many_candidates(hsa):
+    """K = 64 with few groups per lane forces the candidate buffer to be cut back."""
+    cfg = small(q_len=64, kv_len=65536, q_pos0=65536 - 64, top_k=64)
+    parity(hsa, W.generate(cfg, mode="grid_small"), exact=True, ret_scale=0.125)
+
+
+def test_deterministic(hsa):
+    import torch
+    inp = W.generate(W.shrink(W.CONFIGS[3], kv_len=1 << 18))
+    a = run_forward(hsa, inp)
+    b = run_forward(hsa, inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# ----------------------------------------------------------------------------
+# the two halves through their own entry points
+# ----------------------------------------------------------------------------
+
+def test_retrieve_topk_entry(hsa):
+    cfg = W.shrink(W.CONFIGS[1], q_len=1024, kv_len=1024)
+    inp = W.generate(cfg)
+    q, lm = (to_device(a, cfg.dtype) for a in (inp.q_ret, inp.landmarks))
+    idx, score = hsa.retrieve_topk(q, lm, q_pos0=0, top_k=cfg.top_k)
+    oi, os_, _, _ = oracle.forward(inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v, q_pos0=0,
+                                   top_k=cfg.top_k, with_output=False)
+    rows = np.arange(cfg.q_len)
+    check_selection(inp, rows, idx.cpu().numpy().reshape(-1, 1, cfg.top_k),
+                    score.cpu().numpy().reshape(-1, 1, cfg.top_k), oi, os_,
+                    ret_scale=oracle.default_scale(128))
+
+
+def test_chunk_attend_blend_entry_with_given_selection(hsa):
+    """Oracle indices fed in, unsorted scores, unused (-1) and out-of-range slots."""
+    cfg = small(q_len=300, kv_len=2048, q_pos0=1748, top_k=6, n_kv_heads=2, n_q_heads=8)
+    inp = W.generate(cfg)
+    oi, os_, _, _ = oracle.forward(inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v,
+                                   q_pos0=cfg.q_pos0, top_k=cfg.top_k, with_output=False)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(cfg.top_k)
+    sel = oi[:, :, perm].copy()
+    sc = os_[:, :, perm].copy()
+    sel[::7, :, 2] = -1
+    sel[::11, 1, 0] = 10 ** 6          # outside [0, Nc): skipped
+    sel[5] = -1                        # a row with nothing selected -> 0
+    w, ref = oracle.attend_blend(inp.q_attn, inp.k, inp.v, sel, sc)
+    qa, k, v = (to_device(a, cfg.dtype) for a in (inp.q_attn, inp.k, inp.v))
+    import torch
+    ti = torch.from_numpy(sel.reshape(1, cfg.q_len, 2, cfg.top_k)).cuda()
+    ts = torch.from_numpy(sc.reshape(1, cfg.q_len, 2, cfg.top_k).astype(np.float32)).cuda()
+    out = hsa.chunk_attend_blend(qa, k, v, ti, ts)
+    got = out_to_f64(out).reshape(cfg.q_len, cfg.n_q_heads, cfg.head_dim)
+    assert np.abs(got - ref).max() <= TOL["bf16"]
+    assert np.all(got[5] == 0)

@@ -1,0 +1,243 @@
+// hsa_api.hip -- C ABI of the HSA forward (see include/hsa.h): argument checks,
+// work planning, workspace layout and kernel launch order.
+#include <cmath>
+#include <cstdint>
+
+#include "hsa.h"
+#include "hsa_internal.h"
+
+#define HSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace hsa {
+namespace {
+
+constexpr int64_t kRowsPerWave = 16;
+constexpr int64_t kTargetWaves = 2048;  // ~8 waves per CU on 256 CUs
+constexpr int64_t kMinSplitChunks = 512;
+constexpr int64_t kMaxSplits = 1024;
+
+struct Plan {
+  int64_t B, Lq, q_pos0, Lkv, Nc;
+  int32_t Hq, Hkv, G, D, K;
+  bool bf16, qk_norm;
+  float ret_scale, attn_scale;
+  int64_t rows;          // B * Lq * Hkv selection rows
+  int32_t n_max;         // max eligible chunks over all query rows
+  int32_t split_len, n_splits;
+  int32_t attn_splits, slots_per_split;
+  size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a >= 0 && b >= 0 && (b == 0 || a <= limit / b); }
+
+// check_positions: reject rows whose eligible chunks would reach past the
+// history (not needed when the caller supplies the selection).
+hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
+  if (!s) return HSA_ERR_NULL_POINTER;
+  if (s->batch < 1 || s->q_len < 1 || s->kv_len < 0 || s->q_pos0 < 0 || s->n_q_heads < 1 ||
+      s->n_kv_heads < 1 || s->top_k < 1)
+    return HSA_ERR_BAD_SHAPE;
+  if (s->n_q_heads % s->n_kv_heads) return HSA_ERR_BAD_SHAPE;
+  const int32_t G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return HSA_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return HSA_ERR_UNSUPPORTED;
+  if (s->top_k > HSA_MAX_TOP_K) return HSA_ERR_UNSUPPORTED;
+  if (s->dtype != HSA_DTYPE_F32 && s->dtype != HSA_DTYPE_BF16) return HSA_ERR_UNSUPPORTED;
+  if (s->flags & ~HSA_FLAG_QK_L2NORM) return HSA_ERR_UNSUPPORTED;
+  if (!(std::isfinite(s->ret_scale) && std::isfinite(s->attn_scale))) return HSA_ERR_BAD_SHAPE;
+
+  const int64_t lim = INT64_C(1) << 60;
+  const int64_t Nc = s->kv_len / HSA_CHUNK_TOKENS;
+  if (Nc > INT32_MAX - 1) return HSA_ERR_BAD_SHAPE;
+  if (s->q_pos0 > lim - s->q_len) return HSA_ERR_BAD_SHAPE;
+  const int64_t last_pos = s->q_pos0 + s->q_len - 1;
+  if (check_positions && last_pos / HSA_CHUNK_TOKENS > Nc) return HSA_ERR_BAD_SHAPE;
+  if (!mul_ok(s->batch, s->q_len, lim) || !mul_ok((int64_t)s->batch * s->q_len, s->n_q_heads, lim) ||
+      !mul_ok((int64_t)s->batch * s->q_len * s->n_q_heads, s->head_dim, lim) ||
+      !mul_ok((int64_t)s->batch * s->n_kv_heads, s->kv_len, lim) ||
+      !mul_ok((int64_t)s->batch * s->n_kv_heads * s->kv_len, s->head_dim, lim))
+    return HSA_ERR_BAD_SHAPE;
+
+  p->B = s->batch; p->Lq = s->q_len; p->q_pos0 = s->q_pos0; p->Lkv = s->kv_len; p->Nc = Nc;
+  p->Hq = s->n_q_heads; p->Hkv = s->n_kv_heads; p->G = G; p->D = s->head_dim; p->K = s->top_k;
+  p->bf16 = s->dtype == HSA_DTYPE_BF16;
+  p->qk_norm = (s->flags & HSA_FLAG_QK_L2NORM) != 0;
+  const float dflt = 1.0f / std::sqrt((float)s->head_dim);
+  p->ret_scale = s->ret_scale > 0.f ? s->ret_scale : dflt;
+  p->attn_scale = s->attn_scale > 0.f ? s->attn_scale : dflt;
+  p->rows = (int64_t)s->batch * s->q_len * s->n_kv_heads;
+  if (p->rows > INT32_MAX) return HSA_ERR_BAD_SHAPE;  // one grid row per selection row
+
+  const int64_t nmax = std::min<int64_t>(last_pos / HSA_CHUNK_TOKENS, Nc);
+  p->n_max = (int32_t)nmax;
+  // Split long chunk ranges over several waves when there are few query rows.
+  const int64_t waves = (s->q_len + kRowsPerWave - 1) / kRowsPerWave * s->batch * s->n_kv_heads;
+  if (waves > INT32_MAX) return HSA_ERR_BAD_SHAPE;
+  int64_t splits = 1;
+  if (nmax > 0) {
+    const int64_t want = (kTargetWaves + waves - 1) / waves;
+    const int64_t most = std::max<int64_t>(1, (nmax + kMinSplitChunks - 1) / kMinSplitChunks);
+    splits = std::min<int64_t>(std::min(want, most), kMaxSplits);
+    if (splits < 1) splits = 1;
+  }
+  int64_t slen = nmax > 0 ? (nmax + splits - 1) / splits : 64;
+  slen = (slen + 63) / 64 * 64;
+  splits = nmax > 0 ? (nmax + slen - 1) / slen : 1;
+  p->split_len = (int32_t)slen;
+  p->n_splits = (int32_t)splits;
+
+  // Spread a row's slots over several waves when there are few rows.
+  int64_t as = 1;
+  if (p->rows < 1024) as = std::min<int64_t>(p->K, (kTargetWaves + p->rows - 1) / p->rows);
+  int64_t sps = (p->K + as - 1) / as;
+  as = (p->K + sps - 1) / sps;
+  p->attn_splits = (int32_t)as;
+  p->slots_per_split = (int32_t)sps;
+
+  size_t off = 0;
+  p->off_idx = off; off = align_up(off + (size_t)p->rows * p->K * 4, 256);
+  p->off_score = off; off = align_up(off + (size_t)p->rows * p->K * 4, 256);
+  p->off_lists = off;
+  if (p->n_splits > 1) off = align_up(off + (size_t)p->rows * p->n_splits * p->K * 8, 256);
+  p->off_partials = off;
+  if (p->attn_splits > 1) off = align_up(off + (size_t)p->rows * p->attn_splits * G * p->D * 4, 256);
+  p->off_counters = off;
+  if (p->attn_splits > 1) off = align_up(off + (size_t)p->rows * 4, 256);
+  p->total = off;
+  return HSA_OK;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+hsa_status_t check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return HSA_ERR_NULL_POINTER;
+  if (!aligned(ws, 256)) return HSA_ERR_MISALIGNED;
+  if (ws_bytes < p.total) return HSA_ERR_WORKSPACE_TOO_SMALL;
+  return HSA_OK;
+}
+
+hsa_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if (!q) return HSA_ERR_NULL_POINTER;
+  for (const void* q : ptrs)
+    if (!aligned(q, 16)) return HSA_ERR_MISALIGNED;
+  return HSA_OK;
+}
+
+hsa_status_t launch_retrieve(const Plan& p, const void* q_ret, const void* landmarks,
+                             int32_t* idx, float* score, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  ScanArgs a;
+  a.q_ret = q_ret; a.landmarks = landmarks; a.out_idx = idx; a.out_score = score;
+  a.lists = reinterpret_cast<uint64_t*>(w + p.off_lists);
+  a.Lq = p.Lq; a.q_pos0 = p.q_pos0; a.Nc = p.Nc; a.Hkv = p.Hkv; a.K = p.K;
+  a.n_max = p.n_max; a.split_len = p.split_len; a.n_splits = p.n_splits; a.ret_scale = p.ret_scale;
+  if (launch_scan(a, p.B, p.bf16, p.D, st) != hipSuccess) return HSA_ERR_DEVICE;
+  if (p.n_splits > 1) {
+    MergeArgs m;
+    m.lists = a.lists; m.out_idx = idx; m.out_score = score; m.rows = p.rows;
+    m.n_splits = p.n_splits; m.K = p.K; m.ret_scale = p.ret_scale;
+    if (launch_merge(m, st) != hipSuccess) return HSA_ERR_DEVICE;
+  }
+  return HSA_OK;
+}
+
+hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* k, const void* v,
+                                 const int32_t* idx, const float* score, void* out, void* ws,
+                                 hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  AttendArgs a;
+  a.q_attn = q_attn; a.k = k; a.v = v; a.idx = idx; a.score = score; a.out = out;
+  a.partials = reinterpret_cast<float*>(w + p.off_partials);
+  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters);
+  a.Lq = p.Lq; a.Lkv = p.Lkv; a.Nc = p.Nc; a.Hq = p.Hq; a.Hkv = p.Hkv; a.K = p.K;
+  a.n_splits = p.attn_splits; a.slots_per_split = p.slots_per_split;
+  a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0;
+  if (p.attn_splits > 1 && launch_fill_u32(a.counters, p.rows, 0u, st) != hipSuccess)
+    return HSA_ERR_DEVICE;
+  if (launch_attend(a, p.B, p.bf16, p.D, p.G, st) != hipSuccess) return HSA_ERR_DEVICE;
+  return HSA_OK;
+}
+
+}  // namespace
+}  // namespace hsa
+
+using hsa::Plan;
+
+HSA_EXPORT hsa_status_t hsa_workspace_size(const hsa_shape_t* shape, size_t* bytes) {
+  if (!bytes) return HSA_ERR_NULL_POINTER;
+  Plan p;
+  const hsa_status_t st = hsa::make_plan(shape, &p, false);
+  if (st != HSA_OK) return st;
+  *bytes = p.total;
+  return HSA_OK;
+}
+
+HSA_EXPORT hsa_status_t hsa_retrieve_topk(const hsa_shape_t* shape, const void* q_ret,
+                                          const void* landmarks, int32_t* topk_idx,
+                                          float* topk_score, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  Plan p;
+  hsa_status_t st = hsa::make_plan(shape, &p, true);
+  if (st != HSA_OK) return st;
+  const void* lm = p.Nc > 0 ? landmarks : q_ret;  // landmarks may be empty when Nc == 0
+  if ((st = hsa::check_ptrs({q_ret, lm, topk_idx, topk_score})) != HSA_OK) return st;
+  if ((st = hsa::check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
+  return hsa::launch_retrieve(p, q_ret, landmarks, topk_idx, topk_score, ws,
+                              static_cast<hipStream_t>(stream));
+}
+
+HSA_EXPORT hsa_status_t hsa_chunk_attend_blend(const hsa_shape_t* shape, const void* q_attn,
+                                               const void* k, const void* v,
+                                               const int32_t* topk_idx, const float* topk_score,
+                                               void* out, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  Plan p;
+  hsa_status_t st = hsa::make_plan(shape, &p, false);
+  if (st != HSA_OK) return st;
+  const void* kk = p.Lkv > 0 ? k : q_attn;
+  const void* vv = p.Lkv > 0 ? v : q_attn;
+  if ((st = hsa::check_ptrs({q_attn, kk, vv, topk_idx, topk_score, out})) != HSA_OK) return st;
+  if ((st = hsa::check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
+  return hsa::launch_attend_blend(p, q_attn, k, v, topk_idx, topk_score, out, ws,
+                                  static_cast<hipStream_t>(stream));
+}
+
+HSA_EXPORT hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret,
+                                    const void* landmarks, const void* q_attn, const void* k,
+                                    const void* v, void* out, int32_t* topk_idx,
+                                    float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  hsa_status_t st = hsa::make_plan(shape, &p, true);
+  if (st != HSA_OK) return st;
+  const void* lm = p.Nc > 0 ? landmarks : q_ret;
+  const void* kk = p.Lkv > 0 ? k : q_attn;
+  const void* vv = p.Lkv > 0 ? v : q_attn;
+  if ((st = hsa::check_ptrs({q_ret, lm, q_attn, kk, vv, out})) != HSA_OK) return st;
+  if ((topk_idx == nullptr) != (topk_score == nullptr)) return HSA_ERR_NULL_POINTER;
+  if (topk_idx && (st = hsa::check_ptrs({topk_idx, topk_score})) != HSA_OK) return st;
+  if ((st = hsa::check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
+  char* w = static_cast<char*>(ws);
+  int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + p.off_idx);
+  float* score = topk_score ? topk_score : reinterpret_cast<float*>(w + p.off_score);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hsa::launch_retrieve(p, q_ret, landmarks, idx, score, ws, s)) != HSA_OK) return st;
+  return hsa::launch_attend_blend(p, q_attn, k, v, idx, score, out, ws, s);
+}
+
+HSA_EXPORT const char* hsa_status_string(hsa_status_t status) {
+  switch (status) {
+    case HSA_OK: return "success";
+    case HSA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case HSA_ERR_BAD_SHAPE: return "inconsistent or out-of-range shape";
+    case HSA_ERR_UNSUPPORTED: return "unsupported head_dim, group size, top_k, dtype or flag";
+    case HSA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than hsa_workspace_size()";
+    case HSA_ERR_DEVICE: return "HIP launch or runtime error";
+    case HSA_ERR_MISALIGNED: return "pointer not 16-byte aligned (workspace: 256-byte)";
+  }
+  return "unknown status";
+}
+
+HSA_EXPORT int32_t hsa_version(void) { return 100; }
