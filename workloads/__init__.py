@@ -11,8 +11,8 @@ Generalizing 16M Ultra-Long Context in LLMs", agent-atlas explainer, section
 contexts out to 16M tokens).
 
 Recipe (all five workloads):
-  * q_ret, q_attn, K, V: i.i.d. N(0,1) drawn in fp64, rounded to fp32 (RNE) and,
-    for bf16 workloads, to bf16 (RNE).  Stored arrays hold the dtype's bits
+  * q_ret, q_attn, K, V: i.i.d. N(0,1) drawn in fp32 (numpy's float32 sampler)
+    and, for bf16 workloads, rounded to bf16 (RNE).  Stored arrays hold the dtype's bits
     (``float32`` or ``uint16`` for bf16).
   * landmark of chunk i = fp64 mean of the chunk's 64 *stored* keys, plus
     optional N(0, noise_std) noise, plus needle boosts, then rounded like the
@@ -23,8 +23,8 @@ Recipe (all five workloads):
     l_n += b * sigma_l * q_ret[o] / ||q_ret[o]||, in every kv head with that
     head's q_ret.
   * RNG: numpy Generator(PCG64(SeedSequence([seed, tensor_id, block]))), with
-    token blocks of 65,536 so any block of a 16M-token history can be drawn on
-    its own.  tensor ids: 0 q_ret, 1 q_attn, 2 K, 3 V, 4 landmark noise,
+    blocks of 2^23 elements of each flattened tensor, so any block of a
+    16M-token history can be drawn on its own.  tensor ids: 0 q_ret, 1 q_attn, 2 K, 3 V, 4 landmark noise,
     5 needles.
 """
 from __future__ import annotations
@@ -38,6 +38,7 @@ import numpy as np
 
 CHUNK = 64
 BLOCK_TOKENS = 65536
+BLOCK_ELEMS = 1 << 23
 
 T_QRET, T_QATTN, T_K, T_V, T_NOISE, T_NEEDLE = range(6)
 
@@ -100,9 +101,13 @@ def config(i: int, **overrides) -> HsaConfig:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (round to nearest, ties to even); return uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    u += t
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -143,22 +148,24 @@ def _threads() -> int:
 
 
 def _normal_rows(seed: int, tensor_id: int, n_rows: int, row_len: int, dtype: str) -> np.ndarray:
-    """[n_rows, row_len] stored N(0,1) values, drawn in blocks of BLOCK_TOKENS rows."""
-    out = np.empty((n_rows, row_len), dtype=storage_dtype(dtype))
-    n_blocks = (n_rows + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+    """[n_rows, row_len] stored N(0,1) values, drawn in blocks of BLOCK_ELEMS elements of the
+    flattened array (block b covers elements [b*BLOCK_ELEMS, (b+1)*BLOCK_ELEMS))."""
+    out = np.empty(n_rows * row_len, dtype=storage_dtype(dtype))
+    n = out.size
+    n_blocks = (n + BLOCK_ELEMS - 1) // BLOCK_ELEMS
 
     def work(blk):
-        lo = blk * BLOCK_TOKENS
-        hi = min(n_rows, lo + BLOCK_TOKENS)
-        x = _rng(seed, tensor_id, blk).standard_normal((hi - lo, row_len))
-        out[lo:hi] = store(x, dtype)
+        lo = blk * BLOCK_ELEMS
+        hi = min(n, lo + BLOCK_ELEMS)
+        x = _rng(seed, tensor_id, blk).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = x if dtype == "f32" else f32_to_bf16_bits(x)
 
     if n_blocks == 1:
         work(0)
     else:
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(work, range(n_blocks)))
-    return out
+    return out.reshape(n_rows, row_len)
 
 
 def _grid_rows(seed: int, tensor_id: int, n_rows: int, row_len: int, dtype: str,
