@@ -8,7 +8,7 @@ Workloads (synthetic, seeded; shapes of the paper's setting):
 
 A step is one hsa_forward call (landmark scan, top-K, per-chunk attention, blend)
 over the whole batch, inputs resident in HBM.  Each step is preceded, outside its
-HIP-event window, by a 1 GiB write that evicts L2 and the 256 MB Infinity Cache,
+HIP-event window, by a 1 GiB read that evicts L2 and the 256 MB Infinity Cache,
 so every step starts cold.  ms_per_step is the mean event-timed step; the wall
 time of the whole timed region (flushes included) is reported as wall_ms_per_step.
 
@@ -51,27 +51,59 @@ def to_dev(a, dtype):
 
 
 class Timer:
-    """HIP events on torch's current stream (the stream the library launches on)."""
+    """Cold-cache timing of a captured HIP graph with HIP events.
+
+    Each step enqueues a 1 GiB read of an unrelated buffer (evicting L2 and the
+    256 MB Infinity Cache with clean lines; a write would leave dirty lines whose
+    write-back competes with the timed step), then event e0, the graph replay,
+    event e1.  The read keeps the GPU busy while the host enqueues e0 and the
+    replay, so the events bracket GPU work only.  Events live on torch's current
+    stream, which is the stream the library launches on."""
 
     def __init__(self):
         import torch
         self.torch = torch
-        self.flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        self.flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda:0")
+        self.pool = []
 
     def cold(self):
-        self.flush.fill_(1)
+        self.torch.sum(self.flush, dim=0, out=self.sink)
 
-    def time(self, fn, steps, flush=True):
+    def events(self, n):
         torch = self.torch
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
+        while len(self.pool) < n:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            self.pool.append((e0, e1))
+        torch.cuda.synchronize()
+        return self.pool[:n]
+
+    def capture(self, fn):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time(self, graph, steps, flush=True):
+        torch = self.torch
+        evs = self.events(steps)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e0, e1 in evs:
             if flush:
                 self.cold()
             e0.record()
-            fn()
+            graph.replay()
             e1.record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
@@ -130,10 +162,16 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log("[bench] %s: warmup done" % name)
-    ms_mean, ms_med, wall_ms = timer.time(step, steps)
-    log("[bench] %s: %.3f ms/step (median %.3f, wall incl. flush %.3f)" % (name, ms_mean, ms_med, wall_ms))
-    warm_mean, _, _ = timer.time(step, steps, flush=False)
+    eager = out.clone()
+    g_step = timer.capture(step)
+    g_step.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, eager):
+        raise RuntimeError("graph replay differs from the eager forward")
+    log("[bench] %s: warmup done, graph replay matches eager" % name)
+    ms_mean, ms_med, wall_ms = timer.time(g_step, steps)
+    log("[bench] %s: %.4f ms/step (median %.4f, wall incl. flush %.3f)" % (name, ms_mean, ms_med, wall_ms))
+    warm_mean, _, _ = timer.time(g_step, steps, flush=False)
 
     # dominant-kernel timing through the two halves of the C ABI
     sel_out = hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=cfg.q_pos0, top_k=cfg.top_k,
@@ -142,16 +180,23 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     score.copy_(sel_out[2])
     U = distinct_chunks(idx, cfg)
     alg = algorithmic(cfg, U)
+    sel_i = torch.empty_like(idx)
+    sel_s = torch.empty_like(score)
+    ws = hsa.new_workspace(hsa.workspace_size(hsa.make_shape(
+        batch=cfg.batch, q_len=cfg.q_len, kv_len=cfg.kv_len, q_pos0=cfg.q_pos0,
+        n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, top_k=cfg.top_k,
+        dtype=hsa.DTYPE_BF16)), "cuda:0")
 
     def retrieve():
-        hsa.retrieve_topk(q_ret, lm, q_pos0=cfg.q_pos0, top_k=cfg.top_k, kv_len=cfg.kv_len)
+        hsa.retrieve_topk(q_ret, lm, q_pos0=cfg.q_pos0, top_k=cfg.top_k, kv_len=cfg.kv_len,
+                          out=(sel_i, sel_s), workspace=ws)
 
     def attend():
-        hsa.chunk_attend_blend(q_attn, k, v, idx, score, out=out)
+        hsa.chunk_attend_blend(q_attn, k, v, idx, score, out=out, workspace=ws)
 
-    r_ms, _, _ = timer.time(retrieve, steps)
-    a_ms, _, _ = timer.time(attend, steps)
-    log("[bench] %s: retrieve %.3f ms, attend %.3f ms, U=%d" % (name, r_ms, a_ms, U))
+    r_ms, _, _ = timer.time(timer.capture(retrieve), steps)
+    a_ms, _, _ = timer.time(timer.capture(attend), steps)
+    log("[bench] %s: retrieve %.4f ms, attend %.4f ms, U=%d" % (name, r_ms, a_ms, U))
 
     qtok = cfg.batch * cfg.q_len
     res = dict(workload=name, config=cfg, value=qtok / (ms_mean / 1e3), ms_per_step=ms_mean,
@@ -161,7 +206,7 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
         # landmark stream: every landmark and query read once per launch
         nbytes = alg["landmark_bytes"] + alg["q_ret_bytes"]
         gbs = nbytes / (r_ms / 1e3) / 1e9
-        res["roofline"] = dict(bound="hbm", kernel="retrieve (scan_topk + merge_topk)",
+        res["roofline"] = dict(bound="hbm", kernel="scan_wide_kernel (landmark scan, top-K, merge)",
                                achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
                                traffic=None, alg_bytes_per_launch=nbytes)
         res["hbm_frac_whole_step"] = (alg["bytes"] / 8e12) / (ms_mean / 1e3)

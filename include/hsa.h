@@ -37,9 +37,11 @@
  * device, 16-byte aligned; outputs must not alias inputs.  The library keeps
  * no state and allocates nothing: scratch memory is the caller's workspace
  * (at least hsa_workspace_size() bytes, 256-byte aligned), which may be reused
- * by calls on the same stream.  `stream` is a hipStream_t (NULL: the default
- * stream); calls only enqueue work.  Concurrent calls on different streams need
- * different workspaces.
+ * by calls on the same stream, for any shape.  Its first 16 KiB hold arrival
+ * counters that must be zero when a call starts: zero them once after
+ * allocating (hsa_workspace_init); every completed call leaves them zero.
+ * `stream` is a hipStream_t (NULL: the default stream); calls only enqueue
+ * work.  Concurrent calls on different streams need different workspaces.
  *
  * Errors: all argument checks run on the host before any launch.  On any error
  * nothing is launched and no output is written.  HSA_ERR_DEVICE reports a
@@ -95,6 +97,10 @@ typedef struct {
  * floor((q_pos0 + Lq - 1)/64) <= Nc: no row may need a chunk the history does
  * not hold (HSA_ERR_BAD_SHAPE otherwise). */
 hsa_status_t hsa_workspace_size(const hsa_shape_t* shape, size_t* bytes);
+
+/* Enqueues the zeroing of the workspace's counter region (its first 16 KiB) on
+ * `stream`.  Call once per newly allocated workspace; ws_bytes >= 16384. */
+hsa_status_t hsa_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Steps 1-2 (landmark scoring, causal eligibility, top-K).
  * Inputs q_ret, landmarks; outputs topk_idx, topk_score (both required).

@@ -123,6 +123,14 @@ def test_forward_rejects_before_launch():
     assert h.load_library().hsa_forward(None, *([None] * 9), 0, None) == 1
 
 
+def test_workspace_init_checks_arguments():
+    lib = h.load_library()
+    assert lib.hsa_workspace_init(None, 1 << 20, None) == 1
+    buf = FakeBuf()
+    assert lib.hsa_workspace_init(ctypes.c_void_p(buf.ptr.value + 16), 1 << 20, None) == 6
+    assert lib.hsa_workspace_init(buf.ptr, 1000, None) == 4
+
+
 def test_attend_entry_ignores_positions():
     """hsa_chunk_attend_blend takes the selection as given: row positions are not checked."""
     s = base(q_len=5000, q_pos0=0, kv_len=128)

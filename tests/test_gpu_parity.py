@@ -243,3 +243,29 @@ def test_chunk_attend_blend_entry_with_given_selection(hsa):
     got = out_to_f64(out).reshape(cfg.q_len, cfg.n_q_heads, cfg.head_dim)
     assert np.abs(got - ref).max() <= TOL["bf16"]
     assert np.all(got[5] == 0)
+
+
+def test_many_row_blocks_one_wave_scan(hsa):
+    """More than 2048 blocks of 16 rows: the one-wave-per-16-rows scan path."""
+    cfg = small(batch=1, n_kv_heads=4, n_q_heads=8, q_len=8256, kv_len=8256, top_k=8, head_dim=64)
+    inp = W.generate(cfg)
+    parity(hsa, inp, rows=sample_rows(cfg, 400))
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes, in the launch configuration bench.py times; the oracle
+# checks sampled rows (all 16 rows for the decode workload)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i,n_rows", [(1, 300), (2, 120), (3, 16), (4, 120)])
+def test_full_size_workloads_sampled(hsa, i, n_rows):
+    cfg = W.CONFIGS[i]
+    inp = W.generate(cfg)
+    parity(hsa, inp, rows=sample_rows(cfg, n_rows, seed=i))
+
+
+def test_one_wave_scan_buffer_compaction(hsa):
+    """One-wave scan path with K = 64 and heavy ties: the LDS buffer is cut back."""
+    cfg = small(batch=2, n_kv_heads=2, n_q_heads=4, q_len=8256, kv_len=8256, top_k=64, head_dim=64)
+    inp = W.generate(cfg, mode="grid_small")
+    parity(hsa, inp, rows=sample_rows(cfg, 150), exact=True, ret_scale=0.125)

@@ -18,7 +18,7 @@ import os
 import threading
 
 __all__ = ["HsaError", "HsaShape", "forward", "retrieve_topk", "chunk_attend_blend",
-           "workspace_size", "library_path", "load_library", "EXPORTED_SYMBOLS"]
+           "workspace_size", "new_workspace", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhsa.so")
@@ -30,8 +30,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 CHUNK = 64
 MAX_TOP_K = 64
 
-EXPORTED_SYMBOLS = ("hsa_workspace_size", "hsa_retrieve_topk", "hsa_chunk_attend_blend",
-                    "hsa_forward", "hsa_status_string", "hsa_version")
+EXPORTED_SYMBOLS = ("hsa_workspace_size", "hsa_workspace_init", "hsa_retrieve_topk",
+                    "hsa_chunk_attend_blend", "hsa_forward", "hsa_status_string", "hsa_version")
 
 _STATUS = {0: "HSA_OK", 1: "HSA_ERR_NULL_POINTER", 2: "HSA_ERR_BAD_SHAPE", 3: "HSA_ERR_UNSUPPORTED",
            4: "HSA_ERR_WORKSPACE_TOO_SMALL", 5: "HSA_ERR_DEVICE", 6: "HSA_ERR_MISALIGNED"}
@@ -77,6 +77,8 @@ def _load():
             shp = ctypes.POINTER(HsaShape)
             lib.hsa_workspace_size.argtypes = [shp, ctypes.POINTER(sz)]
             lib.hsa_workspace_size.restype = st
+            lib.hsa_workspace_init.argtypes = [vp, sz, vp]
+            lib.hsa_workspace_init.restype = st
             lib.hsa_retrieve_topk.argtypes = [shp, vp, vp, vp, vp, vp, sz, vp]
             lib.hsa_retrieve_topk.restype = st
             lib.hsa_chunk_attend_blend.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -146,14 +148,25 @@ def _stream(device):
     return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
 
+def new_workspace(nbytes: int, device):
+    """Allocate a workspace tensor and zero its counter region (hsa_workspace_init)."""
+    ws = _torch().empty(max(int(nbytes), 16384), dtype=_torch().uint8, device=device)
+    st = _load().hsa_workspace_init(_ptr(ws), ws.numel(), _stream(device))
+    if st:
+        raise HsaError(st, "hsa_workspace_init")
+    return ws
+
+
 def _workspace(shape, device, workspace=None):
+    """The caller's workspace (which must have been initialised once), or a
+    cached one per device, grown as needed."""
     need = workspace_size(shape)
     if workspace is not None:
         return workspace, need
     key = (device.index if device.index is not None else _torch().cuda.current_device())
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = _torch().empty(max(need, 256), dtype=_torch().uint8, device=device)
+        ws = new_workspace(need, device)
         _ws_cache[key] = ws
     return ws, need
 
@@ -199,7 +212,7 @@ def forward(q_ret, landmarks, q_attn, k, v, *, q_pos0: int, top_k: int, qk_norm:
 
 
 def retrieve_topk(q_ret, landmarks, *, q_pos0: int, top_k: int, kv_len: int | None = None,
-                  ret_scale: float | None = None, workspace=None):
+                  ret_scale: float | None = None, out=None, workspace=None):
     """Steps 1-2: returns (topk_idx int32, topk_score fp32), each [B, Lq, Hkv, K]."""
     torch = _torch()
     _check(q_ret, "q_ret", 4)
@@ -215,8 +228,15 @@ def retrieve_topk(q_ret, landmarks, *, q_pos0: int, top_k: int, kv_len: int | No
                        ret_scale=ret_scale)
     dev = q_ret.device
     ws, _ = _workspace(shape, dev, workspace)
-    idx = torch.empty((B, Lq, Hkv, top_k), dtype=torch.int32, device=dev)
-    score = torch.empty((B, Lq, Hkv, top_k), dtype=torch.float32, device=dev)
+    if out is None:
+        idx = torch.empty((B, Lq, Hkv, top_k), dtype=torch.int32, device=dev)
+        score = torch.empty((B, Lq, Hkv, top_k), dtype=torch.float32, device=dev)
+    else:
+        idx, score = out
+        _check(idx, "topk_idx", 4, torch.int32)
+        _check(score, "topk_score", 4, torch.float32)
+        if tuple(idx.shape) != (B, Lq, Hkv, top_k) or score.shape != idx.shape:
+            raise ValueError("out must be (topk_idx, topk_score) of shape [B, Lq, Hkv, K]")
     st = _load().hsa_retrieve_topk(ctypes.byref(shape), _ptr(q_ret), _ptr(landmarks), _ptr(idx),
                                    _ptr(score), _ptr(ws), ws.numel(), _stream(dev))
     if st:

@@ -9,10 +9,7 @@
 // and P.V is computed with lane = output dimension.  The blend is folded into
 // the accumulation: out = sum_k (w_k * P_k) V_k.
 //
-// When a row's slots are spread over several waves (few rows, e.g. decode),
-// each wave writes its fp32 partial sum and the last wave to finish -- found
-// with a per-row arrival counter -- adds the partials in slot order, so the
-// result does not depend on timing.
+// (Few rows use attend_slot_kernel below instead.)
 #include "hsa_device.h"
 #include "hsa_internal.h"
 
@@ -48,11 +45,9 @@ __global__ __launch_bounds__(64) void attend_blend_kernel(AttendArgs a) {
   constexpr int XD = D / kWave;                 // output dims per lane
   __shared__ float qs[G][D];
   __shared__ float ps[kChunk][G];
-  __shared__ int last;
 
   const int lane = threadIdx.x;
   const int64_t row = blockIdx.x;               // (b*Lq + r)*Hkv + g
-  const int sk = blockIdx.y;
   const int g = (int)(row % a.Hkv);
   const int64_t br = row / a.Hkv;               // b*Lq + r
   const int64_t b = br / a.Lq;
@@ -90,8 +85,7 @@ __global__ __launch_bounds__(64) void attend_blend_kernel(AttendArgs a) {
 #pragma unroll
     for (int xi = 0; xi < XD; ++xi) acc[h][xi] = 0.f;
 
-  const int k_lo = sk * a.slots_per_split;
-  const int k_hi = min(K, k_lo + a.slots_per_split);
+  const int k_lo = 0, k_hi = K;
   const T* kbase = reinterpret_cast<const T*>(a.k) + (b * a.Hkv + g) * a.Lkv * D;
   const T* vbase = reinterpret_cast<const T*>(a.v) + (b * a.Hkv + g) * a.Lkv * D;
   for (int k = k_lo; k < k_hi; ++k) {
@@ -142,35 +136,195 @@ __global__ __launch_bounds__(64) void attend_blend_kernel(AttendArgs a) {
   }
 
   T* op = reinterpret_cast<T*>(a.out) + (br * a.Hq + (int64_t)g * G) * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int xi = 0; xi < XD; ++xi) E::store(op + h * D + lane + kWave * xi, acc[h][xi]);
+}
+
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(256) void attend_slot_kernel(AttendArgs a) {
+  using E = Elem<BF16>;
+  using T = typename E::T;
+  constexpr int VEC = 16 / (int)sizeof(T);             // elements per 16-byte load
+  constexpr int KROW = D + VEC;                        // padded key row in LDS
+  constexpr int NV = kChunk * D / VEC / 256;           // 16-byte loads per thread per tensor
+  constexpr int HPW = (G + 3) / 4;                     // q heads per wave
+  constexpr int XD = D / kWave;                        // output dims per lane
+  __shared__ __align__(16) T ks[kChunk * KROW];
+  __shared__ __align__(16) T vs[kChunk * D];
+  __shared__ float qs[G][D];
+  __shared__ float ps[G][kChunk];
+  __shared__ int last;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t row = blockIdx.x;
+  const int sk = blockIdx.y;
+  const int g = (int)(row % a.Hkv);
+  const int64_t br = row / a.Hkv;
+  const int64_t b = br / a.Lq;
+  const int K = a.K;
+
+  const int32_t my_idx = lane < K ? a.idx[row * K + lane] : -1;
+  const float my_s = lane < K ? a.score[row * K + lane] : 0.f;
+  const bool valid = my_idx >= 0 && (int64_t)my_idx < a.Nc;
+  const float mxs = wave_max(valid ? my_s : -INFINITY);
+  const float ex = valid ? expf(my_s - mxs) : 0.f;
+  const float den = wave_sum(ex);
+  const int c = __shfl(my_idx, sk, kWave);
+  const float wk = __shfl(valid ? ex / den : 0.f, sk, kWave);
+  const bool use = c >= 0 && (int64_t)c < a.Nc;
+
+  float acc[HPW][XD];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int xi = 0; xi < XD; ++xi) acc[hh][xi] = 0.f;
+
+  if (use) {
+    const int64_t base = ((b * a.Hkv + g) * a.Lkv + (int64_t)c * kChunk) * D;
+    const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.k) + base);
+    const uint4* vp = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.v) + base);
+    uint4 kx[NV], vx[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      kx[i] = kp[tid + 256 * i];
+      vx[i] = vp[tid + 256 * i];
+    }
+    const T* qp = reinterpret_cast<const T*>(a.q_attn) + (br * a.Hq + (int64_t)g * G) * D;
+    for (int i = tid; i < G * D; i += 256) qs[i / D][i % D] = E::load(qp + i);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = (tid + 256 * i) * VEC;
+      *reinterpret_cast<uint4*>(&ks[(e / D) * KROW + e % D]) = kx[i];
+      *reinterpret_cast<uint4*>(&vs[e]) = vx[i];
+    }
+  }
+  __syncthreads();
+  if (use) {
+    // logits of key `lane` for this wave's heads
+    float dot[HPW], rq[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      dot[hh] = 0.f;
+      const int h = w + 4 * hh;
+      float ss = 0.f;
+      if (h < G) {
+#pragma unroll
+        for (int xi = 0; xi < XD; ++xi) ss += qs[h][lane + kWave * xi] * qs[h][lane + kWave * xi];
+      }
+      ss = wave_sum(ss);
+      rq[hh] = a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
+    }
+    float kss = 0.f;
+    const T* kr = &ks[lane * KROW];
+#pragma unroll 4
+    for (int x0 = 0; x0 < D; x0 += VEC) {
+      float kv[VEC];
+      const uint4 u = *reinterpret_cast<const uint4*>(kr + x0);
+      if constexpr (BF16) {
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kv[2 * i] = __uint_as_float(wd[i] << 16);
+          kv[2 * i + 1] = __uint_as_float(wd[i] & 0xFFFF0000u);
+        }
+      } else {
+        const float4 f = __builtin_bit_cast(float4, u);
+        kv[0] = f.x; kv[1] = f.y; kv[2] = f.z; kv[3] = f.w;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        kss += kv[e] * kv[e];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+          if (w + 4 * hh < G) dot[hh] += qs[w + 4 * hh][x0 + e] * kv[e];
+      }
+    }
+    const float rk = a.qk_norm ? 1.0f / fmaxf(sqrtf(kss), 1e-6f) : 1.0f;
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = w + 4 * hh;
+      const float logit = dot[hh] * rq[hh] * rk * a.attn_scale;
+      const float m = wave_max(logit);
+      const float p = expf(logit - m);
+      const float sp = wave_sum(p);
+      if (h < G) ps[h][lane] = p / sp * wk;
+    }
+    // P.V (the wave reads back only its own heads' P)
+#pragma unroll 4
+    for (int t = 0; t < kChunk; ++t) {
+      float vv[XD];
+      if constexpr (BF16 && XD == 2) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(&vs[t * D + 2 * lane]);
+        vv[0] = __uint_as_float(u << 16);
+        vv[1] = __uint_as_float(u & 0xFFFF0000u);
+      } else {
+#pragma unroll
+        for (int xi = 0; xi < XD; ++xi) vv[xi] = E::load(&vs[t * D + XD * lane + xi]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const int h = w + 4 * hh;
+        if (h < G) {
+          const float pt = ps[h][t];
+#pragma unroll
+          for (int xi = 0; xi < XD; ++xi) acc[hh][xi] += pt * vv[xi];
+        }
+      }
+    }
+  }
+
+  T* op = reinterpret_cast<T*>(a.out) + (br * a.Hq + (int64_t)g * G) * D;
   if (a.n_splits == 1) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = w + 4 * hh;
+      if (h < G)
 #pragma unroll
-      for (int xi = 0; xi < XD; ++xi) E::store(op + h * D + lane + kWave * xi, acc[h][xi]);
+        for (int xi = 0; xi < XD; ++xi) E::store(op + h * D + XD * lane + xi, acc[hh][xi]);
+    }
     return;
   }
   float* part = a.partials + (row * a.n_splits + sk) * (int64_t)(G * D);
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = w + 4 * hh;
+    if (h < G)
 #pragma unroll
-    for (int xi = 0; xi < XD; ++xi) part[h * D + lane + kWave * xi] = acc[h][xi];
-  __threadfence();
+      for (int xi = 0; xi < XD; ++xi) publish(&part[h * D + XD * lane + xi], acc[hh][xi]);
+  }
+  wait_stores();
   __syncthreads();
-  if (lane == 0) last = atomicAdd(&a.counters[row], 1u) == (uint32_t)(a.n_splits - 1);
+  if (tid == 0) last = arrive(&a.counters[row]) == (uint32_t)(a.n_splits - 1);
   __syncthreads();
   if (!last) return;
-  __threadfence();
-  const float* base = a.partials + row * a.n_splits * (int64_t)(G * D);
+  // every thread sums its outputs over the partials; 16 partials per batch of
+  // loads, all outputs of the thread in flight together
+  const float* pb = a.partials + row * a.n_splits * (int64_t)(G * D);
+  constexpr int OPT = (G * D + 255) / 256;
+  float sum[OPT];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int u = 0; u < OPT; ++u) sum[u] = 0.f;
+  for (int p0 = 0; p0 < a.n_splits; p0 += 16) {
+    float x[16][OPT];
 #pragma unroll
-    for (int xi = 0; xi < XD; ++xi) {
-      const int o = h * D + lane + kWave * xi;
-      float s = 0.f;
-      for (int p = 0; p < a.n_splits; ++p) s += base[(int64_t)p * G * D + o];
-      E::store(op + o, s);
-    }
-  if (lane == 0) a.counters[row] = 0;
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) {
+        const int o = tid + 256 * u;
+        x[q][u] = (p0 + q < a.n_splits && o < G * D) ? fetch(&pb[(int64_t)(p0 + q) * G * D + o]) : 0.f;
+      }
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) sum[u] += x[q][u];
+  }
+#pragma unroll
+  for (int u = 0; u < OPT; ++u)
+    if (tid + 256 * u < G * D) E::store(op + tid + 256 * u, sum[u]);
+  if (tid == 0) reset_counter(&a.counters[row]);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
@@ -181,15 +335,22 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 
 template <bool BF16, int D>
 hipError_t launch_g(const AttendArgs& a, int G, dim3 grid, hipStream_t st) {
-  const dim3 block(64);
+  const bool slot = a.mode == 1;
+  const dim3 block(slot ? 256 : 64);
+#define HSA_ATTEND_CASE(GG)                                                              \
+  case GG:                                                                               \
+    if (slot) hipLaunchKernelGGL((attend_slot_kernel<BF16, D, GG>), grid, block, 0, st, a); \
+    else hipLaunchKernelGGL((attend_blend_kernel<BF16, D, GG>), grid, block, 0, st, a);     \
+    break;
   switch (G) {
-    case 1: hipLaunchKernelGGL((attend_blend_kernel<BF16, D, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attend_blend_kernel<BF16, D, 2>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((attend_blend_kernel<BF16, D, 4>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((attend_blend_kernel<BF16, D, 8>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((attend_blend_kernel<BF16, D, 16>), grid, block, 0, st, a); break;
+    HSA_ATTEND_CASE(1)
+    HSA_ATTEND_CASE(2)
+    HSA_ATTEND_CASE(4)
+    HSA_ATTEND_CASE(8)
+    HSA_ATTEND_CASE(16)
     default: return hipErrorInvalidValue;
   }
+#undef HSA_ATTEND_CASE
   return hipGetLastError();
 }
 

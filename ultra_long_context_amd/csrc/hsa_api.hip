@@ -12,9 +12,12 @@ namespace hsa {
 namespace {
 
 constexpr int64_t kRowsPerWave = 16;
-constexpr int64_t kTargetWaves = 2048;  // ~8 waves per CU on 256 CUs
-constexpr int64_t kMinSplitChunks = 512;
 constexpr int64_t kMaxSplits = 1024;
+// The workspace starts with arrival counters that every call leaves at zero.
+constexpr size_t kCounterBytes = 16384;
+constexpr int64_t kScanCounters = 2048;     // counters [0, 2048): wide-scan row blocks
+constexpr int64_t kAttendCounters = 2048;   // counters [2048, 4096): attend rows
+static_assert((kScanCounters + kAttendCounters) * 4 <= (int64_t)kCounterBytes, "counter region");
 
 struct Plan {
   int64_t B, Lq, q_pos0, Lkv, Nc;
@@ -24,7 +27,8 @@ struct Plan {
   int64_t rows;          // B * Lq * Hkv selection rows
   int32_t n_max;         // max eligible chunks over all query rows
   int32_t split_len, n_splits;
-  int32_t attn_splits, slots_per_split;
+  bool wide;             // few-row scan: 16-wave workgroups, last-arriver merge
+  int32_t attn_splits, slots_per_split, attn_mode;
   size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
 };
 
@@ -72,39 +76,37 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
 
   const int64_t nmax = std::min<int64_t>(last_pos / HSA_CHUNK_TOKENS, Nc);
   p->n_max = (int32_t)nmax;
-  // Split long chunk ranges over several waves when there are few query rows.
-  const int64_t waves = (s->q_len + kRowsPerWave - 1) / kRowsPerWave * s->batch * s->n_kv_heads;
-  if (waves > INT32_MAX) return HSA_ERR_BAD_SHAPE;
-  int64_t splits = 1;
-  if (nmax > 0) {
-    const int64_t want = (kTargetWaves + waves - 1) / waves;
-    const int64_t most = std::max<int64_t>(1, (nmax + kMinSplitChunks - 1) / kMinSplitChunks);
-    splits = std::min<int64_t>(std::min(want, most), kMaxSplits);
-    if (splits < 1) splits = 1;
+  // Scan plan.  Up to 2048 row blocks of 16 rows: the wide kernel (1024 chunks
+  // per workgroup; with several splits the last workgroup of each row block
+  // merges).  More row blocks than that: one wave per 16 rows over all chunks.
+  const int64_t row_blocks = (s->q_len + kRowsPerWave - 1) / kRowsPerWave * s->batch * s->n_kv_heads;
+  if (row_blocks > INT32_MAX) return HSA_ERR_BAD_SHAPE;
+  const int64_t wchunks = 1024;
+  const int64_t wsplits = std::max<int64_t>(1, (nmax + wchunks - 1) / wchunks);
+  p->wide = row_blocks <= kScanCounters && wsplits <= kMaxSplits;
+  p->split_len = (int32_t)(p->wide ? wchunks : std::max<int64_t>(64, (nmax + 63) / 64 * 64));
+  p->n_splits = (int32_t)(p->wide ? wsplits : 1);
+
+  // Attend plan.  Few rows: one workgroup per (row, slot), partials combined by
+  // the last slot to finish.  Many rows: one wave per row.
+  if (p->rows < 1024) {
+    p->attn_mode = 1;
+    p->attn_splits = p->K;
+    p->slots_per_split = 1;
+  } else {
+    p->attn_mode = 0;
+    p->attn_splits = 1;
+    p->slots_per_split = p->K;
   }
-  int64_t slen = nmax > 0 ? (nmax + splits - 1) / splits : 64;
-  slen = (slen + 63) / 64 * 64;
-  splits = nmax > 0 ? (nmax + slen - 1) / slen : 1;
-  p->split_len = (int32_t)slen;
-  p->n_splits = (int32_t)splits;
 
-  // Spread a row's slots over several waves when there are few rows.
-  int64_t as = 1;
-  if (p->rows < 1024) as = std::min<int64_t>(p->K, (kTargetWaves + p->rows - 1) / p->rows);
-  int64_t sps = (p->K + as - 1) / as;
-  as = (p->K + sps - 1) / sps;
-  p->attn_splits = (int32_t)as;
-  p->slots_per_split = (int32_t)sps;
-
-  size_t off = 0;
+  size_t off = kCounterBytes;
+  p->off_counters = 0;
   p->off_idx = off; off = align_up(off + (size_t)p->rows * p->K * 4, 256);
   p->off_score = off; off = align_up(off + (size_t)p->rows * p->K * 4, 256);
   p->off_lists = off;
   if (p->n_splits > 1) off = align_up(off + (size_t)p->rows * p->n_splits * p->K * 8, 256);
   p->off_partials = off;
   if (p->attn_splits > 1) off = align_up(off + (size_t)p->rows * p->attn_splits * G * p->D * 4, 256);
-  p->off_counters = off;
-  if (p->attn_splits > 1) off = align_up(off + (size_t)p->rows * 4, 256);
   p->total = off;
   return HSA_OK;
 }
@@ -132,16 +134,12 @@ hsa_status_t launch_retrieve(const Plan& p, const void* q_ret, const void* landm
   ScanArgs a;
   a.q_ret = q_ret; a.landmarks = landmarks; a.out_idx = idx; a.out_score = score;
   a.lists = reinterpret_cast<uint64_t*>(w + p.off_lists);
+  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters);
   a.Lq = p.Lq; a.q_pos0 = p.q_pos0; a.Nc = p.Nc; a.Hkv = p.Hkv; a.K = p.K;
   a.n_max = p.n_max; a.split_len = p.split_len; a.n_splits = p.n_splits; a.ret_scale = p.ret_scale;
-  if (launch_scan(a, p.B, p.bf16, p.D, st) != hipSuccess) return HSA_ERR_DEVICE;
-  if (p.n_splits > 1) {
-    MergeArgs m;
-    m.lists = a.lists; m.out_idx = idx; m.out_score = score; m.rows = p.rows;
-    m.n_splits = p.n_splits; m.K = p.K; m.ret_scale = p.ret_scale;
-    if (launch_merge(m, st) != hipSuccess) return HSA_ERR_DEVICE;
-  }
-  return HSA_OK;
+  const hipError_t e = p.wide ? launch_scan_wide(a, p.B, p.bf16, p.D, st)
+                             : launch_scan(a, p.B, p.bf16, p.D, st);
+  return e == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
 }
 
 hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* k, const void* v,
@@ -151,12 +149,10 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
   AttendArgs a;
   a.q_attn = q_attn; a.k = k; a.v = v; a.idx = idx; a.score = score; a.out = out;
   a.partials = reinterpret_cast<float*>(w + p.off_partials);
-  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters);
+  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters) + kScanCounters;
   a.Lq = p.Lq; a.Lkv = p.Lkv; a.Nc = p.Nc; a.Hq = p.Hq; a.Hkv = p.Hkv; a.K = p.K;
   a.n_splits = p.attn_splits; a.slots_per_split = p.slots_per_split;
-  a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0;
-  if (p.attn_splits > 1 && launch_fill_u32(a.counters, p.rows, 0u, st) != hipSuccess)
-    return HSA_ERR_DEVICE;
+  a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0; a.mode = p.attn_mode;
   if (launch_attend(a, p.B, p.bf16, p.D, p.G, st) != hipSuccess) return HSA_ERR_DEVICE;
   return HSA_OK;
 }
@@ -173,6 +169,15 @@ HSA_EXPORT hsa_status_t hsa_workspace_size(const hsa_shape_t* shape, size_t* byt
   if (st != HSA_OK) return st;
   *bytes = p.total;
   return HSA_OK;
+}
+
+HSA_EXPORT hsa_status_t hsa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return HSA_ERR_NULL_POINTER;
+  if (!hsa::aligned(ws, 256)) return HSA_ERR_MISALIGNED;
+  if (ws_bytes < hsa::kCounterBytes) return HSA_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = hsa::launch_fill_u32(static_cast<uint32_t*>(ws), hsa::kCounterBytes / 4, 0u,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
 }
 
 HSA_EXPORT hsa_status_t hsa_retrieve_topk(const hsa_shape_t* shape, const void* q_ret,

@@ -64,25 +64,184 @@ __device__ __forceinline__ uint32_t cand_key(uint64_t c) { return (uint32_t)(c >
 
 // ---------------------------------------------------------------------------
 // wave reductions (64 lanes)
+//
+// Within each 16-lane row, DPP butterflies (xor 1, xor 2, half-row mirror, row
+// mirror) leave the row's result in every lane; the four row results are then
+// combined with v_readlane, so nothing goes through the LDS crossbar.
 // ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x141>(v);
+  v += dpp_i<0x140>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
+// number of lanes whose predicate holds
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   uint32_t lo = __shfl((uint32_t)v, src, kWave), hi = __shfl((uint32_t)(v >> 32), src, kWave);
   return ((uint64_t)hi << 32) | lo;
+}
+
+}  // namespace hsa
+
+namespace hsa {
+
+// ---------------------------------------------------------------------------
+// hand-off between workgroups of one kernel
+//
+// The per-XCD L2 caches are not coherent with each other.  Data that another
+// workgroup reads after an arrival-counter hand-off is written and read with
+// device-scope atomic accesses (sc1: write-through / re-fetch past the L2), and
+// each thread waits for its stores to complete before the barrier that
+// precedes the counter increment.  This gives the ordering of a release /
+// acquire pair without the full L2 write-back a device-scope fence costs.
+// ---------------------------------------------------------------------------
+template <class T>
+__device__ __forceinline__ void publish(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T fetch(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every global store of this thread has completed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ uint32_t arrive(uint32_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(uint32_t* ctr) {
+  __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// wave-level selection over packed candidates held in LDS
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (1ull << (threadIdx.x & (kWave - 1))) - 1ull;
+}
+
+// K-th largest of the register-held packed candidates e[0..nlive) of the wave
+// (slot i of every lane; unique nonzero keys, zeros ignored; nlive <= N is
+// wave-uniform); 0 when at most K are nonzero.  Counts come from ballots, so a
+// bisection step costs a few scalar operations per live slot.
+template <int N>
+__device__ __forceinline__ uint64_t wave_kth_regs(const uint64_t (&e)[N], int nlive, int K) {
+  int nz = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i < nlive) nz += wave_count(e[i] != 0ull);
+  if (nz <= K) return 0ull;
+  uint32_t t32 = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t32 | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (i < nlive) c += wave_count(cand_key(e[i]) >= cand);
+    if (c >= K) t32 = cand;
+  }
+  int above = 0, at = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i < nlive) {
+      above += wave_count(cand_key(e[i]) > t32);
+      at += wave_count(e[i] != 0ull && cand_key(e[i]) == t32);
+    }
+  }
+  const int need = K - above;
+  uint32_t tl = 0;
+  if (at > need) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tl | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (i < nlive) c += wave_count(e[i] != 0ull && cand_key(e[i]) == t32 && (uint32_t)e[i] >= cand);
+      if (c >= need) tl = cand;
+    }
+  }
+  return ((uint64_t)t32 << 32) | tl;
+}
+
+// Largest key value t such that at least K of the register-held candidates
+// have key >= t (0 if fewer than K are nonzero).  A lower bound of the K-th
+// largest candidate's key that skips tie resolution.
+template <int N>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint64_t (&e)[N], int nlive, int K) {
+  uint32_t t32 = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t32 | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (i < nlive) c += wave_count(cand_key(e[i]) >= cand);
+    if (c >= K) t32 = cand;
+  }
+  return t32;
+}
+
+// Keeps the top min(n, K) entries of arr[0..n) at arr[0..m), unordered, and
+// returns m.  n <= kPerLane * 64.
+template <int kPerLane>
+__device__ __forceinline__ int wave_keep_top(uint64_t* arr, int n, int K, int lane) {
+  if (n <= K) return n;
+  const int nlive = (n + kWave - 1) / kWave;
+  uint64_t e[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int p = lane + kWave * i;
+    e[i] = (i < nlive && p < n) ? arr[p] : 0ull;
+  }
+  const uint64_t t = wave_kth_regs<kPerLane>(e, nlive, K);
+  int off = 0;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    if (i >= nlive) break;
+    const bool keep = e[i] != 0ull && e[i] >= t;
+    const uint64_t mask = __ballot(keep);
+    if (keep) arr[off + __popcll(mask & lanemask_lt())] = e[i];
+    off += __popcll(mask);
+  }
+  return off;
+}
+
+// Rank-sorts arr[0..m) (m <= 64, unique keys) into dst[0..m), best first.
+// dst must not alias arr.
+__device__ __forceinline__ void wave_rank_sort(const uint64_t* arr, int m, uint64_t* dst, int lane) {
+  if (lane < m) {
+    const uint64_t e = arr[lane];
+    int rank = 0;
+    for (int i = 0; i < m; ++i) rank += arr[i] > e;
+    dst[rank] = e;
+  }
 }
 
 }  // namespace hsa

@@ -10,24 +10,15 @@ namespace hsa {
 struct ScanArgs {
   const void* q_ret;      // [B, Lq, Hkv, D]
   const void* landmarks;  // [B, Hkv, Nc, D]
-  int32_t* out_idx;       // [B, Lq, Hkv, K]   written when n_splits == 1
-  float* out_score;       // [B, Lq, Hkv, K]   written when n_splits == 1
-  uint64_t* lists;        // [B*Lq*Hkv, n_splits, K] packed candidates when n_splits > 1
+  int32_t* out_idx;       // [B, Lq, Hkv, K]
+  float* out_score;       // [B, Lq, Hkv, K]
+  uint64_t* lists;        // [B*Lq*Hkv, n_splits, K] per-split sorted candidates (wide, n_splits > 1)
+  uint32_t* counters;     // one arrival counter per row block (wide, n_splits > 1), zero on entry
   int64_t Lq, q_pos0, Nc;
   int32_t Hkv, K;
   int32_t n_max;          // max eligible chunks over all rows
-  int32_t split_len;      // chunks per split (multiple of 64)
-  int32_t n_splits;
-  float ret_scale;
-};
-
-// Merge of per-split candidate lists into the final top-K.
-struct MergeArgs {
-  const uint64_t* lists;  // [rows, n_splits, K]
-  int32_t* out_idx;       // [rows, K]
-  float* out_score;       // [rows, K]
-  int64_t rows;
-  int32_t n_splits, K;
+  int32_t split_len;      // chunks per split: 1024 (wide) or all eligible chunks
+  int32_t n_splits;       // 1 for the one-wave scan
   float ret_scale;
 };
 
@@ -46,10 +37,12 @@ struct AttendArgs {
   int32_t n_splits, slots_per_split;
   float attn_scale;
   int32_t qk_norm;
+  int32_t mode;           // 0: wave per row (many rows); 1: workgroup per (row, slot)
 };
 
 hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
-hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
+int scan_wide_chunks();
 hipError_t launch_attend(const AttendArgs& a, int64_t B, bool bf16, int D, int G, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 

@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kRows = 16;              // query rows per wave (MFMA N)
 constexpr int kCap = 96;               // candidate buffer entries per row
-constexpr int kMaxSplits = 1024;
+constexpr int kMaxSplits = 1024;      // wide-scan splits per row block (16 list heads per lane)
 
 template <bool BF16, int D> struct QOperand;
 
@@ -267,109 +267,263 @@ __global__ __launch_bounds__(64) void scan_topk_kernel(ScanArgs a) {
     const uint64_t e = buf[qrow][p];
     int rank = 0;
     for (int o = 0; o < m; ++o) rank += buf[qrow][o] > e;
-    if (a.n_splits == 1) {
-      a.out_idx[row_flat * a.K + rank] = (int32_t)cand_chunk(e);
-      a.out_score[row_flat * a.K + rank] = key_score(cand_key(e)) * a.ret_scale;
-    } else {
-      a.lists[(row_flat * a.n_splits + s) * a.K + rank] = e;
-    }
+    a.out_idx[row_flat * a.K + rank] = (int32_t)cand_chunk(e);
+    a.out_score[row_flat * a.K + rank] = key_score(cand_key(e)) * a.ret_scale;
   }
   for (int k = m + ((j - m) & 3); k < a.K; k += 4) {
-    if (a.n_splits == 1) {
-      a.out_idx[row_flat * a.K + k] = -1;
-      a.out_score[row_flat * a.K + k] = -INFINITY;
-    } else {
-      a.lists[(row_flat * a.n_splits + s) * a.K + k] = 0;
-    }
+    a.out_idx[row_flat * a.K + k] = -1;
+    a.out_score[row_flat * a.K + k] = -INFINITY;
   }
 }
 
-// K-th largest of arr[0..n) (unique packed keys) with the whole wave; 0 if n <= K.
-__device__ uint64_t wave_kth(const uint64_t* arr, int n, int K, int lane) {
-  if (n <= K) return 0;
-  uint32_t t32 = 0;
+// ---------------------------------------------------------------------------
+// Wide scan: few query rows over a long history (decode, appended rows).
+//
+// A workgroup of 16 waves scores one block of 16 rows against 1024 chunks in a
+// single pass: every wave issues all loads of its 64 landmarks at once, runs the
+// MFMA tiles and parks the 64x16 score keys in LDS.  Wave w then owns row w of
+// the block: its 64 lanes hold the row's 1024 keys (16 each), the K-th largest
+// lane maximum bounds the row's K-th key from below, and the few keys at or
+// above it are cut to the exact top K.  Each workgroup writes one sorted list
+// per row; the last workgroup of the row block to finish (arrival counter)
+// merges the lists and writes the final selection.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = 16;
+constexpr int kWideChunksPerWave = 64;
+constexpr int kWideChunks = kWideWaves * kWideChunksPerWave;
+constexpr int kWideRowWords = kWideChunks + 4;     // padded LDS row (u32 keys)
+constexpr int kWideCandCap = 512;                  // u64 candidates that fit a row's LDS
+
+// K-th largest of the wave's register-held u32 keys v[0..N) (multiplicity
+// counted); 0 if fewer than K are nonzero.
+template <int N>
+__device__ __forceinline__ uint32_t wave_kth_u32(const uint32_t (&v)[N], int K) {
+  uint32_t t = 0;
   for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = t32 | (1u << bit);
+    const uint32_t cand = t | (1u << bit);
     int c = 0;
-    for (int p = lane; p < n; p += kWave) c += cand_key(arr[p]) >= cand;
-    if (wave_sum_i(c) >= K) t32 = cand;
+#pragma unroll
+    for (int i = 0; i < N; ++i) c += wave_count(v[i] >= cand);
+    if (c >= K) t = cand;
   }
-  int above = 0, at = 0;
-  for (int p = lane; p < n; p += kWave) {
-    const uint32_t k = cand_key(arr[p]);
-    above += k > t32;
-    at += k == t32;
-  }
-  above = wave_sum_i(above);
-  at = wave_sum_i(at);
-  const int need = K - above;
-  uint32_t tl = 0;
-  if (at > need) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tl | (1u << bit);
-      int c = 0;
-      for (int p = lane; p < n; p += kWave) {
-        const uint64_t e = arr[p];
-        c += (cand_key(e) == t32) && ((uint32_t)e >= cand);
-      }
-      if (wave_sum_i(c) >= need) tl = cand;
-    }
-  }
-  return ((uint64_t)t32 << 32) | tl;
+  return t;
 }
 
-__global__ __launch_bounds__(64) void merge_topk_kernel(MergeArgs a) {
-  __shared__ uint64_t heads[kMaxSplits];
-  __shared__ uint64_t pool[kMaxTopK * kMaxTopK];
-  __shared__ uint64_t top[kMaxTopK];
-  __shared__ int n_pool;
-
-  const int lane = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int S = a.n_splits, K = a.K;
-  const uint64_t* L = a.lists + row * S * K;
-
-  for (int s = lane; s < S; s += kWave) heads[s] = L[(int64_t)s * K];
-  if (lane == 0) n_pool = 0;
-  __syncthreads();
-  // Only lists whose head reaches the K-th largest head can hold a top-K entry;
-  // at most K such lists exist, so the pool holds at most K*K entries.
-  const uint64_t th = wave_kth(heads, S, K, lane);
-  for (int s = lane; s < S; s += kWave) {
-    if (heads[s] == 0 || heads[s] < th) continue;
-    for (int k = 0; k < K; ++k) {
-      const uint64_t e = L[(int64_t)s * K + k];
-      if (e == 0 || e < th) break;
-      pool[atomicAdd(&n_pool, 1)] = e;
-    }
-  }
-  __syncthreads();
-  const int n = n_pool;
-  const uint64_t t = wave_kth(pool, n, K, lane);
-  int off = 0;
-  for (int base = 0; base < n; base += kWave) {
-    const int p = base + lane;
-    const uint64_t e = p < n ? pool[p] : 0;
-    const bool keep = p < n && e >= t && e != 0;
-    const uint64_t mask = __ballot(keep);
-    if (keep) top[off + __popcll(mask & ((1ull << lane) - 1))] = e;
-    off += __popcll(mask);
-  }
-  __syncthreads();
-  const int m = off;
+// Writes a row's final selection (sorted top[0..m), padding after it).
+__device__ __forceinline__ void write_selection(const uint64_t* top, int m, int K, int lane,
+                                                int32_t* idx, float* score, float ret_scale) {
   if (lane < K) {
-    const int64_t o = row * K;
     if (lane < m) {
       const uint64_t e = top[lane];
-      int rank = 0;
-      for (int i = 0; i < m; ++i) rank += top[i] > e;
-      a.out_idx[o + rank] = (int32_t)cand_chunk(e);
-      a.out_score[o + rank] = key_score(cand_key(e)) * a.ret_scale;
+      idx[lane] = (int32_t)cand_chunk(e);
+      score[lane] = key_score(cand_key(e)) * ret_scale;
     } else {
-      a.out_idx[o + lane] = -1;
-      a.out_score[o + lane] = -INFINITY;
+      idx[lane] = -1;
+      score[lane] = -INFINITY;
     }
   }
+}
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
+  using T = typename Elem<BF16>::T;
+  constexpr int LOADS = BF16 ? D / 32 : D / 16;
+  __shared__ __align__(16) uint32_t S[kWideWaves][kWideRowWords];
+  __shared__ uint64_t top[kWideWaves][kMaxTopK];
+  __shared__ int last;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qrow = lane & 15, j = lane >> 4;
+  const int s = blockIdx.y;
+  const int64_t rbk = (a.Lq + kRows - 1) / kRows;
+  const int64_t rb = (int64_t)blockIdx.x % rbk;
+  const int bg = (int)((int64_t)blockIdx.x / rbk);
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int c_begin = s * kWideChunks;
+  const int c_end = min(c_begin + kWideChunks, a.n_max);
+
+  // --- scores of this wave's 64 chunks for the block's 16 rows -------------
+  {
+    const int64_t r = rb * kRows + qrow;
+    const bool row_ok = r < a.Lq;
+    int lim = 0;
+    if (row_ok) {
+      const int64_t n = (a.q_pos0 + r) / kChunk;
+      lim = min((int)(n < a.Nc ? n : a.Nc), c_end);
+    }
+    QOperand<BF16, D> q;
+    q.load(reinterpret_cast<const T*>(a.q_ret) + ((b * a.Lq + (row_ok ? r : 0)) * a.Hkv + g) * D,
+           row_ok, j);
+    const T* lm = reinterpret_cast<const T*>(a.landmarks) + (int64_t)bg * a.Nc * D;
+    const int cw = c_begin + w * kWideChunksPerWave;
+    // landmark loads of GRP sub-tiles are all issued before their MFMAs
+    // (GRP = 4 for bf16: the wave's whole 16 KiB in flight at once)
+    constexpr int GRP = BF16 ? 4 : (D == 128 ? 1 : 2);
+#pragma unroll
+    for (int s0 = 0; s0 < 4; s0 += GRP) {
+      uint4 x[GRP][LOADS];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int cc = cw + (s0 + u) * 16 + qrow;
+        const bool ok = cc < c_end;
+        const T* p = lm + (int64_t)cc * D + (BF16 ? 8 : 4) * j;
+#pragma unroll
+        for (int t = 0; t < LOADS; ++t) {
+          x[u][t] = make_uint4(0, 0, 0, 0);
+          if (ok) x[u][t] = *reinterpret_cast<const uint4*>(p + (BF16 ? 32 : 16) * t);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int sub = s0 + u;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < LOADS; ++t) {
+          if constexpr (BF16) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[u][t]),
+                                                          q.v[t], acc, 0, 0, 0);
+          } else {
+            const float4 f = __builtin_bit_cast(float4, x[u][t]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.x, q.v[t].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.y, q.v[t].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.z, q.v[t].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.w, q.v[t].w, acc, 0, 0, 0);
+          }
+        }
+        uint4 kv;
+        const int c0 = cw + sub * 16 + 4 * j;
+        kv.x = c0 + 0 < lim ? score_key(acc[0]) : 0u;
+        kv.y = c0 + 1 < lim ? score_key(acc[1]) : 0u;
+        kv.z = c0 + 2 < lim ? score_key(acc[2]) : 0u;
+        kv.w = c0 + 3 < lim ? score_key(acc[3]) : 0u;
+        *reinterpret_cast<uint4*>(&S[qrow][w * kWideChunksPerWave + sub * 16 + 4 * j]) = kv;
+      }
+    }
+  }
+  __syncthreads();
+
+  // --- wave w: exact top K of row w over the workgroup's 1024 chunks --------
+  const int64_t rw = rb * kRows + w;
+  const bool rw_ok = rw < a.Lq;
+  const int K = a.K;
+  uint64_t* C = reinterpret_cast<uint64_t*>(&S[w][0]);
+  uint32_t v[16];
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = S[w][lane + kWave * i];
+    mx = max(mx, v[i]);
+  }
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    if (__popcll(__ballot(mx >= cand)) >= K) tau = cand;
+  }
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) total += wave_count(v[i] != 0u && v[i] >= tau);
+  uint32_t need_at = 0xFFFFFFFFu;   // exact path: ties at the threshold admitted in chunk order
+  int need = 0;
+  if (total > kWideCandCap) {
+    tau = wave_kth_u32<16>(v, K);
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) above += wave_count(v[i] > tau);
+    need = K - above;
+    need_at = tau;
+  }
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    bool keep = v[i] != 0u && (need_at == 0xFFFFFFFFu ? v[i] >= tau : v[i] > tau);
+    if (need_at != 0xFFFFFFFFu) {
+      const bool tie = v[i] != 0u && v[i] == need_at;
+      const uint64_t tm = __ballot(tie);
+      const int before = (int)__popcll(tm & lanemask_lt());
+      keep = keep || (tie && before < need);
+      const int nt = (int)__popcll(tm);
+      need -= need < nt ? need : nt;
+    }
+    const uint64_t mask = __ballot(keep);
+    if (keep) C[n + __popcll(mask & lanemask_lt())] = pack_cand(v[i], (uint32_t)(c_begin + lane + kWave * i));
+    n += __popcll(mask);
+  }
+  const int m = wave_keep_top<kWideCandCap / kWave>(C, n, K, lane);
+  wave_rank_sort(C, m, top[w], lane);
+
+  const int64_t row_flat = (b * a.Lq + rw) * a.Hkv + g;
+  if (a.n_splits == 1) {
+    if (rw_ok) write_selection(top[w], m, K, lane, a.out_idx + row_flat * K, a.out_score + row_flat * K,
+                               a.ret_scale);
+    return;
+  }
+  if (rw_ok && lane < K)
+    publish(&a.lists[(row_flat * a.n_splits + s) * K + lane], lane < m ? top[w][lane] : (uint64_t)0);
+
+  // --- last workgroup of the row block merges the per-split lists ------------
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) last = arrive(&a.counters[blockIdx.x]) == (uint32_t)(a.n_splits - 1);
+  __syncthreads();
+  if (!last) return;
+  if (rw_ok) {
+    const uint64_t* L = a.lists + row_flat * a.n_splits * K;
+    const int nh = (a.n_splits + kWave - 1) / kWave;      // live head slots per lane
+    uint64_t h[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sp = lane + kWave * i;
+      h[i] = (i < nh && sp < a.n_splits) ? fetch(&L[(int64_t)sp * K]) : 0ull;
+    }
+    // Only lists whose head reaches the K-th largest head key can hold a top-K
+    // entry.  Normally at most K + a few lists do; if ties push that past 64,
+    // the exact K-th head (ties broken by chunk) admits exactly K lists.
+    uint64_t lo = (uint64_t)wave_kth_key<16>(h, nh, K) << 32;
+    int n_on = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < nh) n_on += wave_count(h[i] != 0ull && h[i] >= lo);
+    if (n_on > kWave) lo = wave_kth_regs<16>(h, nh, K);
+    int* act = reinterpret_cast<int*>(&top[w][0]);
+    int na = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i >= nh) break;
+      const bool on = h[i] != 0ull && h[i] >= lo;
+      const uint64_t mask = __ballot(on);
+      if (on) act[na + __popcll(mask & lanemask_lt())] = lane + kWave * i;
+      na += __popcll(mask);
+    }
+    const int my_list = lane < na ? act[lane] : -1;
+    int cnt = 0;
+    bool more = my_list >= 0;
+    for (int q0 = 0; q0 < K && __any(more); q0 += 8) {
+      uint64_t e[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        e[q] = (more && q0 + q < K) ? fetch(&L[(int64_t)my_list * K + q0 + q]) : 0ull;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (cnt + kWave > kWideCandCap) {      // make room: keep the exact top K so far
+          cnt = wave_keep_top<kWideCandCap / kWave>(C, cnt, K, lane);
+          if (cnt >= K) {
+            uint64_t mn = ~0ull;
+            for (int p = 0; p < cnt; ++p) mn = C[p] < mn ? C[p] : mn;
+            lo = mn + 1;
+          }
+        }
+        const bool keep = e[q] != 0ull && e[q] >= lo;
+        const uint64_t mask = __ballot(keep);
+        if (keep) C[cnt + __popcll(mask & lanemask_lt())] = e[q];
+        cnt += __popcll(mask);
+      }
+      more = more && e[7] != 0ull && e[7] >= lo;
+    }
+    const int mm = wave_keep_top<kWideCandCap / kWave>(C, cnt, K, lane);
+    wave_rank_sort(C, mm, top[w], lane);
+    write_selection(top[w], mm, K, lane, a.out_idx + row_flat * K, a.out_score + row_flat * K,
+                    a.ret_scale);
+  }
+  if (tid == 0) reset_counter(&a.counters[blockIdx.x]);
 }
 
 }  // namespace
@@ -388,10 +542,23 @@ hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
-  if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_topk_kernel, dim3((unsigned)a.rows), dim3(64), 0, st, a);
+
+hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st) {
+  if (a.split_len != kWideChunks || a.n_splits > kMaxSplits) return hipErrorInvalidValue;
+  const int64_t rbk = (a.Lq + kRows - 1) / kRows;
+  const dim3 grid((unsigned)(rbk * B * a.Hkv), (unsigned)a.n_splits, 1);
+  const dim3 block(kWideWaves * 64, 1, 1);
+  if (bf16) {
+    if (D == 128) hipLaunchKernelGGL((scan_wide_kernel<true, 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_wide_kernel<true, 64>), grid, block, 0, st, a);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((scan_wide_kernel<false, 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_wide_kernel<false, 64>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
+
+int scan_wide_chunks() { return kWideChunks; }
+
 
 }  // namespace hsa
