@@ -269,3 +269,32 @@ def test_one_wave_scan_buffer_compaction(hsa):
     cfg = small(batch=2, n_kv_heads=2, n_q_heads=4, q_len=8256, kv_len=8256, top_k=64, head_dim=64)
     inp = W.generate(cfg, mode="grid_small")
     parity(hsa, inp, rows=sample_rows(cfg, 150), exact=True, ret_scale=0.125)
+
+
+@pytest.mark.parametrize("G,d", [(1, 128), (4, 64), (16, 128)])
+def test_chunk_major_attend_group_sizes(hsa, G, d):
+    """Many rows in bf16: pairs bucketed by chunk, MFMA tiles of 16/G pairs."""
+    cfg = small(n_q_heads=G, n_kv_heads=1, head_dim=d, q_len=1024, kv_len=4096, q_pos0=3072, top_k=8)
+    parity(hsa, W.generate(cfg), rows=sample_rows(cfg, 400))
+
+
+def test_chunk_major_given_selection_with_gaps(hsa):
+    """hsa_chunk_attend_blend in the chunk-major mode with -1 and out-of-range slots."""
+    import torch
+    cfg = small(q_len=1100, kv_len=4096, q_pos0=2996, top_k=6, n_kv_heads=2, n_q_heads=16)
+    inp = W.generate(cfg)
+    oi, os_, _, _ = oracle.forward(inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v,
+                                   q_pos0=cfg.q_pos0, top_k=cfg.top_k, with_output=False)
+    sel, sc = oi.copy(), os_.copy()
+    sel[::5, :, 1] = -1
+    sel[::13, 0, 3] = 10 ** 6
+    sel[7] = -1
+    rows = sample_rows(cfg, 300)
+    _, ref = oracle.attend_blend(inp.q_attn, inp.k, inp.v, sel[rows], sc[rows], rows=rows)
+    qa, k, v = (to_device(a, cfg.dtype) for a in (inp.q_attn, inp.k, inp.v))
+    ti = torch.from_numpy(sel.reshape(1, cfg.q_len, 2, cfg.top_k)).cuda()
+    ts = torch.from_numpy(sc.reshape(1, cfg.q_len, 2, cfg.top_k).astype(np.float32)).cuda()
+    out = hsa.chunk_attend_blend(qa, k, v, ti, ts)
+    got = out_to_f64(out).reshape(cfg.q_len, cfg.n_q_heads, cfg.head_dim)
+    assert np.abs(got[rows] - ref).max() <= TOL["bf16"]
+    assert np.all(got[7] == 0)

@@ -1,0 +1,364 @@
+// attend_chunk.hip -- chunk-major per-chunk attention and blend for many query
+// rows (Steps 3-4 of the HSA step in "Every Token Counts", agent-atlas
+// explainer, "How It Works (Technically)").
+//
+// With many rows the same chunk is selected by many (row, slot) pairs, while the
+// pairs of one row point at unrelated chunks.  Gathering per row would move a
+// chunk's 2*64*d values once per pair; here the pairs are bucketed by chunk so a
+// workgroup stages one chunk's K and V^T in LDS once and runs every pair that
+// selected it on MFMA tiles:
+//   count    per row: blend weights w_k (softmax of the selected scores) and a
+//            histogram of pairs per (batch, kv head, chunk) bin;
+//   scan     bin offsets and the list of work items (bin, block of kPairs pairs);
+//   scatter  pair ids into their bins;
+//   attend   per work item: K (row-major) and V^T in LDS, key norms once; per
+//            tile of 16 head-rows (16/G pairs x G heads): S = Q K^T on
+//            v_mfma_f32_16x16x32_bf16, in-chunk softmax across the tile's rows,
+//            P (times w_k, rounded to bf16) V on MFMA, fp16 partial per pair;
+//   combine  per row: the partials of its slots summed in slot order.
+// Results do not depend on the order of pairs inside a bin: every pair writes
+// only its own partial, and the combine order is fixed.
+#include "hsa_device.h"
+#include "hsa_internal.h"
+
+namespace hsa {
+namespace {
+
+constexpr int kPairs = 64;   // pairs per work item
+
+__device__ __forceinline__ int64_t bin_of(int64_t row, int32_t c, const ChunkArgs& a) {
+  const int64_t bg = (row / ((int64_t)a.Lq * a.Hkv)) * a.Hkv + row % a.Hkv;
+  return bg * a.Nc + c;
+}
+
+// --- count: blend weights and pairs per bin (one wave per row) --------------
+__global__ __launch_bounds__(256) void chunk_count_kernel(ChunkArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int K = a.K;
+  const int32_t c = lane < K ? a.idx[row * K + lane] : -1;
+  const float s = lane < K ? a.score[row * K + lane] : 0.f;
+  const bool valid = c >= 0 && (int64_t)c < a.Nc;
+  const float mx = wave_max(valid ? s : -INFINITY);
+  const float ex = valid ? expf(s - mx) : 0.f;
+  const float den = wave_sum(ex);
+  if (lane < K) a.wts[row * K + lane] = valid ? ex / den : 0.f;
+  if (valid) atomicAdd(&a.counts[bin_of(row, c, a)], 1u);
+}
+
+// --- scan: bin offsets, scatter cursors, work items (one workgroup) ----------
+__global__ __launch_bounds__(1024) void chunk_scan_kernel(ChunkArgs a) {
+  __shared__ uint32_t sp[1024], si[1024];
+  const int t = threadIdx.x;
+  const int64_t n = a.n_bins;
+  const int64_t seg = (n + 1023) / 1024;
+  const int64_t lo = t * seg, hi = min(n, lo + seg);
+  uint32_t tp = 0, ti = 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    const uint32_t c = a.counts[i];
+    tp += c;
+    ti += (c + kPairs - 1) / kPairs;
+  }
+  sp[t] = tp;
+  si[t] = ti;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
+    const uint32_t vp = t >= o ? sp[t - o] : 0u, vi = t >= o ? si[t - o] : 0u;
+    __syncthreads();
+    sp[t] += vp;
+    si[t] += vi;
+    __syncthreads();
+  }
+  uint32_t rp = sp[t] - tp, ri = si[t] - ti;
+  for (int64_t i = lo; i < hi; ++i) {
+    const uint32_t c = a.counts[i];
+    a.offsets[i] = rp;
+    a.cursor[i] = rp;
+    const uint32_t ni = (c + kPairs - 1) / kPairs;
+    for (uint32_t j = 0; j < ni; ++j) a.items[ri + j] = (uint64_t)i | ((uint64_t)j << 32);
+    rp += c;
+    ri += ni;
+    a.counts[i] = 0u;                    // ready for the next call
+  }
+  if (t == 1023) {
+    a.offsets[n] = rp;
+    *a.n_items = ri;
+  }
+}
+
+// --- scatter: pair ids into bins (one wave per row) --------------------------
+__global__ __launch_bounds__(256) void chunk_scatter_kernel(ChunkArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int K = a.K;
+  const int32_t c = lane < K ? a.idx[row * K + lane] : -1;
+  if (c >= 0 && (int64_t)c < a.Nc) {
+    const uint32_t pos = atomicAdd(&a.cursor[bin_of(row, c, a)], 1u);
+    a.pairs[pos] = (uint32_t)(row * K + lane);
+  }
+}
+
+// --- attend: one work item (a block of pairs of one chunk) per workgroup ----
+// Loads the A operand (attention queries of one 16-row tile) of a wave.
+template <int D, int G>
+__device__ __forceinline__ void load_q_tile(const ChunkArgs& a, const uint32_t* pid_s, int n_pairs,
+                                            int tile, int g, int ma, int jg, bf16x8 (&qa)[D / 32]) {
+  constexpr int PT = 16 / G;
+  const int pa = tile * PT + ma / G, ha = ma % G;
+  const bool va = pa < n_pairs;
+  const int64_t row = va ? (int64_t)(pid_s[pa] / (uint32_t)a.K) : 0;
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_attn) +
+                       ((row / a.Hkv) * a.Hq + (int64_t)g * G + ha) * D + 8 * jg;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (va) x = *reinterpret_cast<const uint4*>(qp + 32 * t);
+    qa[t] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
+  constexpr int KROW = D + 8;          // bf16 elements per K row in LDS (16-byte pad)
+  constexpr int VROW = kChunk + 8;     // bf16 elements per V^T row
+  constexpr int PROW = kChunk + 8;     // bf16 elements per P row
+  constexpr int OROW = D + 8;          // fp16 elements per staged output row
+  constexpr int PT = 16 / G;           // pairs per MFMA tile (16 head-rows)
+  constexpr int KSTEP = D / 32;        // MFMA K-steps over the head dimension
+  constexpr int NT = D / 16;           // output dimension tiles
+  __shared__ __align__(16) uint16_t ks[kChunk * KROW];
+  __shared__ __align__(16) uint16_t vt[D * VROW];
+  __shared__ float rk[kChunk];
+  __shared__ __align__(16) uint16_t ps[4][16 * PROW];
+  __shared__ __align__(16) uint16_t ob[4][16 * OROW];
+  __shared__ float rqs[4][16];
+  __shared__ uint32_t pid_s[kPairs];
+  __shared__ float w_s[kPairs];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const uint32_t item_i = blockIdx.x;
+  if (item_i >= *a.n_items) return;
+  const uint64_t item = a.items[item_i];
+  const int64_t bin = (int64_t)(item & 0xFFFFFFFFull);
+  const uint32_t blk = (uint32_t)(item >> 32);
+  const uint32_t p_begin = a.offsets[bin] + blk * kPairs;
+  const uint32_t p_end = min(p_begin + (uint32_t)kPairs, a.offsets[bin + 1]);
+  const int n_pairs = (int)(p_end - p_begin);
+  const int64_t bg = bin / a.Nc;
+  const int64_t c = bin - bg * a.Nc;
+  const int g = (int)(bg % a.Hkv);
+
+  // pair ids and blend weights of the item; K (row-major) and V^T in LDS
+  if (tid < n_pairs) {
+    const uint32_t pid = a.pairs[p_begin + tid];
+    pid_s[tid] = pid;
+    w_s[tid] = a.wts[pid];
+  }
+  {
+    const int64_t base = (bg * a.Lkv + c * kChunk) * D;
+    const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k) + base);
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v) + base;
+    constexpr int NV = kChunk * D / 8 / 256;
+    uint4 kx[NV], vx[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      kx[i] = kp[tid + 256 * i];
+      const int key = tid & 63, dg = (tid >> 6) + 4 * i;       // lane = key: transposed writes
+      vx[i] = *reinterpret_cast<const uint4*>(vp + key * D + 8 * dg);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = (tid + 256 * i) * 8;
+      *reinterpret_cast<uint4*>(&ks[(e / D) * KROW + e % D]) = kx[i];
+      const int key = tid & 63, dg = (tid >> 6) + 4 * i;
+      const uint32_t wv[4] = {vx[i].x, vx[i].y, vx[i].z, vx[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        vt[(8 * dg + 2 * q) * VROW + key] = (uint16_t)(wv[q] & 0xFFFFu);
+        vt[(8 * dg + 2 * q + 1) * VROW + key] = (uint16_t)(wv[q] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  {  // key inverse norms: 4 threads per key
+    const int key = tid >> 2, qd = tid & 3;
+    float ss = 0.f;
+#pragma unroll
+    for (int x = 0; x < D / 4; x += 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(&ks[key * KROW + qd * (D / 4) + x]);
+      const float lo = __uint_as_float(u << 16), hi = __uint_as_float(u & 0xFFFF0000u);
+      ss += lo * lo + hi * hi;
+    }
+    ss += __shfl_xor(ss, 1, kWave);
+    ss += __shfl_xor(ss, 2, kWave);
+    if (qd == 0) rk[key] = a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
+  }
+  __syncthreads();
+
+  const int n_tiles = (n_pairs + PT - 1) / PT;
+  const int ma = lane & 15, jg = lane >> 4;        // A-operand row, K-group
+  float rkv[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) rkv[nt] = rk[16 * nt + ma] * a.attn_scale;
+
+  bf16x8 qa[KSTEP], qn[KSTEP];
+  if (w < n_tiles) load_q_tile<D, G>(a, pid_s, n_pairs, w, g, ma, jg, qa);
+  for (int tile = w; tile < n_tiles; tile += 4) {
+    // prefetch the next tile's queries while this one computes
+    if (tile + 4 < n_tiles) load_q_tile<D, G>(a, pid_s, n_pairs, tile + 4, g, ma, jg, qn);
+    // query norms of the 16 rows
+    float qss = 0.f;
+#pragma unroll
+    for (int t = 0; t < KSTEP; ++t) {
+      const uint4 x = __builtin_bit_cast(uint4, qa[t]);
+      const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(wd[q] << 16), hi = __uint_as_float(wd[q] & 0xFFFF0000u);
+        qss += lo * lo + hi * hi;
+      }
+    }
+    qss += __shfl_xor(qss, 16, kWave);
+    qss += __shfl_xor(qss, 32, kWave);
+    if (lane < 16) rqs[w][ma] = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
+    // S = Q K^T: lane holds S[4*jg + i][16*nt + ma]
+    floatx4 s[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      s[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KSTEP; ++t) {
+        const uint4 b = *reinterpret_cast<const uint4*>(&ks[(16 * nt + ma) * KROW + 32 * t + 8 * jg]);
+        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], __builtin_bit_cast(bf16x8, b), s[nt], 0, 0, 0);
+      }
+    }
+    // softmax over the 64 keys of each head-row; P scaled by the pair's weight
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * jg + i;
+      const int pm = tile * PT + m / G;
+      const float rq = rqs[w][m];
+      float x[4], mx = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        x[nt] = s[nt][i] * rq * rkv[nt];
+        mx = fmaxf(mx, x[nt]);
+      }
+      mx = fmaxf(mx, dpp_f<0xB1>(mx));
+      mx = fmaxf(mx, dpp_f<0x4E>(mx));
+      mx = fmaxf(mx, dpp_f<0x141>(mx));
+      mx = fmaxf(mx, dpp_f<0x140>(mx));
+      float sum = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        x[nt] = expf(x[nt] - mx);
+        sum += x[nt];
+      }
+      sum += dpp_f<0xB1>(sum);
+      sum += dpp_f<0x4E>(sum);
+      sum += dpp_f<0x141>(sum);
+      sum += dpp_f<0x140>(sum);
+      const float scale = (pm < n_pairs ? w_s[pm] : 0.f) / sum;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) ps[w][m * PROW + 16 * nt + ma] = f32_to_bf16(x[nt] * scale);
+    }
+    // O = P V: lane holds O[4*jg + i][16*nt + ma]; staged to LDS as fp16
+    bf16x8 pa8[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      pa8[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&ps[w][ma * PROW + 32 * st + 8 * jg]));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint4 b = *reinterpret_cast<const uint4*>(&vt[(16 * nt + ma) * VROW + 32 * st + 8 * jg]);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8[st], __builtin_bit_cast(bf16x8, b), o, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ob[w][(4 * jg + i) * OROW + 16 * nt + ma] = __half_as_ushort(__float2half(o[i]));
+    }
+    // each pair's G x D block is contiguous in the partials: 16-byte stores
+    constexpr int V16 = 16 * D / 8;                  // 16-byte pieces in the tile
+#pragma unroll
+    for (int q = 0; q < V16 / kWave; ++q) {
+      const int e = lane + kWave * q;                // piece index
+      const int m = e / (D / 8), col = (e % (D / 8)) * 8;
+      const int pm = tile * PT + m / G;
+      if (pm < n_pairs) {
+        const uint4 val = *reinterpret_cast<const uint4*>(&ob[w][m * OROW + col]);
+        *reinterpret_cast<uint4*>(&a.partials[((int64_t)pid_s[pm] * G + (m % G)) * D + col]) = val;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KSTEP; ++t) qa[t] = qn[t];
+  }
+}
+
+// --- combine: out = sum over slots of the partials (slot order) --------------
+template <int D, int G>
+__global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int J = D / 8;
+  const int64_t total = a.rows * G * J;
+  if (t >= total) return;
+  const int64_t row = t / (G * J);
+  const int h = (int)((t / J) % G), j = (int)(t % J);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < a.K; ++k) {
+    const int32_t c = a.idx[row * a.K + k];
+    if (c < 0 || (int64_t)c >= a.Nc) continue;
+    const uint4 u = *reinterpret_cast<const uint4*>(&a.partials[((row * a.K + k) * G + h) * D + 8 * j]);
+    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += __half2float(__ushort_as_half((unsigned short)(wd[q] & 0xFFFFu)));
+      acc[2 * q + 1] += __half2float(__ushort_as_half((unsigned short)(wd[q] >> 16)));
+    }
+  }
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+  const int g = (int)(row % a.Hkv);
+  *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) +
+                            ((row / a.Hkv) * a.Hq + (int64_t)g * G + h) * D + 8 * j) = o;
+}
+
+template <int D, int G>
+hipError_t launch_dg(const ChunkArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((chunk_attend_kernel<D, G>), dim3((unsigned)a.max_items), dim3(256), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  const int64_t total = a.rows * G * (D / 8);
+  hipLaunchKernelGGL((chunk_combine_kernel<D, G>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t chunk_pairs_per_item() { return kPairs; }
+
+hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st) {
+  hipError_t e = launch_fill_u32(a.counts, a.n_bins, 0u, st);
+  if (e != hipSuccess) return e;
+  const unsigned row_blocks = (unsigned)((a.rows + 3) / 4);
+  hipLaunchKernelGGL(chunk_count_kernel, dim3(row_blocks), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(1024), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+#define HSA_CHUNK_CASE(DD, GG) \
+  if (D == DD && G == GG) return launch_dg<DD, GG>(a, st);
+  HSA_CHUNK_CASE(128, 1) HSA_CHUNK_CASE(128, 2) HSA_CHUNK_CASE(128, 4) HSA_CHUNK_CASE(128, 8)
+  HSA_CHUNK_CASE(128, 16) HSA_CHUNK_CASE(64, 1) HSA_CHUNK_CASE(64, 2) HSA_CHUNK_CASE(64, 4)
+  HSA_CHUNK_CASE(64, 8) HSA_CHUNK_CASE(64, 16)
+#undef HSA_CHUNK_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hsa

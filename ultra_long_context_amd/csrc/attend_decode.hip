@@ -1,0 +1,343 @@
+// attend_decode.hip -- per-chunk attention and blend for few query rows over a
+// long history (decode), bf16 (Steps 2-4 of the HSA step in "Every Token
+// Counts", agent-atlas explainer, "How It Works (Technically)").
+//
+// One workgroup of 4 waves serves 4 selected slots of one query row:
+//   selection  when the landmark scan left one sorted candidate list per chunk
+//              range, wave 0 merges them (only lists whose head reaches the
+//              K-th largest head key can contribute) and the workgroup of slot
+//              block 0 writes the row's final topk_idx / topk_score;
+//   attend     each wave takes one slot: the chunk's keys are the B operand of
+//              v_mfma_f32_16x16x32_bf16 straight from HBM, the G attention
+//              queries the A operand (16 rows, G of them used), V is staged
+//              transposed in LDS for the P.V product;
+//   blend      the 4 waves' weighted outputs are summed in LDS, published as the
+//              workgroup's partial, and the last workgroup of the row adds the
+//              partials in slot order.
+#include "hsa_device.h"
+#include "hsa_internal.h"
+
+namespace hsa {
+namespace {
+
+constexpr int kSlotsPerBlock = 4;
+constexpr int kMergeCap = 512;
+constexpr int kMaxHeadSlots = 8;     // list heads per lane: up to 512 splits
+
+// Exact top K of one row from per-split sorted lists (whole wave).  Leaves the
+// sorted selection in top[0..m) and returns m.
+__device__ int merge_row_lists(const uint64_t* L, int n_splits, int K, uint64_t* C, uint64_t* top,
+                               int* act, int lane) {
+  const int nh = (n_splits + kWave - 1) / kWave;      // <= kMaxHeadSlots
+  uint64_t h[kMaxHeadSlots];
+#pragma unroll
+  for (int i = 0; i < kMaxHeadSlots; ++i) {
+    const int sp = lane + kWave * i;
+    h[i] = (i < nh && sp < n_splits) ? L[(int64_t)sp * K] : 0ull;
+  }
+  uint64_t lo = (uint64_t)wave_kth_key<kMaxHeadSlots>(h, nh, K) << 32;
+  int n_on = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxHeadSlots; ++i)
+    if (i < nh) n_on += wave_count(h[i] != 0ull && h[i] >= lo);
+  if (n_on > kWave) lo = wave_kth_regs<kMaxHeadSlots>(h, nh, K);
+  int na = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxHeadSlots; ++i) {
+    if (i >= nh) break;
+    const bool on = h[i] != 0ull && h[i] >= lo;
+    const uint64_t mask = __ballot(on);
+    if (on) act[na + __popcll(mask & lanemask_lt())] = lane + kWave * i;
+    na += __popcll(mask);
+  }
+  const int my_list = lane < na ? act[lane] : -1;
+  int cnt = 0;
+  bool more = my_list >= 0;
+  for (int q0 = 0; q0 < K && __any(more); q0 += 8) {
+    uint64_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = (more && q0 + q < K) ? L[(int64_t)my_list * K + q0 + q] : 0ull;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (cnt + kWave > kMergeCap) {
+        cnt = wave_keep_top<kMergeCap / kWave>(C, cnt, K, lane);
+        if (cnt >= K) {
+          uint64_t mn = ~0ull;
+          for (int p = 0; p < cnt; ++p) mn = C[p] < mn ? C[p] : mn;
+          lo = mn + 1;
+        }
+      }
+      const bool keep = e[q] != 0ull && e[q] >= lo;
+      const uint64_t mask = __ballot(keep);
+      if (keep) C[cnt + __popcll(mask & lanemask_lt())] = e[q];
+      cnt += __popcll(mask);
+    }
+    more = more && e[7] != 0ull && e[7] >= lo;
+  }
+  const int m = wave_keep_top<kMergeCap / kWave>(C, cnt, K, lane);
+  wave_rank_sort(C, m, top, lane);
+  return m;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attend_decode_kernel(DecodeArgs a) {
+  constexpr int KSTEP = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int VROW = kChunk + 8;     // bf16 elements per V^T row
+  constexpr int PROW = kChunk + 8;
+  __shared__ __align__(16) uint16_t vt[kSlotsPerBlock][D * VROW];
+  __shared__ __align__(16) uint16_t ps[kSlotsPerBlock][16 * PROW];
+  __shared__ uint64_t cand[kMergeCap];
+  __shared__ uint64_t top[kMaxTopK];
+  __shared__ int act[kWave];
+  __shared__ float osum[kSlotsPerBlock][G * D];
+  __shared__ int32_t sel_c[kMaxTopK];
+  __shared__ float sel_w[kMaxTopK];
+  __shared__ int last;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int64_t row = blockIdx.x;                     // (b*Lq + r)*Hkv + g
+  const int blk = blockIdx.y;
+  const int g = (int)(row % a.Hkv);
+  const int64_t br = row / a.Hkv;
+  const int64_t b = br / a.Lq;
+  const int K = a.K;
+
+  // --- the row's selection and blend weights -------------------------------
+  if (w == 0) {
+    int m;
+    if (a.lists != nullptr) {
+      m = merge_row_lists(a.lists + row * a.n_splits * K, a.n_splits, K, cand, top, act, lane);
+    } else {
+      const int32_t ci = lane < K ? a.idx_in[row * K + lane] : -1;
+      const float si = lane < K ? a.score_in[row * K + lane] : 0.f;
+      // given selection: keep it as is (slot order), packing only valid entries
+      m = -1;
+      if (lane < K) {
+        sel_c[lane] = (ci >= 0 && (int64_t)ci < a.Nc) ? ci : -1;
+        sel_w[lane] = si;
+      }
+    }
+    float s = -INFINITY;
+    int32_t c = -1;
+    if (m >= 0) {                         // merged: sorted top[0..m)
+      if (lane < m) {
+        c = (int32_t)cand_chunk(top[lane]);
+        s = key_score(cand_key(top[lane])) * a.ret_scale;
+      }
+      if (blk == 0 && lane < K && a.idx_out != nullptr) {
+        a.idx_out[row * K + lane] = lane < m ? c : -1;
+        a.score_out[row * K + lane] = lane < m ? s : -INFINITY;
+      }
+    } else if (lane < K) {
+      c = sel_c[lane];
+      s = sel_w[lane];
+    }
+    const bool valid = c >= 0;
+    const float mx = wave_max(valid ? s : -INFINITY);
+    const float ex = valid ? expf(s - mx) : 0.f;
+    const float den = wave_sum(ex);
+    if (lane < K) {
+      sel_c[lane] = valid ? c : -1;
+      sel_w[lane] = valid ? ex / den : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // --- one slot per wave ----------------------------------------------------
+  const int slot = blk * kSlotsPerBlock + w;
+  const int c = slot < K ? sel_c[slot] : -1;
+  const float wk = slot < K ? sel_w[slot] : 0.f;
+  const int ma = lane & 15, jg = lane >> 4;
+  floatx4 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (c >= 0) {
+    const int64_t base = ((b * a.Hkv + g) * a.Lkv + (int64_t)c * kChunk) * D;
+    const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k) + base;
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v) + base;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_attn) + (br * a.Hq + (int64_t)g * G) * D;
+    // all loads first: keys as B operands, queries as A operands, V rows (lane = key)
+    uint4 kb[4][KSTEP], qa[KSTEP], vx[D / 8];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int t = 0; t < KSTEP; ++t)
+        kb[nt][t] = *reinterpret_cast<const uint4*>(kp + (16 * nt + ma) * D + 32 * t + 8 * jg);
+#pragma unroll
+    for (int t = 0; t < KSTEP; ++t) {
+      qa[t] = make_uint4(0, 0, 0, 0);
+      if (ma < G) qa[t] = *reinterpret_cast<const uint4*>(qp + ma * D + 32 * t + 8 * jg);
+    }
+#pragma unroll
+    for (int dg = 0; dg < D / 8; ++dg) vx[dg] = *reinterpret_cast<const uint4*>(vp + lane * D + 8 * dg);
+    // V^T into LDS
+#pragma unroll
+    for (int dg = 0; dg < D / 8; ++dg) {
+      const uint32_t wv[4] = {vx[dg].x, vx[dg].y, vx[dg].z, vx[dg].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        vt[w][(8 * dg + 2 * q) * VROW + lane] = (uint16_t)(wv[q] & 0xFFFFu);
+        vt[w][(8 * dg + 2 * q + 1) * VROW + lane] = (uint16_t)(wv[q] >> 16);
+      }
+    }
+    // norms: lane holds 32 dims of query row ma and of key 16*nt + ma
+    float qss = 0.f, kss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KSTEP; ++t) {
+      const uint32_t qw[4] = {qa[t].x, qa[t].y, qa[t].z, qa[t].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(qw[q] << 16), hi = __uint_as_float(qw[q] & 0xFFFF0000u);
+        qss += lo * lo + hi * hi;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t kw[4] = {kb[nt][t].x, kb[nt][t].y, kb[nt][t].z, kb[nt][t].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = __uint_as_float(kw[q] << 16), hi = __uint_as_float(kw[q] & 0xFFFF0000u);
+          kss[nt] += lo * lo + hi * hi;
+        }
+      }
+    }
+    qss += __shfl_xor(qss, 16, kWave);
+    qss += __shfl_xor(qss, 32, kWave);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      kss[nt] += __shfl_xor(kss[nt], 16, kWave);
+      kss[nt] += __shfl_xor(kss[nt], 32, kWave);
+    }
+    const float rq_mine = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
+    float rk[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) rk[nt] = (a.qk_norm ? 1.0f / fmaxf(sqrtf(kss[nt]), 1e-6f) : 1.0f) * a.attn_scale;
+    // S = Q K^T: lane holds S[4*jg + i][16*nt + ma]
+    floatx4 s[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      s[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KSTEP; ++t)
+        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[t]),
+                                                        __builtin_bit_cast(bf16x8, kb[nt][t]), s[nt], 0, 0, 0);
+    }
+    // softmax per query row over the 64 keys
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * jg + i;
+      const float rq = __shfl(rq_mine, m, kWave);
+      float x[4], mx = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        x[nt] = s[nt][i] * rq * rk[nt];
+        mx = fmaxf(mx, x[nt]);
+      }
+      mx = fmaxf(mx, dpp_f<0xB1>(mx));
+      mx = fmaxf(mx, dpp_f<0x4E>(mx));
+      mx = fmaxf(mx, dpp_f<0x141>(mx));
+      mx = fmaxf(mx, dpp_f<0x140>(mx));
+      float sum = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        x[nt] = expf(x[nt] - mx);
+        sum += x[nt];
+      }
+      sum += dpp_f<0xB1>(sum);
+      sum += dpp_f<0x4E>(sum);
+      sum += dpp_f<0x141>(sum);
+      sum += dpp_f<0x140>(sum);
+      const float scale = (m < G ? wk : 0.f) / sum;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) ps[w][m * PROW + 16 * nt + ma] = f32_to_bf16(x[nt] * scale);
+    }
+    // O = P V
+    bf16x8 pa8[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      pa8[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&ps[w][ma * PROW + 32 * st + 8 * jg]));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint4 bv = *reinterpret_cast<const uint4*>(&vt[w][(16 * nt + ma) * VROW + 32 * st + 8 * jg]);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8[st], __builtin_bit_cast(bf16x8, bv), o[nt], 0, 0, 0);
+      }
+  }
+  // --- sum the 4 waves' outputs; lane holds O[4*jg + i][16*nt + ma] ----------
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * jg + i;
+      if (m < G) osum[w][m * D + 16 * nt + ma] = o[nt][i];
+    }
+  __syncthreads();
+  const int n_blk = a.n_blocks;
+  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (br * a.Hq + (int64_t)g * G) * D;
+  float* part = a.partials + (row * n_blk + blk) * (int64_t)(G * D);
+  for (int e = tid; e < G * D; e += 256) {
+    const float v = (osum[0][e] + osum[1][e]) + (osum[2][e] + osum[3][e]);
+    if (n_blk == 1) op[e] = f32_to_bf16(v);
+    else publish(&part[e], v);
+  }
+  if (n_blk == 1) return;
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) last = arrive(&a.counters[row]) == (uint32_t)(n_blk - 1);
+  __syncthreads();
+  if (!last) return;
+  const float* pb = a.partials + row * n_blk * (int64_t)(G * D);
+  for (int e = tid; e < G * D; e += 256) {
+    float v = 0.f;
+#pragma unroll 4
+    for (int p = 0; p < n_blk; ++p) v += fetch(&pb[(int64_t)p * G * D + e]);
+    op[e] = f32_to_bf16(v);
+  }
+  if (tid == 0) reset_counter(&a.counters[row]);
+}
+
+// One wave per row: merge the per-split lists into the final selection.
+__global__ __launch_bounds__(64) void merge_lists_kernel(MergeArgs a) {
+  __shared__ uint64_t cand[kMergeCap];
+  __shared__ uint64_t top[kMaxTopK];
+  __shared__ int act[kWave];
+  const int lane = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int K = a.K;
+  const int m = merge_row_lists(a.lists + row * a.n_splits * K, a.n_splits, K, cand, top, act, lane);
+  if (lane < K) {
+    if (lane < m) {
+      a.out_idx[row * K + lane] = (int32_t)cand_chunk(top[lane]);
+      a.out_score[row * K + lane] = key_score(cand_key(top[lane])) * a.ret_scale;
+    } else {
+      a.out_idx[row * K + lane] = -1;
+      a.out_score[row * K + lane] = -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+int decode_slots_per_block() { return kSlotsPerBlock; }
+
+hipError_t launch_merge_lists(const MergeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(merge_lists_kernel, dim3((unsigned)a.rows), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_decode(const DecodeArgs& a, int64_t rows, int D, int G, hipStream_t st) {
+  const dim3 grid((unsigned)rows, (unsigned)a.n_blocks, 1), block(256);
+#define HSA_DEC_CASE(DD, GG)                                                                  \
+  if (D == DD && G == GG) {                                                                   \
+    hipLaunchKernelGGL((attend_decode_kernel<DD, GG>), grid, block, 0, st, a);                 \
+    return hipGetLastError();                                                                 \
+  }
+  HSA_DEC_CASE(128, 1) HSA_DEC_CASE(128, 2) HSA_DEC_CASE(128, 4) HSA_DEC_CASE(128, 8)
+  HSA_DEC_CASE(128, 16) HSA_DEC_CASE(64, 1) HSA_DEC_CASE(64, 2) HSA_DEC_CASE(64, 4)
+  HSA_DEC_CASE(64, 8) HSA_DEC_CASE(64, 16)
+#undef HSA_DEC_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hsa

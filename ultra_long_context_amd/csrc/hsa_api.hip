@@ -12,7 +12,7 @@ namespace hsa {
 namespace {
 
 constexpr int64_t kRowsPerWave = 16;
-constexpr int64_t kMaxSplits = 1024;
+constexpr int64_t kMaxSplits = 512;    // wide scan: 1024 chunks x 512 splits
 // The workspace starts with arrival counters that every call leaves at zero.
 constexpr size_t kCounterBytes = 16384;
 constexpr int64_t kScanCounters = 2048;     // counters [0, 2048): wide-scan row blocks
@@ -29,7 +29,10 @@ struct Plan {
   int32_t split_len, n_splits;
   bool wide;             // few-row scan: 16-wave workgroups, last-arriver merge
   int32_t attn_splits, slots_per_split, attn_mode;
+  int64_t n_bins, max_items;   // chunk-major attend
   size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
+  size_t off_ccounts, off_coffsets, off_ccursor, off_citems, off_cnitems, off_cpairs, off_cwts,
+      off_cparts;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -88,11 +91,24 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
   p->n_splits = (int32_t)(p->wide ? wsplits : 1);
 
   // Attend plan.  Few rows: one workgroup per (row, slot), partials combined by
-  // the last slot to finish.  Many rows: one wave per row.
-  if (p->rows < 1024) {
+  // the last slot to finish.  Many rows, bf16: pairs bucketed by chunk, one
+  // MFMA workgroup per block of pairs of a chunk, then a slot-ordered combine.
+  // Many rows, fp32: one wave per row.
+  p->n_bins = (int64_t)s->batch * s->n_kv_heads * Nc;
+  const int64_t n_pairs = p->rows * p->K;
+  p->max_items = (n_pairs + chunk_pairs_per_item() - 1) / chunk_pairs_per_item() + p->n_bins;
+  if (p->rows < 1024 && p->bf16) {
+    p->attn_mode = 3;
+    p->attn_splits = (p->K + decode_slots_per_block() - 1) / decode_slots_per_block();
+    p->slots_per_split = decode_slots_per_block();
+  } else if (p->rows < 1024) {
     p->attn_mode = 1;
     p->attn_splits = p->K;
     p->slots_per_split = 1;
+  } else if (p->bf16 && n_pairs < INT32_MAX && p->n_bins + 1 < INT32_MAX && p->max_items < INT32_MAX) {
+    p->attn_mode = 2;
+    p->attn_splits = 1;
+    p->slots_per_split = p->K;
   } else {
     p->attn_mode = 0;
     p->attn_splits = 1;
@@ -107,6 +123,19 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
   if (p->n_splits > 1) off = align_up(off + (size_t)p->rows * p->n_splits * p->K * 8, 256);
   p->off_partials = off;
   if (p->attn_splits > 1) off = align_up(off + (size_t)p->rows * p->attn_splits * G * p->D * 4, 256);
+  p->off_ccounts = p->off_coffsets = p->off_ccursor = p->off_citems = p->off_cnitems = 0;
+  p->off_cpairs = p->off_cwts = p->off_cparts = 0;
+  if (p->attn_mode == 2) {
+    const size_t nb = (size_t)p->n_bins, np = (size_t)n_pairs;
+    p->off_ccounts = off; off = align_up(off + nb * 4, 256);
+    p->off_coffsets = off; off = align_up(off + (nb + 1) * 4, 256);
+    p->off_ccursor = off; off = align_up(off + nb * 4, 256);
+    p->off_citems = off; off = align_up(off + (size_t)p->max_items * 8, 256);
+    p->off_cnitems = off; off = align_up(off + 4, 256);
+    p->off_cpairs = off; off = align_up(off + np * 4, 256);
+    p->off_cwts = off; off = align_up(off + np * 4, 256);
+    p->off_cparts = off; off = align_up(off + np * G * p->D * 2, 256);
+  }
   p->total = off;
   return HSA_OK;
 }
@@ -128,18 +157,42 @@ hsa_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
   return HSA_OK;
 }
 
+// Landmark scan; with several splits, the per-split lists are merged into the
+// final selection unless the caller merges them itself (merge = false).
 hsa_status_t launch_retrieve(const Plan& p, const void* q_ret, const void* landmarks,
-                             int32_t* idx, float* score, void* ws, hipStream_t st) {
+                             int32_t* idx, float* score, void* ws, hipStream_t st, bool merge) {
   char* w = static_cast<char*>(ws);
   ScanArgs a;
   a.q_ret = q_ret; a.landmarks = landmarks; a.out_idx = idx; a.out_score = score;
   a.lists = reinterpret_cast<uint64_t*>(w + p.off_lists);
-  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters);
   a.Lq = p.Lq; a.q_pos0 = p.q_pos0; a.Nc = p.Nc; a.Hkv = p.Hkv; a.K = p.K;
   a.n_max = p.n_max; a.split_len = p.split_len; a.n_splits = p.n_splits; a.ret_scale = p.ret_scale;
   const hipError_t e = p.wide ? launch_scan_wide(a, p.B, p.bf16, p.D, st)
                              : launch_scan(a, p.B, p.bf16, p.D, st);
-  return e == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
+  if (e != hipSuccess) return HSA_ERR_DEVICE;
+  if (merge && p.n_splits > 1) {
+    MergeArgs m;
+    m.lists = a.lists; m.out_idx = idx; m.out_score = score; m.rows = p.rows;
+    m.n_splits = p.n_splits; m.K = p.K; m.ret_scale = p.ret_scale;
+    if (launch_merge_lists(m, st) != hipSuccess) return HSA_ERR_DEVICE;
+  }
+  return HSA_OK;
+}
+
+// Decode attend: merges the scan's lists itself when `lists` is given.
+hsa_status_t launch_decode(const Plan& p, const void* q_attn, const void* k, const void* v,
+                           const uint64_t* lists, const int32_t* idx_in, const float* score_in,
+                           int32_t* idx_out, float* score_out, void* out, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  DecodeArgs a;
+  a.q_attn = q_attn; a.k = k; a.v = v; a.lists = lists; a.idx_in = idx_in; a.score_in = score_in;
+  a.idx_out = idx_out; a.score_out = score_out; a.out = out;
+  a.partials = reinterpret_cast<float*>(w + p.off_partials);
+  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters) + kScanCounters;
+  a.Lq = p.Lq; a.Lkv = p.Lkv; a.Nc = p.Nc; a.Hq = p.Hq; a.Hkv = p.Hkv; a.K = p.K;
+  a.n_splits = p.n_splits; a.n_blocks = p.attn_splits;
+  a.ret_scale = p.ret_scale; a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0;
+  return launch_attend_decode(a, p.rows, p.D, p.G, st) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
 }
 
 hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* k, const void* v,
@@ -153,6 +206,24 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
   a.Lq = p.Lq; a.Lkv = p.Lkv; a.Nc = p.Nc; a.Hq = p.Hq; a.Hkv = p.Hkv; a.K = p.K;
   a.n_splits = p.attn_splits; a.slots_per_split = p.slots_per_split;
   a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0; a.mode = p.attn_mode;
+  if (p.attn_mode == 3)
+    return launch_decode(p, q_attn, k, v, nullptr, idx, score, nullptr, nullptr, out, ws, st);
+  if (p.attn_mode == 2) {
+    ChunkArgs c;
+    c.q_attn = q_attn; c.k = k; c.v = v; c.idx = idx; c.score = score; c.out = out;
+    c.counts = reinterpret_cast<uint32_t*>(w + p.off_ccounts);
+    c.offsets = reinterpret_cast<uint32_t*>(w + p.off_coffsets);
+    c.cursor = reinterpret_cast<uint32_t*>(w + p.off_ccursor);
+    c.items = reinterpret_cast<uint64_t*>(w + p.off_citems);
+    c.n_items = reinterpret_cast<uint32_t*>(w + p.off_cnitems);
+    c.pairs = reinterpret_cast<uint32_t*>(w + p.off_cpairs);
+    c.wts = reinterpret_cast<float*>(w + p.off_cwts);
+    c.partials = reinterpret_cast<__half*>(w + p.off_cparts);
+    c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
+    c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
+    c.attn_scale = p.attn_scale; c.qk_norm = p.qk_norm ? 1 : 0;
+    return launch_attend_chunk(c, p.D, p.G, st) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
+  }
   if (launch_attend(a, p.B, p.bf16, p.D, p.G, st) != hipSuccess) return HSA_ERR_DEVICE;
   return HSA_OK;
 }
@@ -191,7 +262,7 @@ HSA_EXPORT hsa_status_t hsa_retrieve_topk(const hsa_shape_t* shape, const void* 
   if ((st = hsa::check_ptrs({q_ret, lm, topk_idx, topk_score})) != HSA_OK) return st;
   if ((st = hsa::check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
   return hsa::launch_retrieve(p, q_ret, landmarks, topk_idx, topk_score, ws,
-                              static_cast<hipStream_t>(stream));
+                              static_cast<hipStream_t>(stream), true);
 }
 
 HSA_EXPORT hsa_status_t hsa_chunk_attend_blend(const hsa_shape_t* shape, const void* q_attn,
@@ -228,7 +299,12 @@ HSA_EXPORT hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret,
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + p.off_idx);
   float* score = topk_score ? topk_score : reinterpret_cast<float*>(w + p.off_score);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = hsa::launch_retrieve(p, q_ret, landmarks, idx, score, ws, s)) != HSA_OK) return st;
+  if (p.attn_mode == 3 && p.n_splits > 1) {   // decode: the attend merges the lists
+    if ((st = hsa::launch_retrieve(p, q_ret, landmarks, idx, score, ws, s, false)) != HSA_OK) return st;
+    return hsa::launch_decode(p, q_attn, k, v, reinterpret_cast<const uint64_t*>(w + p.off_lists),
+                              nullptr, nullptr, topk_idx, topk_score, out, ws, s);
+  }
+  if ((st = hsa::launch_retrieve(p, q_ret, landmarks, idx, score, ws, s, true)) != HSA_OK) return st;
   return hsa::launch_attend_blend(p, q_attn, k, v, idx, score, out, ws, s);
 }
 

@@ -1,6 +1,7 @@
 // hsa_internal.h -- launch interface between the C ABI host code and the kernels.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -13,13 +14,41 @@ struct ScanArgs {
   int32_t* out_idx;       // [B, Lq, Hkv, K]
   float* out_score;       // [B, Lq, Hkv, K]
   uint64_t* lists;        // [B*Lq*Hkv, n_splits, K] per-split sorted candidates (wide, n_splits > 1)
-  uint32_t* counters;     // one arrival counter per row block (wide, n_splits > 1), zero on entry
   int64_t Lq, q_pos0, Nc;
   int32_t Hkv, K;
   int32_t n_max;          // max eligible chunks over all rows
   int32_t split_len;      // chunks per split: 1024 (wide) or all eligible chunks
   int32_t n_splits;       // 1 for the one-wave scan
   float ret_scale;
+};
+
+// Merge of per-split sorted candidate lists into the final selection.
+struct MergeArgs {
+  const uint64_t* lists;  // [rows, n_splits, K]
+  int32_t* out_idx;       // [rows, K]
+  float* out_score;       // [rows, K]
+  int64_t rows;
+  int32_t n_splits, K;
+  float ret_scale;
+};
+
+// Decode attend (few rows, bf16): merge in the prologue, MFMA per slot.
+struct DecodeArgs {
+  const void* q_attn;
+  const void* k;
+  const void* v;
+  const uint64_t* lists;     // per-split sorted candidates [rows, n_splits, K], or nullptr
+  const int32_t* idx_in;     // given selection when lists == nullptr
+  const float* score_in;
+  int32_t* idx_out;          // final selection written by slot block 0 (merged path; may be null)
+  float* score_out;
+  void* out;
+  float* partials;           // [rows, n_blocks, G, D]
+  uint32_t* counters;        // [rows], zero on entry
+  int64_t Lq, Lkv, Nc;
+  int32_t Hq, Hkv, K, n_splits, n_blocks;
+  float ret_scale, attn_scale;
+  int32_t qk_norm;
 };
 
 // Per-chunk attention + blend (Steps 3-4).
@@ -40,10 +69,37 @@ struct AttendArgs {
   int32_t mode;           // 0: wave per row (many rows); 1: workgroup per (row, slot)
 };
 
+// Chunk-major attend + blend (many rows, bf16): pairs bucketed by chunk.
+struct ChunkArgs {
+  const void* q_attn;     // [B, Lq, Hq, D] bf16
+  const void* k;          // [B, Hkv, Lkv, D] bf16
+  const void* v;          // [B, Hkv, Lkv, D] bf16
+  const int32_t* idx;     // [rows, K]
+  const float* score;     // [rows, K]
+  void* out;              // [B, Lq, Hq, D] bf16
+  uint32_t* counts;       // [n_bins]      pairs per (b, kv head, chunk)
+  uint32_t* offsets;      // [n_bins + 1]  first pair of each bin
+  uint32_t* cursor;       // [n_bins]      scatter positions
+  uint64_t* items;        // [max_items]   bin | block << 32
+  uint32_t* n_items;      // number of valid items
+  uint32_t* pairs;        // [rows * K]    pair ids (row * K + slot), grouped by bin
+  float* wts;             // [rows * K]    blend weights
+  __half* partials;       // [rows * K, G, D] weighted per-chunk outputs
+  int64_t rows, Lq, Lkv, Nc, n_bins, max_items;
+  int32_t Hq, Hkv, K;
+  float attn_scale;
+  int32_t qk_norm;
+};
+
 hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 int scan_wide_chunks();
 hipError_t launch_attend(const AttendArgs& a, int64_t B, bool bf16, int D, int G, hipStream_t st);
+hipError_t launch_merge_lists(const MergeArgs& a, hipStream_t st);
+hipError_t launch_attend_decode(const DecodeArgs& a, int64_t rows, int D, int G, hipStream_t st);
+int decode_slots_per_block();
+hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st);
+int64_t chunk_pairs_per_item();
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 
 }  // namespace hsa

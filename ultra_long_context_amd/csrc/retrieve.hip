@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kRows = 16;              // query rows per wave (MFMA N)
 constexpr int kCap = 96;               // candidate buffer entries per row
-constexpr int kMaxSplits = 1024;      // wide-scan splits per row block (16 list heads per lane)
+constexpr int kMaxSplits = 512;       // wide-scan splits per row block (8 list heads per lane in the merge)
 
 template <bool BF16, int D> struct QOperand;
 
@@ -284,9 +284,9 @@ __global__ __launch_bounds__(64) void scan_topk_kernel(ScanArgs a) {
 // MFMA tiles and parks the 64x16 score keys in LDS.  Wave w then owns row w of
 // the block: its 64 lanes hold the row's 1024 keys (16 each), the K-th largest
 // lane maximum bounds the row's K-th key from below, and the few keys at or
-// above it are cut to the exact top K.  Each workgroup writes one sorted list
-// per row; the last workgroup of the row block to finish (arrival counter)
-// merges the lists and writes the final selection.
+// above it are cut to the exact top K.  With one split the workgroup writes the
+// final selection; otherwise it writes one sorted list per row and split, which
+// a merge (merge_lists_kernel, or the decode attend's prologue) combines.
 // ---------------------------------------------------------------------------
 constexpr int kWideWaves = 16;
 constexpr int kWideChunksPerWave = 64;
@@ -330,7 +330,6 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
   constexpr int LOADS = BF16 ? D / 32 : D / 16;
   __shared__ __align__(16) uint32_t S[kWideWaves][kWideRowWords];
   __shared__ uint64_t top[kWideWaves][kMaxTopK];
-  __shared__ int last;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qrow = lane & 15, j = lane >> 4;
   const int s = blockIdx.y;
@@ -456,74 +455,7 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
                                a.ret_scale);
     return;
   }
-  if (rw_ok && lane < K)
-    publish(&a.lists[(row_flat * a.n_splits + s) * K + lane], lane < m ? top[w][lane] : (uint64_t)0);
-
-  // --- last workgroup of the row block merges the per-split lists ------------
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) last = arrive(&a.counters[blockIdx.x]) == (uint32_t)(a.n_splits - 1);
-  __syncthreads();
-  if (!last) return;
-  if (rw_ok) {
-    const uint64_t* L = a.lists + row_flat * a.n_splits * K;
-    const int nh = (a.n_splits + kWave - 1) / kWave;      // live head slots per lane
-    uint64_t h[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int sp = lane + kWave * i;
-      h[i] = (i < nh && sp < a.n_splits) ? fetch(&L[(int64_t)sp * K]) : 0ull;
-    }
-    // Only lists whose head reaches the K-th largest head key can hold a top-K
-    // entry.  Normally at most K + a few lists do; if ties push that past 64,
-    // the exact K-th head (ties broken by chunk) admits exactly K lists.
-    uint64_t lo = (uint64_t)wave_kth_key<16>(h, nh, K) << 32;
-    int n_on = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i < nh) n_on += wave_count(h[i] != 0ull && h[i] >= lo);
-    if (n_on > kWave) lo = wave_kth_regs<16>(h, nh, K);
-    int* act = reinterpret_cast<int*>(&top[w][0]);
-    int na = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i >= nh) break;
-      const bool on = h[i] != 0ull && h[i] >= lo;
-      const uint64_t mask = __ballot(on);
-      if (on) act[na + __popcll(mask & lanemask_lt())] = lane + kWave * i;
-      na += __popcll(mask);
-    }
-    const int my_list = lane < na ? act[lane] : -1;
-    int cnt = 0;
-    bool more = my_list >= 0;
-    for (int q0 = 0; q0 < K && __any(more); q0 += 8) {
-      uint64_t e[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        e[q] = (more && q0 + q < K) ? fetch(&L[(int64_t)my_list * K + q0 + q]) : 0ull;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (cnt + kWave > kWideCandCap) {      // make room: keep the exact top K so far
-          cnt = wave_keep_top<kWideCandCap / kWave>(C, cnt, K, lane);
-          if (cnt >= K) {
-            uint64_t mn = ~0ull;
-            for (int p = 0; p < cnt; ++p) mn = C[p] < mn ? C[p] : mn;
-            lo = mn + 1;
-          }
-        }
-        const bool keep = e[q] != 0ull && e[q] >= lo;
-        const uint64_t mask = __ballot(keep);
-        if (keep) C[cnt + __popcll(mask & lanemask_lt())] = e[q];
-        cnt += __popcll(mask);
-      }
-      more = more && e[7] != 0ull && e[7] >= lo;
-    }
-    const int mm = wave_keep_top<kWideCandCap / kWave>(C, cnt, K, lane);
-    wave_rank_sort(C, mm, top[w], lane);
-    write_selection(top[w], mm, K, lane, a.out_idx + row_flat * K, a.out_score + row_flat * K,
-                    a.ret_scale);
-  }
-  if (tid == 0) reset_counter(&a.counters[blockIdx.x]);
+  if (rw_ok && lane < K) a.lists[(row_flat * a.n_splits + s) * K + lane] = lane < m ? top[w][lane] : 0ull;
 }
 
 }  // namespace
