@@ -12,10 +12,17 @@ HIP-event window, by a 1 GiB read that evicts L2 and the 256 MB Infinity Cache,
 so every step starts cold.  ms_per_step is the mean event-timed step; the wall
 time of the whole timed region (flushes included) is reported as wall_ms_per_step.
 
-roofline: the dominant kernel of each workload is timed on its own with HIP events
-on the launch stream (same cold-cache procedure) and priced against MI355X peaks:
-  decode  -> landmark scan kernel(s), HBM bytes of the landmarks and queries;
-  prefill -> attend/blend kernel, its contraction FLOPs.
+roofline: a second pass of `steps` cold forwards has the library record HIP events
+around each kernel stage on the launch stream (hsa_forward_profiled); the stage
+with the largest mean duration is the dominant kernel, priced against MI355X
+peaks by its algorithmic work per launch:
+  decode  scan   -> HBM bytes of the eligible landmarks and q_ret;
+          attend -> HBM bytes of the distinct selected chunks' K/V, q_attn, out;
+  prefill attend -> bf16 MFMA FLOPs, 4*G*64*d per selection;
+          scan   -> bf16 MFMA FLOPs, 2*d per candidate.
+  traffic: HBM bytes per launch from two rocprofv3 counter passes (FETCH_SIZE,
+  WRITE_SIZE) scaled by a 1 GiB calibration copy, read from the summary under
+  profiles/ (null when none exists or the kernel sources changed since).
 cpu_baseline: the fp64 oracle on a bounded, stratified sample of query rows of the
 same workload, timed on this host's cores (test infrastructure, not the product).
 """
@@ -37,6 +44,18 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 VALU_FP32_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 FLOP (FMA) x 2.4 GHz, non-packed
 
 WORKLOADS = {"prefill_128K": 2, "decode_16M": 3}
+
+# the kernel behind each (workload, stage) of the plan the library picks for it
+KERNELS = {
+    ("decode_16M", "scan"): "scan_wide_kernel<true, 128>",
+    ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
+    ("prefill_128K", "scan"): "scan_topk_kernel<true, 128>",
+    ("prefill_128K", "bucket"): "chunk_count/scan/scatter kernels",
+    ("prefill_128K", "attend"): "chunk_attend_kernel<128, 8>",
+    ("prefill_128K", "combine"): "chunk_combine_kernel<128, 8>",
+}
+COPY_BYTES = 1 << 30          # calibration copy: 2^28 fp32 read and written
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
@@ -111,6 +130,32 @@ class Timer:
         return float(np.mean(ms)), float(np.median(ms)), wall * 1e3
 
 
+    def stages(self, call, steps):
+        """Mean duration (ms) of each kernel stage over `steps` cold eager calls;
+        call(evs) runs one forward with the library recording evs[stage] =
+        (start, end) on the launch stream."""
+        import ultra_long_context_amd as hsa
+        torch = self.torch
+        evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for n in hsa.STAGES} for _ in range(steps)]
+        for d in evs:                      # create the events before the marker
+            for e0, e1 in d.values():
+                e0.record()
+                e1.record()
+        marker = torch.cuda.Event(enable_timing=True)
+        marker.record()
+        for d in evs:
+            self.cold()
+            call(d)
+        torch.cuda.synchronize()
+        out = {}
+        for n in hsa.STAGES:
+            # a stage the plan does not run keeps its events from before the marker
+            if all(marker.elapsed_time(d[n][0]) > 0 for d in evs):
+                out[n] = float(np.mean([d[n][0].elapsed_time(d[n][1]) for d in evs]))
+        return out
+
+
 def distinct_chunks(idx_t, cfg) -> int:
     """U: distinct (batch, kv head, chunk) triples selected (each chunk's K/V read once)."""
     import torch
@@ -140,6 +185,65 @@ def algorithmic(cfg, U, elem=2):
                 scan_flops=2 * d * cand, attend_flops=4 * cfg.group * 64 * d * sel)
 
 
+def source_digest() -> str:
+    """sha256 over the library's kernel sources (traffic figures go stale with them)."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "ultra_long_context_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(src, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload, kernel):
+    return os.path.join(PROFILES, "%s_%s_hbm_traffic.txt" % (kernel.split("<")[0], workload))
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed counter summary, or None if there
+    is none or the kernel sources changed since it was taken."""
+    path = traffic_file(workload, kernel)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k_, v_ = line.split(":", 1)
+                kv[k_.strip()] = v_.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def roofline(workload, stage, ms, alg):
+    """Roofline entry for one kernel stage: algorithmic bytes or FLOPs per launch
+    over its measured duration."""
+    kernel = KERNELS.get((workload, stage), stage)
+    prefill = workload.startswith("prefill")
+    if stage == "attend" and prefill:
+        units = ("mfma", alg["attend_flops"], "4*G*64*d FLOP per selection x %d selections"
+                 % alg["selections"])
+    elif stage == "scan" and prefill:
+        units = ("mfma", alg["scan_flops"], "2*d FLOP per candidate x %d candidates" % alg["candidates"])
+    elif stage == "attend":
+        units = ("hbm", alg["kv_bytes"] + alg["q_attn_bytes"] + alg["out_bytes"],
+                 "2*64*d*2 B per distinct selected chunk x U + q_attn + out")
+    else:
+        units = ("hbm", alg["landmark_bytes"] + alg["q_ret_bytes"],
+                 "d*2 B per eligible landmark + q_ret")
+    bound, amount, how = units
+    if bound == "mfma":
+        achieved, peak, unit = amount / (ms / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = amount / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    return dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
+                traffic=measured_traffic(workload, kernel), kernel=kernel, stage=stage,
+                kernel_ms=ms, algorithmic_per_launch=amount, algorithmic_units=how)
+
+
 def bench_workload(name, steps, warmup, timer, cpu_baseline):
     import torch
     import ultra_long_context_amd as hsa
@@ -152,9 +256,6 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     dev = [to_dev(a, cfg.dtype) for a in (inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v)]
     q_ret, lm, q_attn, k, v = dev
     out = torch.empty_like(q_attn)
-    idx = torch.empty((cfg.batch, cfg.q_len, cfg.n_kv_heads, cfg.top_k), dtype=torch.int32,
-                      device="cuda:0")
-    score = torch.empty(idx.shape, dtype=torch.float32, device="cuda:0")
 
     def step():
         hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=cfg.q_pos0, top_k=cfg.top_k, out=out)
@@ -173,52 +274,25 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     log("[bench] %s: %.4f ms/step (median %.4f, wall incl. flush %.3f)" % (name, ms_mean, ms_med, wall_ms))
     warm_mean, _, _ = timer.time(g_step, steps, flush=False)
 
-    # dominant-kernel timing through the two halves of the C ABI
+    # per-kernel timing: the same forward, cold, with HIP events recorded by the
+    # library around each kernel stage on the launch stream
+    stage_ms = timer.stages(lambda evs: hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=cfg.q_pos0,
+                                                    top_k=cfg.top_k, out=out, stage_events=evs),
+                            steps)
+    log("[bench] %s: kernel stages (ms) %s" % (name, json.dumps(stage_ms)))
     sel_out = hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=cfg.q_pos0, top_k=cfg.top_k,
                           return_topk=True)
-    idx.copy_(sel_out[1])
-    score.copy_(sel_out[2])
-    U = distinct_chunks(idx, cfg)
+    U = distinct_chunks(sel_out[1], cfg)
     alg = algorithmic(cfg, U)
-    sel_i = torch.empty_like(idx)
-    sel_s = torch.empty_like(score)
-    ws = hsa.new_workspace(hsa.workspace_size(hsa.make_shape(
-        batch=cfg.batch, q_len=cfg.q_len, kv_len=cfg.kv_len, q_pos0=cfg.q_pos0,
-        n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, top_k=cfg.top_k,
-        dtype=hsa.DTYPE_BF16)), "cuda:0")
-
-    def retrieve():
-        hsa.retrieve_topk(q_ret, lm, q_pos0=cfg.q_pos0, top_k=cfg.top_k, kv_len=cfg.kv_len,
-                          out=(sel_i, sel_s), workspace=ws)
-
-    def attend():
-        hsa.chunk_attend_blend(q_attn, k, v, idx, score, out=out, workspace=ws)
-
-    r_ms, _, _ = timer.time(timer.capture(retrieve), steps)
-    a_ms, _, _ = timer.time(timer.capture(attend), steps)
-    log("[bench] %s: retrieve %.4f ms, attend %.4f ms, U=%d" % (name, r_ms, a_ms, U))
+    del sel_out
 
     qtok = cfg.batch * cfg.q_len
     res = dict(workload=name, config=cfg, value=qtok / (ms_mean / 1e3), ms_per_step=ms_mean,
                ms_median=ms_med, wall_ms_per_step=wall_ms, warm_ms_per_step=warm_mean,
-               retrieve_ms=r_ms, attend_ms=a_ms, alg=alg, U=U)
-    if name == "decode_16M":
-        # landmark stream: every landmark and query read once per launch
-        nbytes = alg["landmark_bytes"] + alg["q_ret_bytes"]
-        gbs = nbytes / (r_ms / 1e3) / 1e9
-        res["roofline"] = dict(bound="hbm", kernel="scan_wide_kernel (landmark scan, top-K, merge)",
-                               achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
-                               traffic=None, alg_bytes_per_launch=nbytes)
-        res["hbm_frac_whole_step"] = (alg["bytes"] / 8e12) / (ms_mean / 1e3)
-    else:
-        fl = alg["attend_flops"]
-        tf = fl / (a_ms / 1e3) / 1e12
-        res["roofline"] = dict(bound="alu", kernel="attend_blend (fp32 VALU contraction)",
-                               achieved=tf, peak=VALU_FP32_PEAK_TFLOPS, unit="TFLOP/s",
-                               frac=tf / VALU_FP32_PEAK_TFLOPS, traffic=None,
-                               alg_flops_per_launch=fl,
-                               mfma_bf16_frac=tf / MFMA_BF16_PEAK_TFLOPS)
-        res["hbm_frac_whole_step"] = (alg["bytes"] / 8e12) / (ms_mean / 1e3)
+               stage_ms=stage_ms, alg=alg, U=U)
+    dom = max(stage_ms, key=stage_ms.get)
+    res["roofline"] = roofline(name, dom, stage_ms[dom], alg)
+    res["hbm_frac_whole_step"] = (alg["bytes"] / 8e12) / (ms_mean / 1e3)
     if cpu_baseline:
         res["cpu_baseline"] = oracle_baseline(cfg, inp)
     del dev, q_ret, lm, q_attn, k, v, out, inp
@@ -250,6 +324,64 @@ def oracle_baseline(cfg, inp, budget_s=20.0):
                     len(rows), total, stride, dt))
 
 
+def pmc_mean_kib(csv_path, counter, match):
+    """Mean per-dispatch value of `counter` over dispatches whose kernel name
+    contains `match`, from a rocprofv3 --pmc counter_collection.csv."""
+    import csv
+    vals = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter and match in row.get("Kernel_Name", ""):
+                d = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit("no %s dispatch of a kernel matching %r in %s" % (counter, match, csv_path))
+    return float(np.mean(list(vals.values()))), len(vals)
+
+
+def pmc_summary(fetch_csv, write_csv, workload, kernel, command):
+    """Text summary of two counter passes: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of `kernel`, each scaled by what the counter reads for the
+    calibration copy (torch.neg over 2^28 fp32: 1 GiB read, 1 GiB written)."""
+    match = kernel.split("<")[0]
+    f_k, nf = pmc_mean_kib(fetch_csv, "FETCH_SIZE", match)
+    w_k, nw = pmc_mean_kib(write_csv, "WRITE_SIZE", match)
+    f_c, _ = pmc_mean_kib(fetch_csv, "FETCH_SIZE", "neg_kernel")
+    w_c, _ = pmc_mean_kib(write_csv, "WRITE_SIZE", "neg_kernel")
+    ff, fw = COPY_BYTES / (f_c * 1024.0), COPY_BYTES / (w_c * 1024.0)
+    lines = [
+        "# HBM traffic of %s, workload %s (rocprofv3 counter passes)" % (kernel, workload),
+        "# command: %s" % command,
+        "kernel: %s" % kernel,
+        "workload: %s" % workload,
+        "source_digest: %s" % source_digest(),
+        "fetch_dispatches: %d" % nf,
+        "write_dispatches: %d" % nw,
+        "FETCH_SIZE_KiB_per_dispatch: %.1f" % f_k,
+        "WRITE_SIZE_KiB_per_dispatch: %.1f" % w_k,
+        "copy_FETCH_SIZE_KiB: %.1f" % f_c,
+        "copy_WRITE_SIZE_KiB: %.1f" % w_c,
+        "copy_bytes_each_way: %d" % COPY_BYTES,
+        "fetch_scale: %.4f" % ff,
+        "write_scale: %.4f" % fw,
+        "fetch_bytes_per_launch: %.0f" % (f_k * 1024.0 * ff),
+        "write_bytes_per_launch: %.0f" % (w_k * 1024.0 * fw),
+        "traffic_bytes_per_launch: %.0f" % (f_k * 1024.0 * ff + w_k * 1024.0 * fw),
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def copy_calibration():
+    """The plain copy kernel the counter passes are scaled by."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,7 +389,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workloads", default="prefill_128K,decode_16M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run the 1 GiB calibration copy first (for counter passes)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of --kernel-of from two counter passes")
+    ap.add_argument("--kernel-of", default="prefill_128K:attend",
+                    help="workload:stage whose kernel --pmc-summary reports")
+    ap.add_argument("--command", default="", help="command recorded in the --pmc-summary header")
     args = ap.parse_args()
+    if args.pmc_summary:
+        wl, stage = args.kernel_of.split(":")
+        sys.stdout.write(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl,
+                                     KERNELS[(wl, stage)], args.command))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the HSA forward here has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -272,6 +416,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
     timer = Timer()
     names = [w for w in args.workloads.split(",") if w]
     results = {}
@@ -297,7 +443,7 @@ def main():
         "roofline": m["roofline"],
         "wall_ms_per_step": m["wall_ms_per_step"], "warm_ms_per_step": m["warm_ms_per_step"],
         "hbm_frac_whole_step": m["hbm_frac_whole_step"],
-        "stage_ms": {"retrieve": m["retrieve_ms"], "attend": m["attend_ms"]},
+        "stage_ms": m["stage_ms"],
     }
     if "cpu_baseline" in m:
         line["cpu_baseline"] = m["cpu_baseline"]
@@ -308,7 +454,7 @@ def main():
                                  "warm_ms_per_step", "roofline", "hbm_frac_whole_step")}
         sub["unit"] = "query-tokens/s"
         sub["config"] = cfg_dict(r["config"])
-        sub["stage_ms"] = {"retrieve": r["retrieve_ms"], "attend": r["attend_ms"]}
+        sub["stage_ms"] = r["stage_ms"]
         if "cpu_baseline" in r:
             sub["cpu_baseline"] = r["cpu_baseline"]
         line[name] = sub

@@ -127,6 +127,32 @@ hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret, const void
                          int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Kernel stages of a forward call, for hsa_forward_profiled.  A stage the
+ * plan does not run records nothing (e.g. MERGE when the attend merges the
+ * per-split candidate lists itself, BUCKET and COMBINE outside the chunk-major
+ * attend). */
+typedef enum {
+  HSA_STAGE_SCAN = 0,     /* landmark scoring + per-split / per-row top-K        */
+  HSA_STAGE_MERGE = 1,    /* merge of per-split candidate lists (separate kernel) */
+  HSA_STAGE_BUCKET = 2,   /* chunk-major attend: bucketing of (row, slot) pairs   */
+  HSA_STAGE_ATTEND = 3,   /* per-chunk attention (with the blend where fused)     */
+  HSA_STAGE_COMBINE = 4,  /* chunk-major attend: slot-ordered blend of partials   */
+  HSA_STAGE_COUNT = 5
+} hsa_stage_t;
+
+/* hsa_forward, with caller-owned HIP events (hipEvent_t, passed as void*)
+ * recorded on `stream` around each kernel stage: stage_events[2*s] before the
+ * stage's first kernel and stage_events[2*s + 1] after its last, for
+ * s < HSA_STAGE_COUNT.  stage_events may be NULL and any entry may be NULL
+ * (nothing recorded).  The library keeps no reference to the events.  An event
+ * record failure returns HSA_ERR_DEVICE.  Diagnostics for per-kernel timing;
+ * outputs are those of hsa_forward. */
+hsa_status_t hsa_forward_profiled(const hsa_shape_t* shape, const void* q_ret,
+                                  const void* landmarks, const void* q_attn, const void* k,
+                                  const void* v, void* out, int32_t* topk_idx, float* topk_score,
+                                  void* ws, size_t ws_bytes, void* stream,
+                                  void* const* stage_events);
+
 /* Static description of a status code. */
 const char* hsa_status_string(hsa_status_t status);
 

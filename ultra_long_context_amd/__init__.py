@@ -31,7 +31,11 @@ CHUNK = 64
 MAX_TOP_K = 64
 
 EXPORTED_SYMBOLS = ("hsa_workspace_size", "hsa_workspace_init", "hsa_retrieve_topk",
-                    "hsa_chunk_attend_blend", "hsa_forward", "hsa_status_string", "hsa_version")
+                    "hsa_chunk_attend_blend", "hsa_forward", "hsa_forward_profiled",
+                    "hsa_status_string", "hsa_version")
+
+# kernel stages (hsa_stage_t)
+STAGES = ("scan", "merge", "bucket", "attend", "combine")
 
 _STATUS = {0: "HSA_OK", 1: "HSA_ERR_NULL_POINTER", 2: "HSA_ERR_BAD_SHAPE", 3: "HSA_ERR_UNSUPPORTED",
            4: "HSA_ERR_WORKSPACE_TOO_SMALL", 5: "HSA_ERR_DEVICE", 6: "HSA_ERR_MISALIGNED"}
@@ -85,6 +89,9 @@ def _load():
             lib.hsa_chunk_attend_blend.restype = st
             lib.hsa_forward.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.hsa_forward.restype = st
+            lib.hsa_forward_profiled.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                 ctypes.POINTER(vp)]
+            lib.hsa_forward_profiled.restype = st
             lib.hsa_status_string.argtypes = [st]
             lib.hsa_status_string.restype = ctypes.c_char_p
             lib.hsa_version.restype = ctypes.c_int32
@@ -171,15 +178,26 @@ def _workspace(shape, device, workspace=None):
     return ws, need
 
 
+def _event_handle(ev) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (created on first record)."""
+    if ev.cuda_event == 0:
+        ev.record()
+    return ev.cuda_event
+
+
 def forward(q_ret, landmarks, q_attn, k, v, *, q_pos0: int, top_k: int, qk_norm: bool = True,
             ret_scale: float | None = None, attn_scale: float | None = None,
-            return_topk: bool = False, out=None, workspace=None):
+            return_topk: bool = False, out=None, workspace=None, stage_events=None):
     """HSA forward (Steps 1-4).
 
     q_ret [B, Lq, Hkv, d], landmarks [B, Hkv, Lkv//64, d], q_attn [B, Lq, Hq, d],
     k, v [B, Hkv, Lkv, d]; all bf16 or all fp32, contiguous, on one GPU.
     Returns out [B, Lq, Hq, d] (and topk_idx int32, topk_score fp32
     [B, Lq, Hkv, K] if return_topk).  Runs on the current stream.
+
+    stage_events: optional {stage name: (start, end) torch.cuda.Event} with
+    names from STAGES; the library records them around that stage's kernels
+    (hsa_forward_profiled).
     """
     torch = _torch()
     for t, n in ((q_ret, "q_ret"), (landmarks, "landmarks"), (q_attn, "q_attn"), (k, "k"), (v, "v")):
@@ -203,11 +221,21 @@ def forward(q_ret, landmarks, q_attn, k, v, *, q_pos0: int, top_k: int, qk_norm:
     if return_topk:
         idx = torch.empty((B, Lq, Hkv, top_k), dtype=torch.int32, device=dev)
         score = torch.empty((B, Lq, Hkv, top_k), dtype=torch.float32, device=dev)
-    st = _load().hsa_forward(ctypes.byref(shape), _ptr(q_ret), _ptr(landmarks), _ptr(q_attn),
-                             _ptr(k), _ptr(v), _ptr(out), _ptr(idx), _ptr(score), _ptr(ws),
-                             ws.numel(), _stream(dev))
-    if st:
-        raise HsaError(st, "hsa_forward")
+    args = (ctypes.byref(shape), _ptr(q_ret), _ptr(landmarks), _ptr(q_attn), _ptr(k), _ptr(v),
+            _ptr(out), _ptr(idx), _ptr(score), _ptr(ws), ws.numel(), _stream(dev))
+    if stage_events is None:
+        st = _load().hsa_forward(*args)
+        if st:
+            raise HsaError(st, "hsa_forward")
+    else:
+        evs = (ctypes.c_void_p * (2 * len(STAGES)))()
+        for name, (e0, e1) in stage_events.items():
+            s = STAGES.index(name)
+            evs[2 * s] = _event_handle(e0)
+            evs[2 * s + 1] = _event_handle(e1)
+        st = _load().hsa_forward_profiled(*args, evs)
+        if st:
+            raise HsaError(st, "hsa_forward_profiled")
     return (out, idx, score) if return_topk else out
 
 

@@ -330,21 +330,27 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs a) {
 }
 
 template <int D, int G>
-hipError_t launch_dg(const ChunkArgs& a, hipStream_t st) {
+hipError_t launch_dg(const ChunkArgs& a, hipStream_t st, const Marks& mk) {
+  hipError_t e;
+  if ((e = mk.rec(kStageAttend, 0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((chunk_attend_kernel<D, G>), dim3((unsigned)a.max_items), dim3(256), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mk.rec(kStageAttend, 1, st)) != hipSuccess) return e;
+  if ((e = mk.rec(kStageCombine, 0, st)) != hipSuccess) return e;
   const int64_t total = a.rows * G * (D / 8);
   hipLaunchKernelGGL((chunk_combine_kernel<D, G>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mk.rec(kStageCombine, 1, st);
 }
 
 }  // namespace
 
 int64_t chunk_pairs_per_item() { return kPairs; }
 
-hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st) {
-  hipError_t e = launch_fill_u32(a.counts, a.n_bins, 0u, st);
-  if (e != hipSuccess) return e;
+hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk) {
+  hipError_t e;
+  if ((e = mk.rec(kStageBucket, 0, st)) != hipSuccess) return e;
+  if ((e = launch_fill_u32(a.counts, a.n_bins, 0u, st)) != hipSuccess) return e;
   const unsigned row_blocks = (unsigned)((a.rows + 3) / 4);
   hipLaunchKernelGGL(chunk_count_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -352,8 +358,9 @@ hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st)
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(chunk_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = mk.rec(kStageBucket, 1, st)) != hipSuccess) return e;
 #define HSA_CHUNK_CASE(DD, GG) \
-  if (D == DD && G == GG) return launch_dg<DD, GG>(a, st);
+  if (D == DD && G == GG) return launch_dg<DD, GG>(a, st, mk);
   HSA_CHUNK_CASE(128, 1) HSA_CHUNK_CASE(128, 2) HSA_CHUNK_CASE(128, 4) HSA_CHUNK_CASE(128, 8)
   HSA_CHUNK_CASE(128, 16) HSA_CHUNK_CASE(64, 1) HSA_CHUNK_CASE(64, 2) HSA_CHUNK_CASE(64, 4)
   HSA_CHUNK_CASE(64, 8) HSA_CHUNK_CASE(64, 16)

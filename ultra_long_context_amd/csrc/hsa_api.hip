@@ -160,21 +160,25 @@ hsa_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
 // Landmark scan; with several splits, the per-split lists are merged into the
 // final selection unless the caller merges them itself (merge = false).
 hsa_status_t launch_retrieve(const Plan& p, const void* q_ret, const void* landmarks,
-                             int32_t* idx, float* score, void* ws, hipStream_t st, bool merge) {
+                             int32_t* idx, float* score, void* ws, hipStream_t st, bool merge,
+                             const Marks& mk) {
   char* w = static_cast<char*>(ws);
   ScanArgs a;
   a.q_ret = q_ret; a.landmarks = landmarks; a.out_idx = idx; a.out_score = score;
   a.lists = reinterpret_cast<uint64_t*>(w + p.off_lists);
   a.Lq = p.Lq; a.q_pos0 = p.q_pos0; a.Nc = p.Nc; a.Hkv = p.Hkv; a.K = p.K;
   a.n_max = p.n_max; a.split_len = p.split_len; a.n_splits = p.n_splits; a.ret_scale = p.ret_scale;
+  if (mk.rec(kStageScan, 0, st) != hipSuccess) return HSA_ERR_DEVICE;
   const hipError_t e = p.wide ? launch_scan_wide(a, p.B, p.bf16, p.D, st)
                              : launch_scan(a, p.B, p.bf16, p.D, st);
-  if (e != hipSuccess) return HSA_ERR_DEVICE;
+  if (e != hipSuccess || mk.rec(kStageScan, 1, st) != hipSuccess) return HSA_ERR_DEVICE;
   if (merge && p.n_splits > 1) {
     MergeArgs m;
     m.lists = a.lists; m.out_idx = idx; m.out_score = score; m.rows = p.rows;
     m.n_splits = p.n_splits; m.K = p.K; m.ret_scale = p.ret_scale;
-    if (launch_merge_lists(m, st) != hipSuccess) return HSA_ERR_DEVICE;
+    if (mk.rec(kStageMerge, 0, st) != hipSuccess || launch_merge_lists(m, st) != hipSuccess ||
+        mk.rec(kStageMerge, 1, st) != hipSuccess)
+      return HSA_ERR_DEVICE;
   }
   return HSA_OK;
 }
@@ -182,7 +186,8 @@ hsa_status_t launch_retrieve(const Plan& p, const void* q_ret, const void* landm
 // Decode attend: merges the scan's lists itself when `lists` is given.
 hsa_status_t launch_decode(const Plan& p, const void* q_attn, const void* k, const void* v,
                            const uint64_t* lists, const int32_t* idx_in, const float* score_in,
-                           int32_t* idx_out, float* score_out, void* out, void* ws, hipStream_t st) {
+                           int32_t* idx_out, float* score_out, void* out, void* ws, hipStream_t st,
+                           const Marks& mk) {
   char* w = static_cast<char*>(ws);
   DecodeArgs a;
   a.q_attn = q_attn; a.k = k; a.v = v; a.lists = lists; a.idx_in = idx_in; a.score_in = score_in;
@@ -192,12 +197,15 @@ hsa_status_t launch_decode(const Plan& p, const void* q_attn, const void* k, con
   a.Lq = p.Lq; a.Lkv = p.Lkv; a.Nc = p.Nc; a.Hq = p.Hq; a.Hkv = p.Hkv; a.K = p.K;
   a.n_splits = p.n_splits; a.n_blocks = p.attn_splits;
   a.ret_scale = p.ret_scale; a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0;
-  return launch_attend_decode(a, p.rows, p.D, p.G, st) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
+  if (mk.rec(kStageAttend, 0, st) != hipSuccess || launch_attend_decode(a, p.rows, p.D, p.G, st) != hipSuccess ||
+      mk.rec(kStageAttend, 1, st) != hipSuccess)
+    return HSA_ERR_DEVICE;
+  return HSA_OK;
 }
 
 hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* k, const void* v,
                                  const int32_t* idx, const float* score, void* out, void* ws,
-                                 hipStream_t st) {
+                                 hipStream_t st, const Marks& mk) {
   char* w = static_cast<char*>(ws);
   AttendArgs a;
   a.q_attn = q_attn; a.k = k; a.v = v; a.idx = idx; a.score = score; a.out = out;
@@ -207,7 +215,7 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
   a.n_splits = p.attn_splits; a.slots_per_split = p.slots_per_split;
   a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0; a.mode = p.attn_mode;
   if (p.attn_mode == 3)
-    return launch_decode(p, q_attn, k, v, nullptr, idx, score, nullptr, nullptr, out, ws, st);
+    return launch_decode(p, q_attn, k, v, nullptr, idx, score, nullptr, nullptr, out, ws, st, mk);
   if (p.attn_mode == 2) {
     ChunkArgs c;
     c.q_attn = q_attn; c.k = k; c.v = v; c.idx = idx; c.score = score; c.out = out;
@@ -222,9 +230,11 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
     c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
     c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
     c.attn_scale = p.attn_scale; c.qk_norm = p.qk_norm ? 1 : 0;
-    return launch_attend_chunk(c, p.D, p.G, st) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
+    return launch_attend_chunk(c, p.D, p.G, st, mk) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
   }
-  if (launch_attend(a, p.B, p.bf16, p.D, p.G, st) != hipSuccess) return HSA_ERR_DEVICE;
+  if (mk.rec(kStageAttend, 0, st) != hipSuccess || launch_attend(a, p.B, p.bf16, p.D, p.G, st) != hipSuccess ||
+      mk.rec(kStageAttend, 1, st) != hipSuccess)
+    return HSA_ERR_DEVICE;
   return HSA_OK;
 }
 
@@ -262,7 +272,7 @@ HSA_EXPORT hsa_status_t hsa_retrieve_topk(const hsa_shape_t* shape, const void* 
   if ((st = hsa::check_ptrs({q_ret, lm, topk_idx, topk_score})) != HSA_OK) return st;
   if ((st = hsa::check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
   return hsa::launch_retrieve(p, q_ret, landmarks, topk_idx, topk_score, ws,
-                              static_cast<hipStream_t>(stream), true);
+                              static_cast<hipStream_t>(stream), true, hsa::Marks{});
 }
 
 HSA_EXPORT hsa_status_t hsa_chunk_attend_blend(const hsa_shape_t* shape, const void* q_attn,
@@ -278,34 +288,60 @@ HSA_EXPORT hsa_status_t hsa_chunk_attend_blend(const hsa_shape_t* shape, const v
   if ((st = hsa::check_ptrs({q_attn, kk, vv, topk_idx, topk_score, out})) != HSA_OK) return st;
   if ((st = hsa::check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
   return hsa::launch_attend_blend(p, q_attn, k, v, topk_idx, topk_score, out, ws,
-                                  static_cast<hipStream_t>(stream));
+                                  static_cast<hipStream_t>(stream), hsa::Marks{});
 }
 
-HSA_EXPORT hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret,
-                                    const void* landmarks, const void* q_attn, const void* k,
-                                    const void* v, void* out, int32_t* topk_idx,
-                                    float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+namespace hsa {
+namespace {
+
+hsa_status_t forward_impl(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                          const void* q_attn, const void* k, const void* v, void* out,
+                          int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                          void* stream, const Marks& mk) {
   Plan p;
-  hsa_status_t st = hsa::make_plan(shape, &p, true);
+  hsa_status_t st = make_plan(shape, &p, true);
   if (st != HSA_OK) return st;
   const void* lm = p.Nc > 0 ? landmarks : q_ret;
   const void* kk = p.Lkv > 0 ? k : q_attn;
   const void* vv = p.Lkv > 0 ? v : q_attn;
-  if ((st = hsa::check_ptrs({q_ret, lm, q_attn, kk, vv, out})) != HSA_OK) return st;
+  if ((st = check_ptrs({q_ret, lm, q_attn, kk, vv, out})) != HSA_OK) return st;
   if ((topk_idx == nullptr) != (topk_score == nullptr)) return HSA_ERR_NULL_POINTER;
-  if (topk_idx && (st = hsa::check_ptrs({topk_idx, topk_score})) != HSA_OK) return st;
-  if ((st = hsa::check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
+  if (topk_idx && (st = check_ptrs({topk_idx, topk_score})) != HSA_OK) return st;
+  if ((st = check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
   char* w = static_cast<char*>(ws);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + p.off_idx);
   float* score = topk_score ? topk_score : reinterpret_cast<float*>(w + p.off_score);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.attn_mode == 3 && p.n_splits > 1) {   // decode: the attend merges the lists
-    if ((st = hsa::launch_retrieve(p, q_ret, landmarks, idx, score, ws, s, false)) != HSA_OK) return st;
-    return hsa::launch_decode(p, q_attn, k, v, reinterpret_cast<const uint64_t*>(w + p.off_lists),
-                              nullptr, nullptr, topk_idx, topk_score, out, ws, s);
+    if ((st = launch_retrieve(p, q_ret, landmarks, idx, score, ws, s, false, mk)) != HSA_OK) return st;
+    return launch_decode(p, q_attn, k, v, reinterpret_cast<const uint64_t*>(w + p.off_lists), nullptr,
+                         nullptr, topk_idx, topk_score, out, ws, s, mk);
   }
-  if ((st = hsa::launch_retrieve(p, q_ret, landmarks, idx, score, ws, s, true)) != HSA_OK) return st;
-  return hsa::launch_attend_blend(p, q_attn, k, v, idx, score, out, ws, s);
+  if ((st = launch_retrieve(p, q_ret, landmarks, idx, score, ws, s, true, mk)) != HSA_OK) return st;
+  return launch_attend_blend(p, q_attn, k, v, idx, score, out, ws, s, mk);
+}
+
+}  // namespace
+}  // namespace hsa
+
+HSA_EXPORT hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret,
+                                    const void* landmarks, const void* q_attn, const void* k,
+                                    const void* v, void* out, int32_t* topk_idx,
+                                    float* topk_score, void* ws, size_t ws_bytes, void* stream) {
+  return hsa::forward_impl(shape, q_ret, landmarks, q_attn, k, v, out, topk_idx, topk_score, ws,
+                           ws_bytes, stream, hsa::Marks{});
+}
+
+HSA_EXPORT hsa_status_t hsa_forward_profiled(const hsa_shape_t* shape, const void* q_ret,
+                                             const void* landmarks, const void* q_attn,
+                                             const void* k, const void* v, void* out,
+                                             int32_t* topk_idx, float* topk_score, void* ws,
+                                             size_t ws_bytes, void* stream,
+                                             void* const* stage_events) {
+  hsa::Marks mk;
+  mk.ev = stage_events;
+  return hsa::forward_impl(shape, q_ret, landmarks, q_attn, k, v, out, topk_idx, topk_score, ws,
+                           ws_bytes, stream, mk);
 }
 
 HSA_EXPORT const char* hsa_status_string(hsa_status_t status) {

@@ -7,6 +7,22 @@
 
 namespace hsa {
 
+// Kernel stages that a caller may bracket with its own HIP events (the order of
+// HSA_STAGE_* in hsa.h).
+enum Stage { kStageScan = 0, kStageMerge = 1, kStageBucket = 2, kStageAttend = 3, kStageCombine = 4,
+             kStages = 5 };
+
+// Optional caller-owned events: ev[2*stage] is recorded on the launch stream
+// before the stage's first kernel, ev[2*stage + 1] after its last.  Null
+// entries (or a null array) record nothing.  The library keeps no reference.
+struct Marks {
+  void* const* ev = nullptr;
+  hipError_t rec(int stage, int end, hipStream_t st) const {
+    if (ev == nullptr || ev[2 * stage + end] == nullptr) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[2 * stage + end]), st);
+  }
+};
+
 // Landmark scan + per-split top-K (Steps 1-2).
 struct ScanArgs {
   const void* q_ret;      // [B, Lq, Hkv, D]
@@ -98,7 +114,7 @@ hipError_t launch_attend(const AttendArgs& a, int64_t B, bool bf16, int D, int G
 hipError_t launch_merge_lists(const MergeArgs& a, hipStream_t st);
 hipError_t launch_attend_decode(const DecodeArgs& a, int64_t rows, int D, int G, hipStream_t st);
 int decode_slots_per_block();
-hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st);
+hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk);
 int64_t chunk_pairs_per_item();
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 
