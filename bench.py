@@ -49,7 +49,7 @@ WORKLOADS = {"prefill_128K": 2, "decode_16M": 3}
 KERNELS = {
     ("decode_16M", "scan"): "scan_wide_kernel<true, 128>",
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
-    ("prefill_128K", "scan"): "scan_topk_kernel<true, 128>",
+    ("prefill_128K", "scan"): "scan_block_kernel<128>",
     ("prefill_128K", "bucket"): "chunk_count/scan/scatter kernels",
     ("prefill_128K", "attend"): "chunk_attend_kernel<128, 8>",
     ("prefill_128K", "combine"): "chunk_combine_kernel<128, 8>",

@@ -246,10 +246,38 @@ def test_chunk_attend_blend_entry_with_given_selection(hsa):
 
 
 def test_many_row_blocks_one_wave_scan(hsa):
-    """More than 2048 blocks of 16 rows: the one-wave-per-16-rows scan path."""
-    cfg = small(batch=1, n_kv_heads=4, n_q_heads=8, q_len=8256, kv_len=8256, top_k=8, head_dim=64)
+    """More than 2048 blocks of 16 rows in fp32: the one-wave-per-16-rows scan path."""
+    cfg = small(batch=1, n_kv_heads=4, n_q_heads=8, q_len=8256, kv_len=8256, top_k=8, head_dim=64,
+                dtype="f32")
     inp = W.generate(cfg)
     parity(hsa, inp, rows=sample_rows(cfg, 400))
+
+
+@pytest.mark.parametrize("d,K", [(64, 8), (128, 32), (128, 1)])
+def test_block_scan_many_rows(hsa, d, K):
+    """More than 2048 blocks of 16 rows in bf16 with K <= 32: the block scan
+    (64 rows per workgroup); ragged rows, history and first position, early
+    rows with fewer than K (or no) eligible chunks."""
+    cfg = small(batch=1, n_kv_heads=4, n_q_heads=8, q_len=8250, kv_len=8300, q_pos0=37, top_k=K,
+                head_dim=d)
+    inp = W.generate(cfg)
+    rows = np.union1d(sample_rows(cfg, 300, seed=d + K), np.arange(0, 200, 7))
+    parity(hsa, inp, rows=rows)
+
+
+def test_block_scan_long_rows(hsa):
+    """Block scan over ~2000 chunks per row: many LDS tiles and candidate cuts."""
+    cfg = small(batch=1, n_kv_heads=1, n_q_heads=8, q_len=33000, q_pos0=98304, kv_len=131304,
+                top_k=16, head_dim=128)
+    inp = W.generate(cfg)
+    parity(hsa, inp, rows=sample_rows(cfg, 200, seed=5))
+
+
+def test_block_scan_ties_exact(hsa):
+    """Block scan with K = 32 on integer-valued scores full of ties: exact order."""
+    cfg = small(batch=2, n_kv_heads=2, n_q_heads=4, q_len=8256, kv_len=8256, top_k=32, head_dim=64)
+    inp = W.generate(cfg, mode="grid_small")
+    parity(hsa, inp, rows=sample_rows(cfg, 150), exact=True, ret_scale=0.125)
 
 
 # ----------------------------------------------------------------------------

@@ -31,34 +31,141 @@ __device__ __forceinline__ int64_t bin_of(int64_t row, int32_t c, const ChunkArg
   return bg * a.Nc + c;
 }
 
-// --- count: blend weights and pairs per bin (one wave per row) --------------
+// Rows are laid out on segments of S lanes (S = the smallest power of two
+// >= K), so a wave holds 64 / S rows and a workgroup 256 / S.
+__device__ __forceinline__ int seg_lanes(int K) { return K <= 1 ? 1 : 1 << (32 - __clz(K - 1)); }
+
+// --- count: blend weights and pairs per bin (one lane per slot) ------------
 __global__ __launch_bounds__(256) void chunk_count_kernel(ChunkArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
-  const int K = a.K;
-  const int32_t c = lane < K ? a.idx[row * K + lane] : -1;
-  const float s = lane < K ? a.score[row * K + lane] : 0.f;
-  const bool valid = c >= 0 && (int64_t)c < a.Nc;
-  const float mx = wave_max(valid ? s : -INFINITY);
+  const int K = a.K, S = seg_lanes(K);
+  const int64_t row = (int64_t)blockIdx.x * (256 / S) + threadIdx.x / S;
+  const int k = threadIdx.x & (S - 1);
+  const bool active = row < a.rows && k < K;
+  int32_t c = -1;
+  float s = 0.f;
+  if (active) {
+    c = a.idx[row * K + k];
+    s = a.score[row * K + k];
+  }
+  const bool valid = active && c >= 0 && (int64_t)c < a.Nc;
+  // xor butterflies: every lane of a segment ends with the same (commutative) result
+  float mx = valid ? s : -INFINITY;
+  for (int o = 1; o < S; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
   const float ex = valid ? expf(s - mx) : 0.f;
-  const float den = wave_sum(ex);
-  if (lane < K) a.wts[row * K + lane] = valid ? ex / den : 0.f;
+  float den = ex;
+  for (int o = 1; o < S; o <<= 1) den += __shfl_xor(den, o, kWave);
+  if (active) a.wts[row * K + k] = valid ? ex / den : 0.f;
   if (valid) atomicAdd(&a.counts[bin_of(row, c, a)], 1u);
 }
 
+// --- bucketing through a workgroup histogram in LDS --------------------------
+// A workgroup takes kBucketRows query rows of one (batch, kv head), counts its
+// pairs per chunk in LDS and adds each nonzero count to the global bin once, so
+// global atomics drop from one per pair to one per (workgroup, chunk).  Used
+// when the chunks of one (batch, kv head) fit the LDS histogram.
+constexpr int kBucketRows = 1024;
+constexpr int kHistMax = 16384;
+constexpr int kBucketBatch = 4;          // row passes whose loads are issued together
+
+struct BucketRange {
+  int64_t bg, r0, r1;                    // (batch, kv head) and query rows [r0, r1)
+  int b, g;
+};
+__device__ __forceinline__ BucketRange bucket_range(const ChunkArgs& a) {
+  BucketRange br;
+  const int64_t rbk = (a.Lq + kBucketRows - 1) / kBucketRows;
+  br.bg = (int64_t)blockIdx.x / rbk;
+  br.r0 = ((int64_t)blockIdx.x % rbk) * kBucketRows;
+  br.r1 = min(br.r0 + kBucketRows, a.Lq);
+  br.b = (int)(br.bg / a.Hkv);
+  br.g = (int)(br.bg % a.Hkv);
+  return br;
+}
+
+// Calls fn(row, slot, chunk, valid) for every slot of the range's rows; rows
+// sit on segments of S lanes, kBucketBatch passes per load batch.  Every lane
+// takes part in every call (the count uses segment shuffles).
+template <class F>
+__device__ __forceinline__ void for_range_slots(const ChunkArgs& a, const BucketRange& br, F&& fn) {
+  const int K = a.K, S = seg_lanes(K), per = 256 / S;
+  const int k = threadIdx.x & (S - 1);
+  for (int64_t base = br.r0; base < br.r1; base += (int64_t)per * kBucketBatch) {
+    int32_t c[kBucketBatch];
+    int64_t row[kBucketBatch];
+    bool act[kBucketBatch];
+#pragma unroll
+    for (int u = 0; u < kBucketBatch; ++u) {
+      const int64_t r = base + (int64_t)u * per + threadIdx.x / S;
+      act[u] = r < br.r1 && k < K;
+      row[u] = ((int64_t)br.b * a.Lq + (act[u] ? r : br.r0)) * a.Hkv + br.g;
+      c[u] = act[u] ? a.idx[row[u] * K + k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBucketBatch; ++u)
+      fn(row[u], k, c[u], act[u], act[u] && c[u] >= 0 && (int64_t)c[u] < a.Nc);
+  }
+}
+
+__global__ __launch_bounds__(256) void chunk_count_lds_kernel(ChunkArgs a) {
+  extern __shared__ uint32_t hist[];
+  const BucketRange br = bucket_range(a);
+  for (int64_t i = threadIdx.x; i < a.Nc; i += 256) hist[i] = 0u;
+  __syncthreads();
+  const int S = seg_lanes(a.K);
+  for_range_slots(a, br, [&](int64_t row, int k, int32_t c, bool active, bool valid) {
+    const float s = active ? a.score[row * a.K + k] : 0.f;
+    float mx = valid ? s : -INFINITY;
+    for (int o = 1; o < S; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    const float ex = valid ? expf(s - mx) : 0.f;
+    float den = ex;
+    for (int o = 1; o < S; o <<= 1) den += __shfl_xor(den, o, kWave);
+    if (active) a.wts[row * a.K + k] = valid ? ex / den : 0.f;
+    if (valid) atomicAdd(&hist[c], 1u);
+  });
+  __syncthreads();
+  uint32_t* cnt = a.counts + br.bg * a.Nc;
+  for (int64_t i = threadIdx.x; i < a.Nc; i += 256)
+    if (hist[i] != 0u) atomicAdd(&cnt[i], hist[i]);
+}
+
+__global__ __launch_bounds__(256) void chunk_scatter_lds_kernel(ChunkArgs a) {
+  extern __shared__ uint32_t hist[];
+  const BucketRange br = bucket_range(a);
+  for (int64_t i = threadIdx.x; i < a.Nc; i += 256) hist[i] = 0u;
+  __syncthreads();
+  for_range_slots(a, br, [&](int64_t, int, int32_t c, bool, bool valid) {
+    if (valid) atomicAdd(&hist[c], 1u);
+  });
+  __syncthreads();
+  // reserve this workgroup's run in every bin it touches
+  uint32_t* cur = a.cursor + br.bg * a.Nc;
+  for (int64_t i = threadIdx.x; i < a.Nc; i += 256)
+    if (hist[i] != 0u) hist[i] = atomicAdd(&cur[i], hist[i]);
+  __syncthreads();
+  for_range_slots(a, br, [&](int64_t row, int k, int32_t c, bool, bool valid) {
+    if (valid) a.pairs[atomicAdd(&hist[c], 1u)] = (uint32_t)(row * a.K + k);
+  });
+}
+
 // --- scan: bin offsets, scatter cursors, work items (one workgroup) ----------
+// Thread t owns a contiguous range of bins; counts are read 16 at a time so
+// the loads of a batch are all in flight together.
 __global__ __launch_bounds__(1024) void chunk_scan_kernel(ChunkArgs a) {
   __shared__ uint32_t sp[1024], si[1024];
   const int t = threadIdx.x;
   const int64_t n = a.n_bins;
   const int64_t seg = (n + 1023) / 1024;
-  const int64_t lo = t * seg, hi = min(n, lo + seg);
+  const int64_t lo = min(n, t * seg), hi = min(n, lo + seg);
   uint32_t tp = 0, ti = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    const uint32_t c = a.counts[i];
-    tp += c;
-    ti += (c + kPairs - 1) / kPairs;
+  for (int64_t i0 = lo; i0 < hi; i0 += 16) {
+    uint32_t c[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[i0 + u] : 0u;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      tp += c[u];
+      ti += (c[u] + kPairs - 1) / kPairs;
+    }
   }
   sp[t] = tp;
   si[t] = ti;
@@ -71,15 +178,23 @@ __global__ __launch_bounds__(1024) void chunk_scan_kernel(ChunkArgs a) {
     __syncthreads();
   }
   uint32_t rp = sp[t] - tp, ri = si[t] - ti;
-  for (int64_t i = lo; i < hi; ++i) {
-    const uint32_t c = a.counts[i];
-    a.offsets[i] = rp;
-    a.cursor[i] = rp;
-    const uint32_t ni = (c + kPairs - 1) / kPairs;
-    for (uint32_t j = 0; j < ni; ++j) a.items[ri + j] = (uint64_t)i | ((uint64_t)j << 32);
-    rp += c;
-    ri += ni;
-    a.counts[i] = 0u;                    // ready for the next call
+  for (int64_t i0 = lo; i0 < hi; i0 += 16) {
+    uint32_t c[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[i0 + u] : 0u;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t i = i0 + u;
+      if (i < hi) {
+        a.offsets[i] = rp;
+        a.cursor[i] = rp;
+        a.counts[i] = 0u;                // ready for the next call
+        const uint32_t ni = (c[u] + kPairs - 1) / kPairs;
+        for (uint32_t jb = 0; jb < ni; ++jb) a.items[ri + jb] = (uint64_t)i | ((uint64_t)jb << 32);
+        rp += c[u];
+        ri += ni;
+      }
+    }
   }
   if (t == 1023) {
     a.offsets[n] = rp;
@@ -87,16 +202,16 @@ __global__ __launch_bounds__(1024) void chunk_scan_kernel(ChunkArgs a) {
   }
 }
 
-// --- scatter: pair ids into bins (one wave per row) --------------------------
+// --- scatter: pair ids into bins (one lane per slot) -----------------------
 __global__ __launch_bounds__(256) void chunk_scatter_kernel(ChunkArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
-  const int K = a.K;
-  const int32_t c = lane < K ? a.idx[row * K + lane] : -1;
+  const int K = a.K, S = seg_lanes(K);
+  const int64_t row = (int64_t)blockIdx.x * (256 / S) + threadIdx.x / S;
+  const int k = threadIdx.x & (S - 1);
+  if (row >= a.rows || k >= K) return;
+  const int32_t c = a.idx[row * K + k];
   if (c >= 0 && (int64_t)c < a.Nc) {
     const uint32_t pos = atomicAdd(&a.cursor[bin_of(row, c, a)], 1u);
-    a.pairs[pos] = (uint32_t)(row * K + lane);
+    a.pairs[pos] = (uint32_t)(row * K + k);
   }
 }
 
@@ -351,12 +466,18 @@ hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st,
   hipError_t e;
   if ((e = mk.rec(kStageBucket, 0, st)) != hipSuccess) return e;
   if ((e = launch_fill_u32(a.counts, a.n_bins, 0u, st)) != hipSuccess) return e;
-  const unsigned row_blocks = (unsigned)((a.rows + 3) / 4);
-  hipLaunchKernelGGL(chunk_count_kernel, dim3(row_blocks), dim3(256), 0, st, a);
+  const bool lds = a.Nc <= kHistMax;
+  const int64_t seg = a.K <= 1 ? 1 : (int64_t)1 << (32 - __builtin_clz((unsigned)a.K - 1));
+  const unsigned row_blocks = (unsigned)((a.rows + 256 / seg - 1) / (256 / seg));
+  const unsigned range_blocks = (unsigned)((a.Lq + kBucketRows - 1) / kBucketRows * (a.rows / a.Lq));
+  const size_t hist_bytes = (size_t)a.Nc * 4;
+  if (lds) hipLaunchKernelGGL(chunk_count_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
+  else hipLaunchKernelGGL(chunk_count_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(1024), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, a);
+  if (lds) hipLaunchKernelGGL(chunk_scatter_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
+  else hipLaunchKernelGGL(chunk_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mk.rec(kStageBucket, 1, st)) != hipSuccess) return e;
 #define HSA_CHUNK_CASE(DD, GG) \

@@ -27,7 +27,8 @@ struct Plan {
   int64_t rows;          // B * Lq * Hkv selection rows
   int32_t n_max;         // max eligible chunks over all query rows
   int32_t split_len, n_splits;
-  bool wide;             // few-row scan: 16-wave workgroups, last-arriver merge
+  bool wide;             // few-row scan: 16-wave workgroups, per-split lists
+  bool block;            // many-row scan (bf16, K <= 32): 64 rows per workgroup
   int32_t attn_splits, slots_per_split, attn_mode;
   int64_t n_bins, max_items;   // chunk-major attend
   size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
@@ -80,13 +81,15 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
   const int64_t nmax = std::min<int64_t>(last_pos / HSA_CHUNK_TOKENS, Nc);
   p->n_max = (int32_t)nmax;
   // Scan plan.  Up to 2048 row blocks of 16 rows: the wide kernel (1024 chunks
-  // per workgroup; with several splits the last workgroup of each row block
-  // merges).  More row blocks than that: one wave per 16 rows over all chunks.
+  // per workgroup; with several splits a merge combines the per-split lists).
+  // More row blocks than that: bf16 with K <= 32 takes the block kernel (64
+  // rows per workgroup over all their chunks); otherwise one wave per 16 rows.
   const int64_t row_blocks = (s->q_len + kRowsPerWave - 1) / kRowsPerWave * s->batch * s->n_kv_heads;
   if (row_blocks > INT32_MAX) return HSA_ERR_BAD_SHAPE;
   const int64_t wchunks = 1024;
   const int64_t wsplits = std::max<int64_t>(1, (nmax + wchunks - 1) / wchunks);
   p->wide = row_blocks <= kScanCounters && wsplits <= kMaxSplits;
+  p->block = !p->wide && p->bf16 && p->K <= scan_block_max_k();
   p->split_len = (int32_t)(p->wide ? wchunks : std::max<int64_t>(64, (nmax + 63) / 64 * 64));
   p->n_splits = (int32_t)(p->wide ? wsplits : 1);
 
@@ -169,8 +172,9 @@ hsa_status_t launch_retrieve(const Plan& p, const void* q_ret, const void* landm
   a.Lq = p.Lq; a.q_pos0 = p.q_pos0; a.Nc = p.Nc; a.Hkv = p.Hkv; a.K = p.K;
   a.n_max = p.n_max; a.split_len = p.split_len; a.n_splits = p.n_splits; a.ret_scale = p.ret_scale;
   if (mk.rec(kStageScan, 0, st) != hipSuccess) return HSA_ERR_DEVICE;
-  const hipError_t e = p.wide ? launch_scan_wide(a, p.B, p.bf16, p.D, st)
-                             : launch_scan(a, p.B, p.bf16, p.D, st);
+  const hipError_t e = p.wide    ? launch_scan_wide(a, p.B, p.bf16, p.D, st)
+                       : p.block ? launch_scan_block(a, p.B, p.D, st)
+                                 : launch_scan(a, p.B, p.bf16, p.D, st);
   if (e != hipSuccess || mk.rec(kStageScan, 1, st) != hipSuccess) return HSA_ERR_DEVICE;
   if (merge && p.n_splits > 1) {
     MergeArgs m;

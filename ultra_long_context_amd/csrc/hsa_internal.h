@@ -110,6 +110,8 @@ struct ChunkArgs {
 hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 int scan_wide_chunks();
+hipError_t launch_scan_block(const ScanArgs& a, int64_t B, int D, hipStream_t st);
+int scan_block_max_k();
 hipError_t launch_attend(const AttendArgs& a, int64_t B, bool bf16, int D, int G, hipStream_t st);
 hipError_t launch_merge_lists(const MergeArgs& a, hipStream_t st);
 hipError_t launch_attend_decode(const DecodeArgs& a, int64_t rows, int D, int G, hipStream_t st);

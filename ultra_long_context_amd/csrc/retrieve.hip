@@ -458,6 +458,297 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
   if (rw_ok && lane < K) a.lists[(row_flat * a.n_splits + s) * K + lane] = lane < m ? top[w][lane] : 0ull;
 }
 
+// ---------------------------------------------------------------------------
+// Block scan: many query rows (prefill), bf16, K <= 32.
+//
+// A workgroup of 4 waves takes 64 consecutive query rows of one (batch, kv
+// head); they share their eligible chunk range up to one chunk.  Landmark tiles
+// of 64 chunks go through LDS (double-buffered: the next tile's global loads
+// are in flight while the current one is scored), so a landmark leaves L2 once
+// per 64 rows and pass.  Wave w scores its 16 rows with
+// v_mfma_f32_16x16x32_bf16 (A = landmarks from LDS, B = the rows' retrieval
+// queries): lane l holds row l & 15 and chunks 4*(l >> 4) + i of each
+// 16-chunk sub-tile.
+//   pass 1  keeps, per lane, the running maximum of 16 chunk groups (64 groups
+//           per row).  K distinct chunks reach the K-th largest group maximum,
+//           so it bounds the row's K-th score from below; the bound is taken
+//           on the upper 16 bits of the ordering key (still a lower bound).
+//   pass 2  rescores and appends each chunk at or above the bound to the row's
+//           LDS slots as (score, chunk); each lane of a row owns every 4th slot
+//           past the row's kept entries, so appends need no cross-lane count.
+//           If slots run low, the row is cut to its exact top K and, since
+//           later chunks lose ties, the bound rises strictly above the K-th.
+//   final   exact top K per row, rank sort, write.
+// Cuts work in a quad layout (lane l holds row l >> 2, slots (l & 3) + 4s), so
+// per-row counts are two DPP adds.  Rows are wave-local: the selection needs
+// no workgroup barrier.
+// ---------------------------------------------------------------------------
+constexpr int kBlkWaves = 4;
+constexpr int kBlkRows = kBlkWaves * kRows;     // query rows per workgroup
+constexpr int kTile = 64;                       // chunks per LDS tile
+constexpr int kBlkCap = 64;                     // candidate slots per row
+constexpr int kBlkStride = kBlkCap + 1;         // padded: a wave's 16 rows start on different banks
+constexpr int kBlkMaxK = 32;                    // a cut leaves >= 32 free slots
+constexpr uint64_t kEmpty = ~0ull;              // free slot: chunk field 0xFFFFFFFF
+
+// Sum over the 4 lanes of a quad (DPP, no LDS).
+__device__ __forceinline__ int quad_total(int v) {
+  v += dpp_i<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_i<0x4E>(v);    // quad_perm [2,3,0,1]
+  return v;
+}
+// Value of quad lane q (0..3) in every lane of the quad.
+template <int Q>
+__device__ __forceinline__ int quad_get(int v) {
+  return dpp_i<Q * 0x55>(v);   // quad_perm [Q,Q,Q,Q]
+}
+// Sum over the 4 lanes (j = 0..3) that hold a row in the MFMA layout.
+__device__ __forceinline__ int row_total(int v) {
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// Smallest float above x (x not NaN; +inf stays +inf): one step along the
+// IEEE-754 ordering of the bit patterns.
+__device__ __forceinline__ float float_above(float x) {
+  const uint32_t b = __float_as_uint(x);
+  if (x == 0.0f) return __uint_as_float(1u);
+  if (b == 0x7F800000u) return x;
+  return __uint_as_float((b & 0x80000000u) ? b - 1u : b + 1u);
+}
+
+// A slot holds (score bits << 32) | chunk; its ordering key is the packed candidate.
+__device__ __forceinline__ uint64_t slot_cand(uint64_t s) {
+  return s == kEmpty ? 0ull : pack_cand(score_key(__uint_as_float((uint32_t)(s >> 32))), (uint32_t)s);
+}
+__device__ __forceinline__ uint64_t make_slot(float score, uint32_t chunk) {
+  return ((uint64_t)__float_as_uint(score) << 32) | chunk;
+}
+
+// Exact K-th largest of each quad row's register-held candidates e[0..16)
+// (unique nonzero keys, zeros ignored); 0 when the row holds at most K.
+__device__ __forceinline__ uint64_t quad_kth(const uint64_t (&e)[16], int n, int K) {
+  if (!__any(n > K)) return 0ull;
+  uint32_t t32 = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t32 | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) c += cand_key(e[s]) >= cand;
+    if (quad_total(c) >= K) t32 = cand;
+  }
+  int above = 0, at = 0;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    above += cand_key(e[s]) > t32;
+    at += e[s] != 0ull && cand_key(e[s]) == t32;
+  }
+  above = quad_total(above);
+  at = quad_total(at);
+  const int need = K - above;            // candidates taken at key t32 (<= at)
+  uint32_t tl = 0;
+  if (__any(n > K && at > need)) {       // ties at the K-th key: lower chunk index first
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tl | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) c += e[s] != 0ull && cand_key(e[s]) == t32 && (uint32_t)e[s] >= cand;
+      if (quad_total(c) >= need) tl = cand;
+    }
+  }
+  if (at <= need) tl = 0;
+  return n > K ? (((uint64_t)t32 << 32) | tl) : 0ull;
+}
+
+// Cuts every row of the wave (quad layout: rows[rq]) to its exact top K.
+// Rewrites the row as kept slots [0, m) and free slots after; returns m.  kth
+// receives the row's K-th candidate (0 if the row held at most K).
+__device__ __forceinline__ int block_cut(uint64_t* row, int K, int jq, uint64_t& kth, bool packed_out) {
+  uint64_t e[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) e[s] = slot_cand(row[jq + 4 * s]);
+  int nz = 0;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) nz += e[s] != 0ull;
+  const int n = quad_total(nz);
+  kth = quad_kth(e, n, K);
+  const uint64_t t = kth != 0ull ? kth : 1ull;
+  int kept = 0;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) kept += e[s] >= t;
+  const int k0 = quad_get<0>(kept), k1 = quad_get<1>(kept), k2 = quad_get<2>(kept);
+  int off = (jq > 0 ? k0 : 0) + (jq > 1 ? k1 : 0) + (jq > 2 ? k2 : 0);
+  const int m = n > K ? K : n;
+  // every slot of the row is in registers: free the tail, then write the kept
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    if (jq + 4 * s >= m) row[jq + 4 * s] = kEmpty;
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    if (e[s] >= t)
+      row[off++] = packed_out ? e[s]
+                              : make_slot(key_score(cand_key(e[s])), cand_chunk(e[s]));
+  return m;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
+  constexpr int LROW = D + 8;            // bf16 per landmark row in LDS (16-byte pad)
+  constexpr int RU = D / 8;              // 16-byte units per landmark
+  constexpr int NU = kTile * RU / 256;   // 16-byte tile loads per thread
+  constexpr int KSTEP = D / 32;
+  __shared__ __align__(16) uint16_t lmt[2][kTile * LROW];
+  __shared__ uint64_t buf[kBlkWaves][kRows * kBlkStride];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int qrow = lane & 15, j = lane >> 4;     // MFMA layout
+  const int rq = lane >> 2, jq = lane & 3;       // quad layout
+  // consecutive workgroups: the same row block of successive (batch, kv head)
+  // pairs (each XCD keeps to the landmarks of one pair), latest rows first
+  const int64_t rbk = (a.Lq + kBlkRows - 1) / kBlkRows;
+  const int64_t nbg = (int64_t)gridDim.x / rbk;
+  const int bg = (int)((int64_t)blockIdx.x % nbg);
+  const int64_t rb = rbk - 1 - (int64_t)blockIdx.x / nbg;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int64_t r0 = rb * kBlkRows, rw0 = r0 + w * kRows;
+  auto limit = [&](int64_t r) -> int {   // chunks [0, limit) are eligible for row r
+    if (r >= a.Lq) return 0;
+    const int64_t n = (a.q_pos0 + r) / kChunk;
+    return (int)(n < a.Nc ? n : a.Nc);
+  };
+  const int64_t r = rw0 + qrow;
+  const int lim = limit(r);
+  const int c_stop = limit(min(r0 + kBlkRows - 1, a.Lq - 1));   // the block's last row sees the most
+  const int w_stop = rw0 < a.Lq ? limit(min(rw0 + kRows - 1, a.Lq - 1)) : 0;
+  const int w_min = rw0 + kRows <= a.Lq ? limit(rw0) : 0;       // every row of the wave sees [0, w_min)
+
+  QOperand<true, D> q;
+  q.load(reinterpret_cast<const uint16_t*>(a.q_ret) + ((b * a.Lq + (r < a.Lq ? r : 0)) * a.Hkv + g) * D,
+         r < a.Lq, j);
+  const uint16_t* lm = reinterpret_cast<const uint16_t*>(a.landmarks) + (int64_t)bg * a.Nc * D;
+  const int n_tiles = (c_stop + kTile - 1) / kTile;
+  const int K = a.K;
+
+  uint4 pre[NU];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int qi = tid * NU + u;
+      const int c = t * kTile + qi / RU;
+      pre[u] = make_uint4(0, 0, 0, 0);
+      if (c < c_stop) pre[u] = *reinterpret_cast<const uint4*>(lm + (int64_t)c * D + (qi % RU) * 8);
+    }
+  };
+  auto store_tile = [&](int bi) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int qi = tid * NU + u;
+      *reinterpret_cast<uint4*>(&lmt[bi][(qi / RU) * LROW + (qi % RU) * 8]) = pre[u];
+    }
+  };
+  // one pass over the tiles; fn(sub-tile scores, first chunk, whole sub-tile eligible for every row)
+  auto sweep = [&](auto&& fn) {
+    if (n_tiles > 0) {
+      load_tile(0);
+      store_tile(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      if (t + 1 < n_tiles) load_tile(t + 1);
+      const uint16_t* L = lmt[t & 1];
+#pragma unroll
+      for (int sub = 0; sub < kTile / 16; ++sub) {
+        const int cs = t * kTile + 16 * sub;
+        if (cs >= w_stop) break;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KSTEP; ++k) {
+          const uint4 x = *reinterpret_cast<const uint4*>(L + (16 * sub + qrow) * LROW + 32 * k + 8 * j);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), q.v[k], acc, 0, 0, 0);
+        }
+        fn(acc, sub, cs, cs + 16 <= w_min);
+      }
+      if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+      __syncthreads();
+    }
+  };
+
+  // --- pass 1: group maxima, then a lower bound of each row's K-th key -------
+  float gm[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) gm[x] = -INFINITY;
+  sweep([&](const floatx4& acc, int sub, int cs, bool all) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (all || cs + 4 * j + i < lim) gm[4 * sub + i] = fmaxf(gm[4 * sub + i], acc[i]);
+  });
+  uint32_t t16 = 0;
+  {
+    uint32_t hk[16];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)   // group (sub, i) is empty unless its first chunk is eligible
+        hk[4 * sub + i] = 16 * sub + 4 * j + i < lim ? score_key(gm[4 * sub + i]) >> 16 : 0u;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = t16 | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) c += hk[x] >= cand;
+      if (row_total(c) >= K) t16 = cand;
+    }
+  }
+  // keys at or above t16 << 16 are the scores at or above lo (keys up to that
+  // of -inf: every score)
+  float lo = t16 <= 0x7Fu ? -INFINITY : key_score(t16 << 16);
+
+  // --- pass 2: candidates at or above the bound -----------------------------
+  uint64_t* rows = &buf[w][0];
+  uint64_t* qrowbuf = rows + rq * kBlkStride;    // quad layout row
+  uint64_t* mrowbuf = rows + qrow * kBlkStride;  // MFMA layout row
+#pragma unroll
+  for (int s = 0; s < 16; ++s) qrowbuf[jq + 4 * s] = kEmpty;
+  int m = 0, cj = 0;     // kept entries of the row; this lane's appends after them
+  sweep([&](const floatx4& acc, int sub, int cs, bool all) {
+    if (__any(m + j + 4 * cj + 12 >= kBlkCap)) {
+      uint64_t kth;
+      const int mq = block_cut(qrowbuf, K, jq, kth, false);
+      // later chunks lose ties with the row's K-th: the bound becomes strict
+      const float loq = kth != 0ull ? float_above(key_score(cand_key(kth))) : -INFINITY;
+      m = __shfl(mq, 4 * qrow, kWave);
+      lo = fmaxf(lo, __shfl(loq, 4 * qrow, kWave));
+      cj = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = cs + 4 * j + i;
+      if ((all || c < lim) && acc[i] >= lo) {
+        mrowbuf[m + j + 4 * cj] = make_slot(acc[i], (uint32_t)c);
+        ++cj;
+      }
+    }
+  });
+
+  // --- final: exact top K, rank sort, write ---------------------------------
+  uint64_t kth;
+  const int mq = block_cut(qrowbuf, K, jq, kth, true);
+  const int64_t rrow = rw0 + rq;
+  if (rrow >= a.Lq) return;
+  const int64_t row_flat = (b * a.Lq + rrow) * a.Hkv + g;
+  for (int p = jq; p < mq; p += 4) {
+    const uint64_t e = qrowbuf[p];
+    int rank = 0;
+    for (int o = 0; o < mq; ++o) rank += qrowbuf[o] > e;
+    a.out_idx[row_flat * K + rank] = (int32_t)cand_chunk(e);
+    a.out_score[row_flat * K + rank] = key_score(cand_key(e)) * a.ret_scale;
+  }
+  for (int k = mq + ((jq - mq) & 3); k < K; k += 4) {
+    a.out_idx[row_flat * K + k] = -1;
+    a.out_score[row_flat * K + k] = -INFINITY;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st) {
@@ -491,6 +782,17 @@ hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipS
 }
 
 int scan_wide_chunks() { return kWideChunks; }
+
+int scan_block_max_k() { return kBlkMaxK; }
+
+hipError_t launch_scan_block(const ScanArgs& a, int64_t B, int D, hipStream_t st) {
+  if (a.K > kBlkMaxK) return hipErrorInvalidValue;
+  const int64_t rbk = (a.Lq + kBlkRows - 1) / kBlkRows;
+  const dim3 grid((unsigned)(rbk * B * a.Hkv), 1, 1), block(kBlkWaves * 64, 1, 1);
+  if (D == 128) hipLaunchKernelGGL((scan_block_kernel<128>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((scan_block_kernel<64>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
 
 
 }  // namespace hsa
