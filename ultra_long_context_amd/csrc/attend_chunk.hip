@@ -235,20 +235,15 @@ __device__ __forceinline__ void load_q_tile(const ChunkArgs& a, const uint32_t* 
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   constexpr int KROW = D + 8;          // bf16 elements per K row in LDS (16-byte pad)
   constexpr int VROW = kChunk + 8;     // bf16 elements per V^T row
-  constexpr int PROW = kChunk + 8;     // bf16 elements per P row
-  constexpr int OROW = D + 8;          // fp16 elements per staged output row
   constexpr int PT = 16 / G;           // pairs per MFMA tile (16 head-rows)
   constexpr int KSTEP = D / 32;        // MFMA K-steps over the head dimension
   constexpr int NT = D / 16;           // output dimension tiles
   __shared__ __align__(16) uint16_t ks[kChunk * KROW];
   __shared__ __align__(16) uint16_t vt[D * VROW];
   __shared__ float rk[kChunk];
-  __shared__ __align__(16) uint16_t ps[4][16 * PROW];
-  __shared__ __align__(16) uint16_t ob[4][16 * OROW];
-  __shared__ float rqs[4][16];
   __shared__ uint32_t pid_s[kPairs];
   __shared__ float w_s[kPairs];
 
@@ -265,7 +260,9 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const int64_t c = bin - bg * a.Nc;
   const int g = (int)(bg % a.Hkv);
 
-  // pair ids and blend weights of the item; K (row-major) and V^T in LDS
+  // pair ids and blend weights of the item; K (row-major) and V^T in LDS.
+  // V^T columns are permuted inside each 32-key block (key 16h + 4q + r sits
+  // at 8q + 4h + r) so that the P.V operands line up with the S^T accumulators.
   if (tid < n_pairs) {
     const uint32_t pid = a.pairs[p_begin + tid];
     pid_s[tid] = pid;
@@ -275,24 +272,41 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
     const int64_t base = (bg * a.Lkv + c * kChunk) * D;
     const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k) + base);
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v) + base;
-    constexpr int NV = kChunk * D / 8 / 256;
-    uint4 kx[NV], vx[NV];
+    constexpr int NK = kChunk * D / 8 / 256;          // 16-byte K pieces per thread
+    constexpr int NV = (16 * (D / 8) + 255) / 256;    // (4 keys x 8 dims) V blocks per thread
+    uint4 kx[NK], vx[NV][4];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) kx[i] = kp[tid + 256 * i];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      kx[i] = kp[tid + 256 * i];
-      const int key = tid & 63, dg = (tid >> 6) + 4 * i;       // lane = key: transposed writes
-      vx[i] = *reinterpret_cast<const uint4*>(vp + key * D + 8 * dg);
+      const int u = tid + 256 * i, kq = u & 15, dg = u >> 4;
+      if (dg < D / 8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vx[i][r] = *reinterpret_cast<const uint4*>(vp + (4 * kq + r) * D + 8 * dg);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = (tid + 256 * i) * 8;
+      *reinterpret_cast<uint4*>(&ks[(e / D) * KROW + e % D]) = kx[i];
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = (tid + 256 * i) * 8;
-      *reinterpret_cast<uint4*>(&ks[(e / D) * KROW + e % D]) = kx[i];
-      const int key = tid & 63, dg = (tid >> 6) + 4 * i;
-      const uint32_t wv[4] = {vx[i].x, vx[i].y, vx[i].z, vx[i].w};
+      const int u = tid + 256 * i, kq = u & 15, dg = u >> 4;
+      if (dg < D / 8) {
+        const int q8 = kq & 7;                           // 4-key group inside the 32-key block
+        const int col = 32 * (kq >> 3) + 8 * (q8 & 3) + 4 * (q8 >> 2);
+        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vx[i][0]);
+        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vx[i][1]);
+        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vx[i][2]);
+        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vx[i][3]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        vt[(8 * dg + 2 * q) * VROW + key] = (uint16_t)(wv[q] & 0xFFFFu);
-        vt[(8 * dg + 2 * q + 1) * VROW + key] = (uint16_t)(wv[q] >> 16);
+        for (int d = 0; d < 8; ++d) {
+          const int wd = d >> 1, sh = (d & 1) * 16;
+          const uint32_t e0 = (r0[wd] >> sh) & 0xFFFFu, e1 = (r1[wd] >> sh) & 0xFFFFu;
+          const uint32_t e2 = (r2[wd] >> sh) & 0xFFFFu, e3 = (r3[wd] >> sh) & 0xFFFFu;
+          *reinterpret_cast<uint2*>(&vt[(8 * dg + d) * VROW + col]) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
+        }
       }
     }
   }
@@ -308,22 +322,24 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
     }
     ss += __shfl_xor(ss, 1, kWave);
     ss += __shfl_xor(ss, 2, kWave);
-    if (qd == 0) rk[key] = a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
+    if (qd == 0) rk[key] = (a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f) * a.attn_scale;
   }
   __syncthreads();
 
   const int n_tiles = (n_pairs + PT - 1) / PT;
-  const int ma = lane & 15, jg = lane >> 4;        // A-operand row, K-group
-  float rkv[4];
+  const int ma = lane & 15, jg = lane >> 4;        // head-row of the tile, lane group
+  // S^T accumulators: lane holds keys 16*nt + 4*jg + i of head-row ma
+  float rkl[4][4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) rkv[nt] = rk[16 * nt + ma] * a.attn_scale;
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rkl[nt][i] = rk[16 * nt + 4 * jg + i];
 
   bf16x8 qa[KSTEP], qn[KSTEP];
   if (w < n_tiles) load_q_tile<D, G>(a, pid_s, n_pairs, w, g, ma, jg, qa);
   for (int tile = w; tile < n_tiles; tile += 4) {
     // prefetch the next tile's queries while this one computes
     if (tile + 4 < n_tiles) load_q_tile<D, G>(a, pid_s, n_pairs, tile + 4, g, ma, jg, qn);
-    // query norms of the 16 rows
     float qss = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) {
@@ -337,83 +353,74 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
     }
     qss += __shfl_xor(qss, 16, kWave);
     qss += __shfl_xor(qss, 32, kWave);
-    if (lane < 16) rqs[w][ma] = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
-    // S = Q K^T: lane holds S[4*jg + i][16*nt + ma]
+    const float rq = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
+    // S^T = K Q^T on MFMA: A = keys from LDS, B = the tile's queries
     floatx4 s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       s[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < KSTEP; ++t) {
-        const uint4 b = *reinterpret_cast<const uint4*>(&ks[(16 * nt + ma) * KROW + 32 * t + 8 * jg]);
-        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], __builtin_bit_cast(bf16x8, b), s[nt], 0, 0, 0);
+        const uint4 kb = *reinterpret_cast<const uint4*>(&ks[(16 * nt + ma) * KROW + 32 * t + 8 * jg]);
+        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb), qa[t], s[nt], 0, 0, 0);
       }
     }
-    // softmax over the 64 keys of each head-row; P scaled by the pair's weight
+    __builtin_amdgcn_sched_barrier(0);   // keep the P.V operand reads below the softmax
+    // softmax over the 64 keys of head-row ma: 16 in this lane, the rest in
+    // lanes ma + 16, ma + 32, ma + 48
+    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * jg + i;
-      const int pm = tile * PT + m / G;
-      const float rq = rqs[w][m];
-      float x[4], mx = -INFINITY;
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        x[nt] = s[nt][i] * rq * rkv[nt];
-        mx = fmaxf(mx, x[nt]);
+      for (int i = 0; i < 4; ++i) {
+        s[nt][i] = s[nt][i] * rq * rkl[nt][i];
+        mx = fmaxf(mx, s[nt][i]);
       }
-      mx = fmaxf(mx, dpp_f<0xB1>(mx));
-      mx = fmaxf(mx, dpp_f<0x4E>(mx));
-      mx = fmaxf(mx, dpp_f<0x141>(mx));
-      mx = fmaxf(mx, dpp_f<0x140>(mx));
-      float sum = 0.f;
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float sum = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        x[nt] = expf(x[nt] - mx);
-        sum += x[nt];
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[nt][i] = expf(s[nt][i] - mx);
+        sum += s[nt][i];
       }
-      sum += dpp_f<0xB1>(sum);
-      sum += dpp_f<0x4E>(sum);
-      sum += dpp_f<0x141>(sum);
-      sum += dpp_f<0x140>(sum);
-      const float scale = (pm < n_pairs ? w_s[pm] : 0.f) / sum;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) ps[w][m * PROW + 16 * nt + ma] = f32_to_bf16(x[nt] * scale);
-    }
-    // O = P V: lane holds O[4*jg + i][16*nt + ma]; staged to LDS as fp16
-    bf16x8 pa8[2];
+    sum += __shfl_xor(sum, 16, kWave);
+    sum += __shfl_xor(sum, 32, kWave);
+    const int pm = tile * PT + ma / G;
+    const float scale = (pm < n_pairs ? w_s[pm] : 0.f) / sum;
+    // P^T as the B operand of O^T = V^T P^T: step st takes keys of nt = 2st, 2st + 1
+    bf16x8 pb[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
-      pa8[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&ps[w][ma * PROW + 32 * st + 8 * jg]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[st][e] = (__bf16)(s[2 * st + (e >> 2)][e & 3] * scale);
+    // O^T: lane holds dims 16*nt + 4*jg + i of head-row ma; fp16 partial, 8-byte stores
+    const bool live = pm < n_pairs;
+    __half* dst = a.partials + (live ? ((int64_t)pid_s[pm] * G + (ma % G)) * D : 0) + 4 * jg;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       floatx4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint4 b = *reinterpret_cast<const uint4*>(&vt[(16 * nt + ma) * VROW + 32 * st + 8 * jg]);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8[st], __builtin_bit_cast(bf16x8, b), o, 0, 0, 0);
+        const uint4 va = *reinterpret_cast<const uint4*>(&vt[(16 * nt + ma) * VROW + 32 * st + 8 * jg]);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[st], o, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ob[w][(4 * jg + i) * OROW + 16 * nt + ma] = __half_as_ushort(__float2half(o[i]));
-    }
-    // each pair's G x D block is contiguous in the partials: 16-byte stores
-    constexpr int V16 = 16 * D / 8;                  // 16-byte pieces in the tile
-#pragma unroll
-    for (int q = 0; q < V16 / kWave; ++q) {
-      const int e = lane + kWave * q;                // piece index
-      const int m = e / (D / 8), col = (e % (D / 8)) * 8;
-      const int pm = tile * PT + m / G;
-      if (pm < n_pairs) {
-        const uint4 val = *reinterpret_cast<const uint4*>(&ob[w][m * OROW + col]);
-        *reinterpret_cast<uint4*>(&a.partials[((int64_t)pid_s[pm] * G + (m % G)) * D + col]) = val;
+      if (live) {
+        const uint32_t h01 = (uint32_t)__half_as_ushort(__float2half(o[0])) |
+                             ((uint32_t)__half_as_ushort(__float2half(o[1])) << 16);
+        const uint32_t h23 = (uint32_t)__half_as_ushort(__float2half(o[2])) |
+                             ((uint32_t)__half_as_ushort(__float2half(o[3])) << 16);
+        *reinterpret_cast<uint2*>(dst + 16 * nt) = make_uint2(h01, h23);
       }
+      if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // two output tiles in flight
     }
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) qa[t] = qn[t];
   }
 }
 
-// --- combine: out = sum over slots of the partials (slot order) --------------
 template <int D, int G>
 __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs a) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
