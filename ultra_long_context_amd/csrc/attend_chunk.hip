@@ -227,9 +227,9 @@ __device__ __forceinline__ void load_q_tile(const ChunkArgs& a, const uint32_t* 
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_attn) +
                        ((row / a.Hkv) * a.Hq + (int64_t)g * G + ha) * D + 8 * jg;
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (va) x = *reinterpret_cast<const uint4*>(qp + 32 * t);
+  for (int t = 0; t < D / 32; ++t) {      // unconditional load (row 0 when !va), then zero
+    uint4 x = *reinterpret_cast<const uint4*>(qp + 32 * t);
+    if (!va) x = make_uint4(0, 0, 0, 0);
     qa[t] = __builtin_bit_cast(bf16x8, x);
   }
 }

@@ -24,23 +24,38 @@ constexpr int kSlotsPerBlock = 4;
 constexpr int kMergeCap = 512;
 constexpr int kMaxHeadSlots = 8;     // list heads per lane: up to 512 splits
 
-// Exact top K of one row from per-split sorted lists (whole wave).  Leaves the
-// sorted selection in top[0..m) and returns m.
-__device__ int merge_row_lists(const uint64_t* L, int n_splits, int K, uint64_t* C, uint64_t* top,
+// Exact top K of one row from its per-split lists L[s][0..K) (each sorted best
+// first, zero-padded); whole wave.  A list can only contribute if its head
+// reaches the K-th largest head, and then only entries at or above that head:
+// the heads give a bound (upper 16 key bits), the few lists above it are read
+// whole, and the surviving candidates are ranked.  Leaves the sorted selection
+// in top[0..m) and returns m.  Loads are unconditional (indices clamped) so
+// they are all in flight together.
+__device__ __forceinline__ int merge_row_lists(const uint64_t* L, int n_splits, int K, uint64_t* C, uint64_t* top,
                                int* act, int lane) {
   const int nh = (n_splits + kWave - 1) / kWave;      // <= kMaxHeadSlots
   uint64_t h[kMaxHeadSlots];
 #pragma unroll
   for (int i = 0; i < kMaxHeadSlots; ++i) {
     const int sp = lane + kWave * i;
-    h[i] = (i < nh && sp < n_splits) ? L[(int64_t)sp * K] : 0ull;
+    const uint64_t v = L[(int64_t)(sp < n_splits ? sp : 0) * K];
+    h[i] = (i < nh && sp < n_splits) ? v : 0ull;
   }
-  uint64_t lo = (uint64_t)wave_kth_key<kMaxHeadSlots>(h, nh, K) << 32;
+  uint32_t t16 = 0;                      // K heads have key >= t16 << 16
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t cand = t16 | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxHeadSlots; ++i)
+      if (i < nh) c += wave_count((uint32_t)(h[i] >> 48) >= cand);
+    if (c >= K) t16 = cand;
+  }
+  uint64_t lo = (uint64_t)t16 << 48;
   int n_on = 0;
 #pragma unroll
   for (int i = 0; i < kMaxHeadSlots; ++i)
     if (i < nh) n_on += wave_count(h[i] != 0ull && h[i] >= lo);
-  if (n_on > kWave) lo = wave_kth_regs<kMaxHeadSlots>(h, nh, K);
+  if (n_on > kWave) lo = wave_kth_regs<kMaxHeadSlots>(h, nh, K);   // exactly K heads remain
   int na = 0;
 #pragma unroll
   for (int i = 0; i < kMaxHeadSlots; ++i) {
@@ -51,14 +66,15 @@ __device__ int merge_row_lists(const uint64_t* L, int n_splits, int K, uint64_t*
     na += __popcll(mask);
   }
   const int my_list = lane < na ? act[lane] : -1;
+  const uint64_t* lp = L + (int64_t)(my_list >= 0 ? my_list : 0) * K;
   int cnt = 0;
-  bool more = my_list >= 0;
-  for (int q0 = 0; q0 < K && __any(more); q0 += 8) {
-    uint64_t e[8];
+  for (int q0 = 0; q0 < K; q0 += 16) {
+    uint64_t e[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) e[q] = (more && q0 + q < K) ? L[(int64_t)my_list * K + q0 + q] : 0ull;
+    for (int q = 0; q < 16; ++q) e[q] = lp[q0 + q < K ? q0 + q : K - 1];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 16; ++q) {
+      if (my_list < 0 || q0 + q >= K) e[q] = 0ull;
       if (cnt + kWave > kMergeCap) {
         cnt = wave_keep_top<kMergeCap / kWave>(C, cnt, K, lane);
         if (cnt >= K) {
@@ -72,7 +88,15 @@ __device__ int merge_row_lists(const uint64_t* L, int n_splits, int K, uint64_t*
       if (keep) C[cnt + __popcll(mask & lanemask_lt())] = e[q];
       cnt += __popcll(mask);
     }
-    more = more && e[7] != 0ull && e[7] >= lo;
+    // lists are sorted: one whose last entry here is below the bound is done
+    if (!__any(e[15] != 0ull && e[15] >= lo)) break;
+  }
+  if (cnt <= kWave) {                    // rank the candidates directly
+    const uint64_t mine = lane < cnt ? C[lane] : 0ull;
+    int rank = 0;
+    for (int o = 0; o < cnt; ++o) rank += C[o] > mine;
+    if (lane < cnt && rank < K) top[rank] = mine;
+    return cnt < K ? cnt : K;
   }
   const int m = wave_keep_top<kMergeCap / kWave>(C, cnt, K, lane);
   wave_rank_sort(C, m, top, lane);
@@ -165,9 +189,9 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(DecodeArgs a) {
       for (int t = 0; t < KSTEP; ++t)
         kb[nt][t] = *reinterpret_cast<const uint4*>(kp + (16 * nt + ma) * D + 32 * t + 8 * jg);
 #pragma unroll
-    for (int t = 0; t < KSTEP; ++t) {
-      qa[t] = make_uint4(0, 0, 0, 0);
-      if (ma < G) qa[t] = *reinterpret_cast<const uint4*>(qp + ma * D + 32 * t + 8 * jg);
+    for (int t = 0; t < KSTEP; ++t) {    // rows >= G load row 0 (unconditional), then zero
+      qa[t] = *reinterpret_cast<const uint4*>(qp + (ma < G ? ma : 0) * D + 32 * t + 8 * jg);
+      if (ma >= G) qa[t] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int dg = 0; dg < D / 8; ++dg) vx[dg] = *reinterpret_cast<const uint4*>(vp + lane * D + 8 * dg);
@@ -290,7 +314,7 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(DecodeArgs a) {
   const float* pb = a.partials + row * n_blk * (int64_t)(G * D);
   for (int e = tid; e < G * D; e += 256) {
     float v = 0.f;
-#pragma unroll 4
+#pragma unroll 8
     for (int p = 0; p < n_blk; ++p) v += fetch(&pb[(int64_t)p * G * D + e]);
     op[e] = f32_to_bf16(v);
   }

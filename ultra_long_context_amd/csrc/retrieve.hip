@@ -35,11 +35,13 @@ template <bool BF16, int D> struct QOperand;
 // bf16: 16x16x32 MFMA; K-group j of step t covers dims 32t + 8j .. 32t + 8j + 7.
 template <int D> struct QOperand<true, D> {
   bf16x8 v[D / 32];
+  // row must be a valid address even when !ok (the load is unconditional so
+  // that it never waits on earlier loads)
   __device__ __forceinline__ void load(const uint16_t* row, bool ok, int j) {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (ok) x = *reinterpret_cast<const uint4*>(row + 32 * t + 8 * j);
+      uint4 x = *reinterpret_cast<const uint4*>(row + 32 * t + 8 * j);
+      if (!ok) x = make_uint4(0, 0, 0, 0);
       v[t] = __builtin_bit_cast(bf16x8, x);
     }
   }
@@ -51,8 +53,8 @@ template <int D> struct QOperand<false, D> {
   __device__ __forceinline__ void load(const float* row, bool ok, int j) {
 #pragma unroll
     for (int u = 0; u < D / 16; ++u) {
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ok) x = *reinterpret_cast<const float4*>(row + 16 * u + 4 * j);
+      float4 x = *reinterpret_cast<const float4*>(row + 16 * u + 4 * j);
+      if (!ok) x = make_float4(0.f, 0.f, 0.f, 0.f);
       v[u] = x;
     }
   }
@@ -352,7 +354,10 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
     QOperand<BF16, D> q;
     q.load(reinterpret_cast<const T*>(a.q_ret) + ((b * a.Lq + (row_ok ? r : 0)) * a.Hkv + g) * D,
            row_ok, j);
-    const T* lm = reinterpret_cast<const T*>(a.landmarks) + (int64_t)bg * a.Nc * D;
+    // with no eligible chunk at all (then c_begin == c_end == 0) the loads read
+    // the first query row instead: an address that is always valid
+    const T* lm = c_begin < c_end ? reinterpret_cast<const T*>(a.landmarks) + (int64_t)bg * a.Nc * D
+                                  : reinterpret_cast<const T*>(a.q_ret);
     const int cw = c_begin + w * kWideChunksPerWave;
     // landmark loads of GRP sub-tiles are all issued before their MFMAs
     // (GRP = 4 for bf16: the wave's whole 16 KiB in flight at once)
@@ -362,14 +367,13 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
       uint4 x[GRP][LOADS];
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
-        const int cc = cw + (s0 + u) * 16 + qrow;
-        const bool ok = cc < c_end;
+        // chunks past c_end load chunk c_begin instead (their keys are masked):
+        // unconditional loads are all in flight at once
+        const int cc0 = cw + (s0 + u) * 16 + qrow;
+        const int cc = cc0 < c_end ? cc0 : c_begin;
         const T* p = lm + (int64_t)cc * D + (BF16 ? 8 : 4) * j;
 #pragma unroll
-        for (int t = 0; t < LOADS; ++t) {
-          x[u][t] = make_uint4(0, 0, 0, 0);
-          if (ok) x[u][t] = *reinterpret_cast<const uint4*>(p + (BF16 ? 32 : 16) * t);
-        }
+        for (int t = 0; t < LOADS; ++t) x[u][t] = *reinterpret_cast<const uint4*>(p + (BF16 ? 32 : 16) * t);
       }
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {
@@ -592,13 +596,76 @@ __device__ __forceinline__ int block_cut(uint64_t* row, int K, int jq, uint64_t&
   return m;
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
-  constexpr int LROW = D + 8;            // bf16 per landmark row in LDS (16-byte pad)
+// One pass of a block-scan workgroup over its landmark tiles: tile t + 1 is
+// loaded into registers while tile t is scored from LDS.  fn(sub-tile scores,
+// sub-tile, first chunk, whole sub-tile eligible for every row of the wave).
+template <int D, bool kUnrollSub, class F>
+__device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int n_tiles, int w_stop,
+                                            int w_min, uint16_t (*lmt)[kTile * (D + 8)],
+                                            const QOperand<true, D>& q, int tid, int qrow, int j, F&& fn) {
+  constexpr int LROW = D + 8;
   constexpr int RU = D / 8;              // 16-byte units per landmark
   constexpr int NU = kTile * RU / 256;   // 16-byte tile loads per thread
   constexpr int KSTEP = D / 32;
-  __shared__ __align__(16) uint16_t lmt[2][kTile * LROW];
+  uint4 pre[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {         // chunks past c_stop: scores masked
+    const int qi = tid * NU + u, c0 = qi / RU;
+    pre[u] = *reinterpret_cast<const uint4*>(lm + (int64_t)(c0 < c_stop ? c0 : 0) * D + (qi % RU) * 8);
+  }
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int qi = tid * NU + u;
+      *reinterpret_cast<uint4*>(&lmt[0][(qi / RU) * LROW + (qi % RU) * 8]) = pre[u];
+    }
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const bool more = t + 1 < n_tiles;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int qi = tid * NU + u, c0 = (t + 1) * kTile + qi / RU;
+      pre[u] = *reinterpret_cast<const uint4*>(lm + (int64_t)(c0 < c_stop ? c0 : 0) * D + (qi % RU) * 8);
+    }
+    const uint16_t* L = lmt[t & 1];
+    auto sub_tile = [&](int sub) __attribute__((always_inline)) {
+      const int cs = t * kTile + 16 * sub;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KSTEP; ++k) {
+        const uint4 x = *reinterpret_cast<const uint4*>(L + (16 * sub + qrow) * LROW + 32 * k + 8 * j);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), q.v[k], acc, 0, 0, 0);
+      }
+      fn(acc, sub, cs, cs + 16 <= w_min);
+    };
+    if constexpr (kUnrollSub) {          // fn indexes registers by sub-tile
+#pragma unroll
+      for (int sub = 0; sub < kTile / 16; ++sub) {
+        if (t * kTile + 16 * sub >= w_stop) break;
+        sub_tile(sub);
+      }
+    } else {                             // fn is large: one copy of it
+#pragma unroll 1
+      for (int sub = 0; sub < kTile / 16; ++sub) {
+        if (t * kTile + 16 * sub >= w_stop) break;
+        sub_tile(sub);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int qi = tid * NU + u;
+        *reinterpret_cast<uint4*>(&lmt[(t + 1) & 1][(qi / RU) * LROW + (qi % RU) * 8]) = pre[u];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
+  __shared__ __align__(16) uint16_t lmt[2][kTile * (D + 8)];   // landmark tiles, 16-byte row pad
   __shared__ uint64_t buf[kBlkWaves][kRows * kBlkStride];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -612,7 +679,7 @@ __global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
   const int64_t rb = rbk - 1 - (int64_t)blockIdx.x / nbg;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int64_t r0 = rb * kBlkRows, rw0 = r0 + w * kRows;
-  auto limit = [&](int64_t r) -> int {   // chunks [0, limit) are eligible for row r
+  auto limit = [&](int64_t r) -> int __attribute__((always_inline)) {   // chunks [0, limit) are eligible for row r
     if (r >= a.Lq) return 0;
     const int64_t n = (a.q_pos0 + r) / kChunk;
     return (int)(n < a.Nc ? n : a.Nc);
@@ -630,55 +697,18 @@ __global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
   const int n_tiles = (c_stop + kTile - 1) / kTile;
   const int K = a.K;
 
-  uint4 pre[NU];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int qi = tid * NU + u;
-      const int c = t * kTile + qi / RU;
-      pre[u] = make_uint4(0, 0, 0, 0);
-      if (c < c_stop) pre[u] = *reinterpret_cast<const uint4*>(lm + (int64_t)c * D + (qi % RU) * 8);
-    }
+  auto sweep1 = [&](auto&& fn) __attribute__((always_inline)) {
+    block_sweep<D, true>(lm, c_stop, n_tiles, w_stop, w_min, lmt, q, tid, qrow, j, fn);
   };
-  auto store_tile = [&](int bi) {
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int qi = tid * NU + u;
-      *reinterpret_cast<uint4*>(&lmt[bi][(qi / RU) * LROW + (qi % RU) * 8]) = pre[u];
-    }
-  };
-  // one pass over the tiles; fn(sub-tile scores, first chunk, whole sub-tile eligible for every row)
-  auto sweep = [&](auto&& fn) {
-    if (n_tiles > 0) {
-      load_tile(0);
-      store_tile(0);
-    }
-    __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-      if (t + 1 < n_tiles) load_tile(t + 1);
-      const uint16_t* L = lmt[t & 1];
-#pragma unroll
-      for (int sub = 0; sub < kTile / 16; ++sub) {
-        const int cs = t * kTile + 16 * sub;
-        if (cs >= w_stop) break;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < KSTEP; ++k) {
-          const uint4 x = *reinterpret_cast<const uint4*>(L + (16 * sub + qrow) * LROW + 32 * k + 8 * j);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), q.v[k], acc, 0, 0, 0);
-        }
-        fn(acc, sub, cs, cs + 16 <= w_min);
-      }
-      if (t + 1 < n_tiles) store_tile((t + 1) & 1);
-      __syncthreads();
-    }
+  auto sweep2 = [&](auto&& fn) __attribute__((always_inline)) {
+    block_sweep<D, false>(lm, c_stop, n_tiles, w_stop, w_min, lmt, q, tid, qrow, j, fn);
   };
 
   // --- pass 1: group maxima, then a lower bound of each row's K-th key -------
   float gm[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) gm[x] = -INFINITY;
-  sweep([&](const floatx4& acc, int sub, int cs, bool all) {
+  sweep1([&](const floatx4& acc, int sub, int cs, bool all) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (all || cs + 4 * j + i < lim) gm[4 * sub + i] = fmaxf(gm[4 * sub + i], acc[i]);
@@ -710,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
 #pragma unroll
   for (int s = 0; s < 16; ++s) qrowbuf[jq + 4 * s] = kEmpty;
   int m = 0, cj = 0;     // kept entries of the row; this lane's appends after them
-  sweep([&](const floatx4& acc, int sub, int cs, bool all) {
+  sweep2([&](const floatx4& acc, int sub, int cs, bool all) __attribute__((always_inline)) {
     if (__any(m + j + 4 * cj + 12 >= kBlkCap)) {
       uint64_t kth;
       const int mq = block_cut(qrowbuf, K, jq, kth, false);
