@@ -26,9 +26,13 @@ namespace {
 
 constexpr int kPairs = 64;   // pairs per work item
 
+// Bins are (batch, kv head, band of band_rows query rows, chunk): items of one
+// band run close together in time, so the band's queries stay in the
+// Infinity Cache while its pairs are processed.
 __device__ __forceinline__ int64_t bin_of(int64_t row, int32_t c, const ChunkArgs& a) {
   const int64_t bg = (row / ((int64_t)a.Lq * a.Hkv)) * a.Hkv + row % a.Hkv;
-  return bg * a.Nc + c;
+  const int64_t band = ((row / a.Hkv) % a.Lq) / a.band_rows;
+  return (bg * a.n_bands + band) * a.Nc + c;
 }
 
 // Rows are laid out on segments of S lanes (S = the smallest power of two
@@ -64,6 +68,7 @@ __global__ __launch_bounds__(256) void chunk_count_kernel(ChunkArgs a) {
 // global atomics drop from one per pair to one per (workgroup, chunk).  Used
 // when the chunks of one (batch, kv head) fit the LDS histogram.
 constexpr int kBucketRows = 1024;
+constexpr int kBandRows = 8192;          // a multiple of kBucketRows
 constexpr int kHistMax = 16384;
 constexpr int kBucketBatch = 4;          // row passes whose loads are issued together
 
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(256) void chunk_count_lds_kernel(ChunkArgs a) {
     if (valid) atomicAdd(&hist[c], 1u);
   });
   __syncthreads();
-  uint32_t* cnt = a.counts + br.bg * a.Nc;
+  uint32_t* cnt = a.counts + (br.bg * a.n_bands + br.r0 / a.band_rows) * a.Nc;
   for (int64_t i = threadIdx.x; i < a.Nc; i += 256)
     if (hist[i] != 0u) atomicAdd(&cnt[i], hist[i]);
 }
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void chunk_scatter_lds_kernel(ChunkArgs a) {
   });
   __syncthreads();
   // reserve this workgroup's run in every bin it touches
-  uint32_t* cur = a.cursor + br.bg * a.Nc;
+  uint32_t* cur = a.cursor + (br.bg * a.n_bands + br.r0 / a.band_rows) * a.Nc;
   for (int64_t i = threadIdx.x; i < a.Nc; i += 256)
     if (hist[i] != 0u) hist[i] = atomicAdd(&cur[i], hist[i]);
   __syncthreads();
@@ -147,58 +152,113 @@ __global__ __launch_bounds__(256) void chunk_scatter_lds_kernel(ChunkArgs a) {
   });
 }
 
-// --- scan: bin offsets, scatter cursors, work items (one workgroup) ----------
-// Thread t owns a contiguous range of bins; counts are read 16 at a time so
-// the loads of a batch are all in flight together.
-__global__ __launch_bounds__(1024) void chunk_scan_kernel(ChunkArgs a) {
-  __shared__ uint32_t sp[1024], si[1024];
+// --- scan: bin offsets, scatter cursors, work items ------------------------
+// Two kernels over segments of Nc bins (one segment per (batch, kv head,
+// band)): the first scans each segment locally and records its totals; the
+// second adds the totals of all earlier segments, writes the bin offsets, the
+// scatter cursors and the work items, and clears the counts for the next call.
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t& a, uint32_t& b, uint32_t* sa, uint32_t* sb,
+                                                      uint32_t& tot_a, uint32_t& tot_b) {
   const int t = threadIdx.x;
-  const int64_t n = a.n_bins;
-  const int64_t seg = (n + 1023) / 1024;
-  const int64_t lo = min(n, t * seg), hi = min(n, lo + seg);
+  sa[t] = a;
+  sb[t] = b;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {   // inclusive Hillis-Steele scan
+    const uint32_t va = t >= o ? sa[t - o] : 0u, vb = t >= o ? sb[t - o] : 0u;
+    __syncthreads();
+    sa[t] += va;
+    sb[t] += vb;
+    __syncthreads();
+  }
+  tot_a = sa[kScanThreads - 1];
+  tot_b = sb[kScanThreads - 1];
+  a = sa[t] - a;
+  b = sb[t] - b;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kScanThreads) void chunk_seg_scan_kernel(ChunkArgs a) {
+  __shared__ uint32_t sp[kScanThreads], si[kScanThreads];
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * a.Nc, n = a.Nc;
+  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = min(n, t * per), hi = min(n, lo + per);
   uint32_t tp = 0, ti = 0;
   for (int64_t i0 = lo; i0 < hi; i0 += 16) {
     uint32_t c[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[i0 + u] : 0u;
+    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[base + i0 + u] : 0u;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       tp += c[u];
       ti += (c[u] + kPairs - 1) / kPairs;
     }
   }
-  sp[t] = tp;
-  si[t] = ti;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
-    const uint32_t vp = t >= o ? sp[t - o] : 0u, vi = t >= o ? si[t - o] : 0u;
-    __syncthreads();
-    sp[t] += vp;
-    si[t] += vi;
-    __syncthreads();
-  }
-  uint32_t rp = sp[t] - tp, ri = si[t] - ti;
+  uint32_t rp = tp, ri = ti, tot_p, tot_i;
+  block_exclusive_scan2(rp, ri, sp, si, tot_p, tot_i);
+  // local prefixes: pairs into offsets, items into cursor (fixed up next)
   for (int64_t i0 = lo; i0 < hi; i0 += 16) {
     uint32_t c[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[i0 + u] : 0u;
+    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[base + i0 + u] : 0u;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int64_t i = i0 + u;
-      if (i < hi) {
-        a.offsets[i] = rp;
-        a.cursor[i] = rp;
-        a.counts[i] = 0u;                // ready for the next call
-        const uint32_t ni = (c[u] + kPairs - 1) / kPairs;
-        for (uint32_t jb = 0; jb < ni; ++jb) a.items[ri + jb] = (uint64_t)i | ((uint64_t)jb << 32);
+      if (i0 + u < hi) {
+        a.offsets[base + i0 + u] = rp;
+        a.cursor[base + i0 + u] = ri;
         rp += c[u];
-        ri += ni;
+        ri += (c[u] + kPairs - 1) / kPairs;
       }
     }
   }
-  if (t == 1023) {
-    a.offsets[n] = rp;
-    *a.n_items = ri;
+  if (t == 0) {
+    a.seg_tot[2 * blockIdx.x] = tot_p;
+    a.seg_tot[2 * blockIdx.x + 1] = tot_i;
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void chunk_seg_fix_kernel(ChunkArgs a) {
+  __shared__ uint32_t sp[kScanThreads], si[kScanThreads];
+  const int t = threadIdx.x;
+  const int64_t seg = blockIdx.x;
+  uint32_t pb = 0, ib = 0;                       // totals of the earlier segments
+  for (int64_t s = t; s < seg; s += kScanThreads) {
+    pb += a.seg_tot[2 * s];
+    ib += a.seg_tot[2 * s + 1];
+  }
+  uint32_t tot_p, tot_i;
+  block_exclusive_scan2(pb, ib, sp, si, tot_p, tot_i);
+  pb = tot_p;
+  ib = tot_i;
+  const int64_t base = seg * a.Nc, n = a.Nc;
+  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = min(n, t * per), hi = min(n, lo + per);
+  for (int64_t i0 = lo; i0 < hi; i0 += 16) {
+    uint32_t c[16], lp[16], li[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool in = i0 + u < hi;
+      c[u] = in ? a.counts[base + i0 + u] : 0u;
+      lp[u] = in ? a.offsets[base + i0 + u] : 0u;
+      li[u] = in ? a.cursor[base + i0 + u] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t i = base + i0 + u;
+      if (i0 + u < hi) {
+        a.offsets[i] = pb + lp[u];
+        a.cursor[i] = pb + lp[u];
+        a.counts[i] = 0u;                        // ready for the next call
+        const uint32_t ni = (c[u] + kPairs - 1) / kPairs;
+        for (uint32_t jb = 0; jb < ni; ++jb) a.items[ib + li[u] + jb] = (uint64_t)i | ((uint64_t)jb << 32);
+      }
+    }
+  }
+  if (seg == (int64_t)gridDim.x - 1 && t == 0) {
+    a.offsets[a.n_bins] = pb + a.seg_tot[2 * seg];
+    *a.n_items = ib + a.seg_tot[2 * seg + 1];
   }
 }
 
@@ -256,8 +316,9 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   const uint32_t p_begin = a.offsets[bin] + blk * kPairs;
   const uint32_t p_end = min(p_begin + (uint32_t)kPairs, a.offsets[bin + 1]);
   const int n_pairs = (int)(p_end - p_begin);
-  const int64_t bg = bin / a.Nc;
-  const int64_t c = bin - bg * a.Nc;
+  const int64_t bgb = bin / a.Nc;                // (batch, kv head) * n_bands + band
+  const int64_t c = bin - bgb * a.Nc;
+  const int64_t bg = bgb / a.n_bands;
   const int g = (int)(bg % a.Hkv);
 
   // pair ids and blend weights of the item; K (row-major) and V^T in LDS.
@@ -468,6 +529,7 @@ hipError_t launch_dg(const ChunkArgs& a, hipStream_t st, const Marks& mk) {
 }  // namespace
 
 int64_t chunk_pairs_per_item() { return kPairs; }
+int64_t chunk_band_rows() { return kBandRows; }
 
 hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk) {
   hipError_t e;
@@ -481,8 +543,15 @@ hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st,
   if (lds) hipLaunchKernelGGL(chunk_count_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
   else hipLaunchKernelGGL(chunk_count_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(1024), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned n_seg = (unsigned)(a.n_bins / (a.Nc > 0 ? a.Nc : 1));
+  if (n_seg > 0 && a.Nc > 0) {
+    hipLaunchKernelGGL(chunk_seg_scan_kernel, dim3(n_seg), dim3(kScanThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_seg_fix_kernel, dim3(n_seg), dim3(kScanThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else if ((e = launch_fill_u32(a.n_items, 1, 0u, st)) != hipSuccess) {   // no bins: no work items
+    return e;
+  }
   if (lds) hipLaunchKernelGGL(chunk_scatter_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
   else hipLaunchKernelGGL(chunk_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -30,10 +30,10 @@ struct Plan {
   bool wide;             // few-row scan: 16-wave workgroups, per-split lists
   bool block;            // many-row scan (bf16, K <= 32): 64 rows per workgroup
   int32_t attn_splits, slots_per_split, attn_mode;
-  int64_t n_bins, max_items;   // chunk-major attend
+  int64_t n_bins, max_items, n_bands;   // chunk-major attend
   size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
   size_t off_ccounts, off_coffsets, off_ccursor, off_citems, off_cnitems, off_cpairs, off_cwts,
-      off_cparts;
+      off_cparts, off_cseg;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -97,7 +97,8 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
   // the last slot to finish.  Many rows, bf16: pairs bucketed by chunk, one
   // MFMA workgroup per block of pairs of a chunk, then a slot-ordered combine.
   // Many rows, fp32: one wave per row.
-  p->n_bins = (int64_t)s->batch * s->n_kv_heads * Nc;
+  p->n_bands = (s->q_len + chunk_band_rows() - 1) / chunk_band_rows();
+  p->n_bins = (int64_t)s->batch * s->n_kv_heads * p->n_bands * Nc;
   const int64_t n_pairs = p->rows * p->K;
   p->max_items = (n_pairs + chunk_pairs_per_item() - 1) / chunk_pairs_per_item() + p->n_bins;
   if (p->rows < 1024 && p->bf16) {
@@ -127,7 +128,7 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
   p->off_partials = off;
   if (p->attn_splits > 1) off = align_up(off + (size_t)p->rows * p->attn_splits * G * p->D * 4, 256);
   p->off_ccounts = p->off_coffsets = p->off_ccursor = p->off_citems = p->off_cnitems = 0;
-  p->off_cpairs = p->off_cwts = p->off_cparts = 0;
+  p->off_cpairs = p->off_cwts = p->off_cparts = p->off_cseg = 0;
   if (p->attn_mode == 2) {
     const size_t nb = (size_t)p->n_bins, np = (size_t)n_pairs;
     p->off_ccounts = off; off = align_up(off + nb * 4, 256);
@@ -135,6 +136,7 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
     p->off_ccursor = off; off = align_up(off + nb * 4, 256);
     p->off_citems = off; off = align_up(off + (size_t)p->max_items * 8, 256);
     p->off_cnitems = off; off = align_up(off + 4, 256);
+    p->off_cseg = off; off = align_up(off + (Nc > 0 ? nb / (size_t)Nc : 0) * 8, 256);
     p->off_cpairs = off; off = align_up(off + np * 4, 256);
     p->off_cwts = off; off = align_up(off + np * 4, 256);
     p->off_cparts = off; off = align_up(off + np * G * p->D * 2, 256);
@@ -228,11 +230,13 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
     c.cursor = reinterpret_cast<uint32_t*>(w + p.off_ccursor);
     c.items = reinterpret_cast<uint64_t*>(w + p.off_citems);
     c.n_items = reinterpret_cast<uint32_t*>(w + p.off_cnitems);
+    c.seg_tot = reinterpret_cast<uint32_t*>(w + p.off_cseg);
     c.pairs = reinterpret_cast<uint32_t*>(w + p.off_cpairs);
     c.wts = reinterpret_cast<float*>(w + p.off_cwts);
     c.partials = reinterpret_cast<__half*>(w + p.off_cparts);
     c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
     c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
+    c.band_rows = chunk_band_rows(); c.n_bands = p.n_bands;
     c.attn_scale = p.attn_scale; c.qk_norm = p.qk_norm ? 1 : 0;
     return launch_attend_chunk(c, p.D, p.G, st, mk) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
   }

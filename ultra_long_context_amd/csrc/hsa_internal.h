@@ -98,10 +98,12 @@ struct ChunkArgs {
   uint32_t* cursor;       // [n_bins]      scatter positions
   uint64_t* items;        // [max_items]   bin | block << 32
   uint32_t* n_items;      // number of valid items
+  uint32_t* seg_tot;      // [2 * n_bins / Nc] pairs and items per segment of Nc bins
   uint32_t* pairs;        // [rows * K]    pair ids (row * K + slot), grouped by bin
   float* wts;             // [rows * K]    blend weights
   __half* partials;       // [rows * K, G, D] weighted per-chunk outputs
   int64_t rows, Lq, Lkv, Nc, n_bins, max_items;
+  int64_t band_rows, n_bands;   // bins split the query rows of a (batch, kv head) into bands
   int32_t Hq, Hkv, K;
   float attn_scale;
   int32_t qk_norm;
@@ -118,6 +120,7 @@ hipError_t launch_attend_decode(const DecodeArgs& a, int64_t rows, int D, int G,
 int decode_slots_per_block();
 hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk);
 int64_t chunk_pairs_per_item();
+int64_t chunk_band_rows();
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 
 }  // namespace hsa
