@@ -25,6 +25,7 @@ namespace hsa {
 namespace {
 
 constexpr int kPairs = 64;   // pairs per work item
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Bins are (batch, kv head, band of band_rows query rows, chunk): items of one
 // band run close together in time, so the band's queries stay in the
@@ -278,20 +279,29 @@ __global__ __launch_bounds__(256) void chunk_scatter_kernel(ChunkArgs a) {
 // --- attend: one work item (a block of pairs of one chunk) per workgroup ----
 // Loads the A operand (attention queries of one 16-row tile) of a wave.
 template <int D, int G>
-__device__ __forceinline__ void load_q_tile(const ChunkArgs& a, const uint32_t* pid_s, int n_pairs,
-                                            int tile, int g, int ma, int jg, bf16x8 (&qa)[D / 32]) {
+__device__ __forceinline__ void load_q_tile(const ChunkArgs& a, const int64_t* qoff_s, int n_pairs,
+                                            int tile, int ma, int jg, bf16x8 (&qa)[D / 32]) {
   constexpr int PT = 16 / G;
   const int pa = tile * PT + ma / G, ha = ma % G;
   const bool va = pa < n_pairs;
-  const int64_t row = va ? (int64_t)(pid_s[pa] / (uint32_t)a.K) : 0;
-  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_attn) +
-                       ((row / a.Hkv) * a.Hq + (int64_t)g * G + ha) * D + 8 * jg;
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_attn) + (va ? qoff_s[pa] : 0) + ha * D + 8 * jg;
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {      // unconditional load (row 0 when !va), then zero
+  for (int t = 0; t < D / 32; ++t) {      // unconditional load (element 0 when !va), then zero
     uint4 x = *reinterpret_cast<const uint4*>(qp + 32 * t);
     if (!va) x = make_uint4(0, 0, 0, 0);
     qa[t] = __builtin_bit_cast(bf16x8, x);
   }
+}
+
+// Sum of squares of 8 bf16 values (two-term bf16 dot products, fp32 accumulate).
+__device__ __forceinline__ float sumsq8(uint4 x, float acc) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w[q]);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+  }
+  return acc;
 }
 
 template <int D, int G>
@@ -306,6 +316,7 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   __shared__ float rk[kChunk];
   __shared__ uint32_t pid_s[kPairs];
   __shared__ float w_s[kPairs];
+  __shared__ int64_t qoff_s[kPairs];   // element offset of the pair's G attention queries
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const uint32_t item_i = blockIdx.x;
@@ -328,6 +339,8 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     const uint32_t pid = a.pairs[p_begin + tid];
     pid_s[tid] = pid;
     w_s[tid] = a.wts[pid];
+    const int64_t qrow = (int64_t)(pid / (uint32_t)a.K) / a.Hkv;     // b * Lq + r
+    qoff_s[tid] = (qrow * a.Hq + (int64_t)g * G) * D;
   }
   {
     const int64_t base = (bg * a.Lkv + c * kChunk) * D;
@@ -376,14 +389,12 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     const int key = tid >> 2, qd = tid & 3;
     float ss = 0.f;
 #pragma unroll
-    for (int x = 0; x < D / 4; x += 2) {
-      const uint32_t u = *reinterpret_cast<const uint32_t*>(&ks[key * KROW + qd * (D / 4) + x]);
-      const float lo = __uint_as_float(u << 16), hi = __uint_as_float(u & 0xFFFF0000u);
-      ss += lo * lo + hi * hi;
-    }
+    for (int x = 0; x < D / 4; x += 8)
+      ss = sumsq8(*reinterpret_cast<const uint4*>(&ks[key * KROW + qd * (D / 4) + x]), ss);
     ss += __shfl_xor(ss, 1, kWave);
     ss += __shfl_xor(ss, 2, kWave);
-    if (qd == 0) rk[key] = (a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f) * a.attn_scale;
+    // logits are formed in base 2: log2(e) is folded into the key factor
+    if (qd == 0) rk[key] = (a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f) * a.attn_scale * kLog2e;
   }
   __syncthreads();
 
@@ -397,21 +408,13 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     for (int i = 0; i < 4; ++i) rkl[nt][i] = rk[16 * nt + 4 * jg + i];
 
   bf16x8 qa[KSTEP], qn[KSTEP];
-  if (w < n_tiles) load_q_tile<D, G>(a, pid_s, n_pairs, w, g, ma, jg, qa);
+  if (w < n_tiles) load_q_tile<D, G>(a, qoff_s, n_pairs, w, ma, jg, qa);
   for (int tile = w; tile < n_tiles; tile += 4) {
     // prefetch the next tile's queries while this one computes
-    if (tile + 4 < n_tiles) load_q_tile<D, G>(a, pid_s, n_pairs, tile + 4, g, ma, jg, qn);
+    if (tile + 4 < n_tiles) load_q_tile<D, G>(a, qoff_s, n_pairs, tile + 4, ma, jg, qn);
     float qss = 0.f;
 #pragma unroll
-    for (int t = 0; t < KSTEP; ++t) {
-      const uint4 x = __builtin_bit_cast(uint4, qa[t]);
-      const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = __uint_as_float(wd[q] << 16), hi = __uint_as_float(wd[q] & 0xFFFF0000u);
-        qss += lo * lo + hi * hi;
-      }
-    }
+    for (int t = 0; t < KSTEP; ++t) qss = sumsq8(__builtin_bit_cast(uint4, qa[t]), qss);
     qss += __shfl_xor(qss, 16, kWave);
     qss += __shfl_xor(qss, 32, kWave);
     const float rq = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
@@ -444,13 +447,13 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[nt][i] = expf(s[nt][i] - mx);
+        s[nt][i] = __builtin_amdgcn_exp2f(s[nt][i] - mx);   // logits are in base 2
         sum += s[nt][i];
       }
     sum += __shfl_xor(sum, 16, kWave);
     sum += __shfl_xor(sum, 32, kWave);
     const int pm = tile * PT + ma / G;
-    const float scale = (pm < n_pairs ? w_s[pm] : 0.f) / sum;
+    const float scale = (pm < n_pairs ? w_s[pm] : 0.f) * __builtin_amdgcn_rcpf(sum);
     // P^T as the B operand of O^T = V^T P^T: step st takes keys of nt = 2st, 2st + 1
     bf16x8 pb[2];
 #pragma unroll
@@ -469,11 +472,9 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
         o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[st], o, 0, 0, 0);
       }
       if (live) {
-        const uint32_t h01 = (uint32_t)__half_as_ushort(__float2half(o[0])) |
-                             ((uint32_t)__half_as_ushort(__float2half(o[1])) << 16);
-        const uint32_t h23 = (uint32_t)__half_as_ushort(__float2half(o[2])) |
-                             ((uint32_t)__half_as_ushort(__float2half(o[3])) << 16);
-        *reinterpret_cast<uint2*>(dst + 16 * nt) = make_uint2(h01, h23);
+        const half2v h01 = {(_Float16)o[0], (_Float16)o[1]}, h23 = {(_Float16)o[2], (_Float16)o[3]};
+        *reinterpret_cast<uint2*>(dst + 16 * nt) =
+            make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
       }
       if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // two output tiles in flight
     }

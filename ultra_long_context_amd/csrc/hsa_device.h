@@ -12,6 +12,8 @@ constexpr int kMaxTopK = 64;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // element conversion
