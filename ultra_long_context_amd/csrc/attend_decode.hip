@@ -20,9 +20,10 @@
 namespace hsa {
 namespace {
 
-constexpr int kSlotsPerBlock = 4;
+constexpr int kSlotsPerBlock = 4;       // one wave per slot
+constexpr int kThreads = 64 * kSlotsPerBlock;
 constexpr int kMergeCap = 512;
-constexpr int kMaxHeadSlots = 8;     // list heads per lane: up to 512 splits
+constexpr int kMaxHeads = 8;          // list heads per lane: up to 512 splits
 
 // Exact top K of one row from its per-split lists L[s][0..K) (each sorted best
 // first, zero-padded); whole wave.  A list can only contribute if its head
@@ -31,9 +32,11 @@ constexpr int kMaxHeadSlots = 8;     // list heads per lane: up to 512 splits
 // whole, and the surviving candidates are ranked.  Leaves the sorted selection
 // in top[0..m) and returns m.  Loads are unconditional (indices clamped) so
 // they are all in flight together.
-__device__ __forceinline__ int merge_row_lists(const uint64_t* L, int n_splits, int K, uint64_t* C, uint64_t* top,
-                               int* act, int lane) {
-  const int nh = (n_splits + kWave - 1) / kWave;      // <= kMaxHeadSlots
+template <int NH>
+__device__ __forceinline__ int merge_row_lists_nh(const uint64_t* L, int n_splits, int K, uint64_t* C,
+                                                  uint64_t* top, int* act, int lane) {
+  constexpr int kMaxHeadSlots = NH;                  // list heads per lane
+  const int nh = (n_splits + kWave - 1) / kWave;      // <= NH
   uint64_t h[kMaxHeadSlots];
 #pragma unroll
   for (int i = 0; i < kMaxHeadSlots; ++i) {
@@ -91,10 +94,9 @@ __device__ __forceinline__ int merge_row_lists(const uint64_t* L, int n_splits, 
     // lists are sorted: one whose last entry here is below the bound is done
     if (!__any(e[15] != 0ull && e[15] >= lo)) break;
   }
-  if (cnt <= kWave) {                    // rank the candidates directly
+  if (cnt <= kWave) {                    // one candidate per lane: rank in registers
     const uint64_t mine = lane < cnt ? C[lane] : 0ull;
-    int rank = 0;
-    for (int o = 0; o < cnt; ++o) rank += C[o] > mine;
+    const int rank = wave_rank_lanes(mine, cnt);
     if (lane < cnt && rank < K) top[rank] = mine;
     return cnt < K ? cnt : K;
   }
@@ -103,8 +105,16 @@ __device__ __forceinline__ int merge_row_lists(const uint64_t* L, int n_splits, 
   return m;
 }
 
+__device__ __forceinline__ int merge_row_lists(const uint64_t* L, int n_splits, int K, uint64_t* C, uint64_t* top,
+                                               int* act, int lane) {
+  if (n_splits <= kWave) return merge_row_lists_nh<1>(L, n_splits, K, C, top, act, lane);
+  if (n_splits <= 2 * kWave) return merge_row_lists_nh<2>(L, n_splits, K, C, top, act, lane);
+  if (n_splits <= 4 * kWave) return merge_row_lists_nh<4>(L, n_splits, K, C, top, act, lane);
+  return merge_row_lists_nh<kMaxHeads>(L, n_splits, K, C, top, act, lane);
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void attend_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   constexpr int KSTEP = D / 32;
   constexpr int NT = D / 16;
   constexpr int VROW = kChunk + 8;     // bf16 elements per V^T row
@@ -300,8 +310,10 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(DecodeArgs a) {
   const int n_blk = a.n_blocks;
   uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (br * a.Hq + (int64_t)g * G) * D;
   float* part = a.partials + (row * n_blk + blk) * (int64_t)(G * D);
-  for (int e = tid; e < G * D; e += 256) {
-    const float v = (osum[0][e] + osum[1][e]) + (osum[2][e] + osum[3][e]);
+  for (int e = tid; e < G * D; e += kThreads) {
+    float v = osum[0][e];
+#pragma unroll
+    for (int x = 1; x < kSlotsPerBlock; ++x) v += osum[x][e];
     if (n_blk == 1) op[e] = f32_to_bf16(v);
     else publish(&part[e], v);
   }
@@ -312,9 +324,9 @@ __global__ __launch_bounds__(256) void attend_decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (!last) return;
   const float* pb = a.partials + row * n_blk * (int64_t)(G * D);
-  for (int e = tid; e < G * D; e += 256) {
+  for (int e = tid; e < G * D; e += kThreads) {
     float v = 0.f;
-#pragma unroll 8
+#pragma unroll 16
     for (int p = 0; p < n_blk; ++p) v += fetch(&pb[(int64_t)p * G * D + e]);
     op[e] = f32_to_bf16(v);
   }
@@ -351,7 +363,7 @@ hipError_t launch_merge_lists(const MergeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attend_decode(const DecodeArgs& a, int64_t rows, int D, int G, hipStream_t st) {
-  const dim3 grid((unsigned)rows, (unsigned)a.n_blocks, 1), block(256);
+  const dim3 grid((unsigned)rows, (unsigned)a.n_blocks, 1), block(kThreads);
 #define HSA_DEC_CASE(DD, GG)                                                                  \
   if (D == DD && G == GG) {                                                                   \
     hipLaunchKernelGGL((attend_decode_kernel<DD, GG>), grid, block, 0, st, a);                 \

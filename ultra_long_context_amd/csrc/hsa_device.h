@@ -235,6 +235,20 @@ __device__ __forceinline__ int wave_keep_top(uint64_t* arr, int n, int K, int la
   return off;
 }
 
+// Rank of each lane's candidate e among the candidates of lanes [0, n) (one
+// per lane, unique nonzero keys; n wave-uniform): the number of them above e.
+// Lanes are read with v_readlane, so no memory round trip is involved.
+__device__ __forceinline__ int wave_rank_lanes(uint64_t e, int n) {
+  const uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
+  int rank = 0;
+  for (int o = 0; o < n; ++o) {
+    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, o) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, o);
+    rank += x > e;
+  }
+  return rank;
+}
+
 // Rank-sorts arr[0..m) (m <= 64, unique keys) into dst[0..m), best first.
 // dst must not alias arr.
 __device__ __forceinline__ void wave_rank_sort(const uint64_t* arr, int m, uint64_t* dst, int lane) {

@@ -416,11 +416,12 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
     v[i] = S[w][lane + kWave * i];
     mx = max(mx, v[i]);
   }
-  uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  uint32_t tau = 0;                 // K lane maxima reach tau (upper 16 key bits)
+  for (int bit = 15; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
-    if (__popcll(__ballot(mx >= cand)) >= K) tau = cand;
+    if (__popcll(__ballot((mx >> 16) >= cand)) >= K) tau = cand;
   }
+  tau <<= 16;
   int total = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) total += wave_count(v[i] != 0u && v[i] >= tau);
@@ -450,10 +451,32 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
     if (keep) C[n + __popcll(mask & lanemask_lt())] = pack_cand(v[i], (uint32_t)(c_begin + lane + kWave * i));
     n += __popcll(mask);
   }
+  const int64_t row_flat = (b * a.Lq + rw) * a.Hkv + g;
+  if (n <= kWave) {                 // one candidate per lane: rank them in registers
+    const uint64_t e = lane < n ? C[lane] : 0ull;
+    const int rank = wave_rank_lanes(e, n);
+    const int m = n < K ? n : K;
+    if (!rw_ok) return;
+    if (a.n_splits == 1) {
+      int32_t* idx = a.out_idx + row_flat * K;
+      float* score = a.out_score + row_flat * K;
+      if (lane < n && rank < K) {
+        idx[rank] = (int32_t)cand_chunk(e);
+        score[rank] = key_score(cand_key(e)) * a.ret_scale;
+      }
+      if (lane >= m && lane < K) {
+        idx[lane] = -1;
+        score[lane] = -INFINITY;
+      }
+    } else {
+      uint64_t* list = a.lists + (row_flat * a.n_splits + s) * K;
+      if (lane < n && rank < K) list[rank] = e;
+      if (lane >= m && lane < K) list[lane] = 0ull;
+    }
+    return;
+  }
   const int m = wave_keep_top<kWideCandCap / kWave>(C, n, K, lane);
   wave_rank_sort(C, m, top[w], lane);
-
-  const int64_t row_flat = (b * a.Lq + rw) * a.Hkv + g;
   if (a.n_splits == 1) {
     if (rw_ok) write_selection(top[w], m, K, lane, a.out_idx + row_flat * K, a.out_score + row_flat * K,
                                a.ret_scale);
