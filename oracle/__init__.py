@@ -48,6 +48,8 @@ def _load():
         lib.hsa_oracle_attend_blend.argtypes = [i64] * 7 + [dbl, i32, i32] + [vp] * 5 + [vp, i64, vp, vp]
         lib.hsa_oracle_raw_scores.restype = i64
         lib.hsa_oracle_raw_scores.argtypes = [i64] * 6 + [i32, vp, vp, i64, i64, vp]
+        lib.hsa_oracle_chunk_landmarks.restype = i32
+        lib.hsa_oracle_chunk_landmarks.argtypes = [i64] * 4 + [i32, vp, i64, i64, vp]
         lib.hsa_oracle_max_threads.restype = i32
         lib.hsa_oracle_set_threads.argtypes = [i32]
         _lib = lib
@@ -152,6 +154,20 @@ def raw_scores(q_ret, landmarks, *, q_pos0: int, kv_len: int, flat_row: int, g: 
     if n < 0:
         raise ValueError("bad arguments")
     return raw, int(n)
+
+
+def chunk_landmarks(k, *, chunk_begin: int = 0, chunk_end: int | None = None):
+    """fp64 landmarks (chunk means of the keys) of chunks [chunk_begin, chunk_end)
+    for k [B, Hkv, Lkv, d].  Returns [B, Hkv, chunk_end - chunk_begin, d]."""
+    kk = np.ascontiguousarray(k)
+    B, Hkv, Lkv, d = kk.shape
+    c1 = Lkv // 64 if chunk_end is None else int(chunk_end)
+    out = np.empty((B, Hkv, max(0, c1 - int(chunk_begin)), d), np.float64)
+    st = _load().hsa_oracle_chunk_landmarks(B, Hkv, Lkv, d, _is_bf16(kk), _ptr(kk), int(chunk_begin), c1,
+                                            _ptr(out))
+    if st != 0:
+        raise ValueError("hsa_oracle_chunk_landmarks: bad arguments")
+    return out
 
 
 def max_threads() -> int:

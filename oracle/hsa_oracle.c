@@ -351,6 +351,35 @@ int64_t hsa_oracle_raw_scores(int64_t B, int64_t Lq, int64_t q_pos0, int64_t Lkv
   return n;
 }
 
+/*
+ * Landmark of chunk c of one (batch, kv head): the mean of the chunk's 64
+ * stored keys.  Step 1 of the page gives every chunk one landmark from a learned
+ * encoder, which needs trained weights; the workloads' stand-in (the chunk mean
+ * of the keys) is what this computes, in fp64, summing in key order.
+ * out [B, Hkv, c_end - c_begin, d] receives the landmarks of chunks
+ * [c_begin, c_end).
+ */
+int hsa_oracle_chunk_landmarks(int64_t B, int64_t Hkv, int64_t Lkv, int64_t d, int is_bf16,
+                               const void* k, int64_t c_begin, int64_t c_end, double* out) {
+  const int64_t Nc = Lkv / ORC_CHUNK;
+  if (B < 1 || Hkv < 1 || d < 1 || Lkv < 0 || !k || !out || c_begin < 0 || c_end < c_begin || c_end > Nc)
+    return ORC_BAD_ARGS;
+  const int64_t nc = c_end - c_begin;
+#pragma omp parallel for schedule(static)
+  for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+    for (int64_t c = 0; c < nc; ++c) {
+      const int64_t row0 = bg * Lkv + (c_begin + c) * ORC_CHUNK;
+      double* o = out + (bg * nc + c) * d;
+      for (int64_t x = 0; x < d; ++x) {
+        double s = 0.0;
+        for (int64_t j = 0; j < ORC_CHUNK; ++j) s += elem(k, (row0 + j) * d + x, is_bf16);
+        o[x] = s / ORC_CHUNK;
+      }
+    }
+  }
+  return ORC_OK;
+}
+
 int hsa_oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -382,3 +382,64 @@ def test_raw_scores_match_selection():
     assert n == 6 and np.all(np.isnan(raw[6:]))
     idx, score, _, _ = run(inp, rows=[r], with_output=False)
     np.testing.assert_array_equal(raw[idx[0, 0]] / 8.0, score[0, 0])
+
+
+# ----------------------------------------------------------------------------
+# landmark stand-in (chunk mean of the keys): Step 1 gives one landmark per
+# 64-token chunk; the workloads' stand-in for the learned encoder is the mean
+# ----------------------------------------------------------------------------
+
+def test_landmarks_of_constant_chunks_are_the_constant():
+    """Catches a wrong divisor, a dropped key or a chunk offset error."""
+    rng = np.random.default_rng(3)
+    B, Hkv, nc, d = 2, 3, 5, 16
+    vals = rng.standard_normal((B, Hkv, nc, d)).astype(np.float32)
+    k = np.repeat(vals[:, :, :, None, :], 64, axis=3).reshape(B, Hkv, nc * 64, d)
+    out = oracle.chunk_landmarks(k)
+    assert np.array_equal(out, vals.astype(np.float64))
+
+
+def test_landmarks_exact_on_integer_keys():
+    """Integer keys: the mean is sum/64, computed here with Python integers."""
+    rng = np.random.default_rng(4)
+    B, Hkv, L, d = 1, 2, 64 * 7 + 19, 8          # trailing partial chunk has no landmark
+    ki = rng.integers(-50, 51, size=(B, Hkv, L, d))
+    k = ki.astype(np.float32)
+    out = oracle.chunk_landmarks(k)
+    assert out.shape == (B, Hkv, 7, d)
+    for b in range(B):
+        for g in range(Hkv):
+            for c in range(7):
+                for x in range(d):
+                    s = sum(int(v) for v in ki[b, g, 64 * c:64 * c + 64, x])
+                    assert out[b, g, c, x] == s / 64          # exact: s / 64 is a dyadic rational
+
+
+def test_landmarks_range_and_locality():
+    """A chunk range equals the same slice of the full result, and changing one
+    key changes only its own chunk's landmark."""
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((1, 2, 64 * 9, 8)).astype(np.float32)
+    full = oracle.chunk_landmarks(k)
+    part = oracle.chunk_landmarks(k, chunk_begin=3, chunk_end=7)
+    assert np.array_equal(part, full[:, :, 3:7])
+    k2 = k.copy()
+    k2[0, 1, 64 * 5 + 17, 3] += 1.0
+    diff = np.argwhere(oracle.chunk_landmarks(k2) != full)
+    assert diff.tolist() == [[0, 1, 5, 3]]
+    assert oracle.chunk_landmarks(k, chunk_begin=4, chunk_end=4).shape == (1, 2, 0, 8)
+    with pytest.raises(ValueError):
+        oracle.chunk_landmarks(k, chunk_begin=2, chunk_end=10)
+
+
+def test_landmarks_match_the_generators_stand_in():
+    """The generator's landmarks without noise or needles are the stored chunk
+    means: an independent implementation of the same definition (bf16, RNE)."""
+    cfg = small_cfg(dtype="bf16", kv_len=64 * 20, q_len=64, n_kv_heads=2, n_q_heads=2)
+    inp = W.generate(cfg)
+    ref = W.store(oracle.chunk_landmarks(inp.k), "bf16")
+    a = W.bf16_bits_to_f32(ref).astype(np.float64)
+    b = W.bf16_bits_to_f32(inp.landmarks).astype(np.float64)
+    ulp = np.abs(b) * 2.0 ** -7
+    assert np.all(np.abs(a - b) <= ulp)          # at most one bf16 step apart
+    assert np.mean(a == b) > 0.99
