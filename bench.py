@@ -49,6 +49,7 @@ WORKLOADS = {"prefill_128K": 2, "decode_16M": 3}
 KERNELS = {
     ("decode_16M", "scan"): "scan_wide_kernel<true, 128>",
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
+    ("decode_16M", "landmarks"): "chunk_landmark_kernel<true, 128>",
     ("prefill_128K", "scan"): "scan_block_kernel<128>",
     ("prefill_128K", "bucket"): "chunk_count/scan/scatter kernels",
     ("prefill_128K", "attend"): "chunk_attend_kernel<128, 8>",
@@ -293,6 +294,21 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     dom = max(stage_ms, key=stage_ms.get)
     res["roofline"] = roofline(name, dom, stage_ms[dom], alg)
     res["hbm_frac_whole_step"] = (alg["bytes"] / 8e12) / (ms_mean / 1e3)
+    if name == "decode_16M":
+        # KV-cache maintenance beside the step: every chunk-mean landmark of the
+        # history rebuilt from K (hsa_chunk_landmarks), an HBM stream
+        lm_buf = torch.empty_like(lm)
+        lm_ms, _, _ = timer.time(timer.capture(lambda: hsa.chunk_landmarks(k, out=lm_buf)), steps)
+        nbytes = k.numel() * k.element_size() + lm_buf.numel() * lm_buf.element_size()
+        gbs = nbytes / (lm_ms / 1e3) / 1e9
+        res["landmark_rebuild"] = dict(kernel=KERNELS[(name, "landmarks")], chunks=cfg.batch * cfg.n_kv_heads * cfg.n_chunks,
+                                       ms=lm_ms, bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS,
+                                       unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                                       traffic=measured_traffic(name, KERNELS[(name, "landmarks")]),
+                                       algorithmic_per_launch=nbytes,
+                                       algorithmic_units="64*d*2 B of keys read + d*2 B written per chunk")
+        log("[bench] %s: landmark rebuild %.4f ms, %.0f GB/s" % (name, lm_ms, gbs))
+        del lm_buf
     if cpu_baseline:
         res["cpu_baseline"] = oracle_baseline(cfg, inp)
     del dev, q_ret, lm, q_attn, k, v, out, inp
@@ -451,7 +467,8 @@ def main():
         if name == main_name:
             continue
         sub = {k: r[k] for k in ("value", "ms_per_step", "ms_median", "wall_ms_per_step",
-                                 "warm_ms_per_step", "roofline", "hbm_frac_whole_step")}
+                                 "warm_ms_per_step", "roofline", "hbm_frac_whole_step",
+                                 "landmark_rebuild") if k in r}
         sub["unit"] = "query-tokens/s"
         sub["config"] = cfg_dict(r["config"])
         sub["stage_ms"] = r["stage_ms"]

@@ -127,6 +127,21 @@ hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret, const void
                          int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Landmarks of chunks [chunk_begin, chunk_end) of every (batch, kv head): the
+ * mean of each chunk's 64 keys, accumulated in fp32 and stored in the shape's
+ * dtype (bf16: round to nearest even).  Step 1 of "How It Works (Technically)"
+ * gives every chunk one landmark from a learned encoder; without trained
+ * weights this chunk mean is the stand-in.  It also keeps a KV cache's
+ * landmarks current: after appending tokens to k, call it for the chunks the
+ * append completed.
+ * Uses shape->batch, n_kv_heads, kv_len, head_dim and dtype only.
+ * k [B, Hkv, kv_len, d] is read; landmarks [B, Hkv, kv_len / 64, d] is written
+ * for the chunks in the range only.  Requires 0 <= chunk_begin <= chunk_end <=
+ * kv_len / 64 (HSA_ERR_BAD_SHAPE otherwise); an empty range launches nothing.
+ * Pointers 16-byte aligned (HSA_ERR_MISALIGNED).  Asynchronous on `stream`. */
+hsa_status_t hsa_chunk_landmarks(const hsa_shape_t* shape, const void* k, void* landmarks,
+                                 int64_t chunk_begin, int64_t chunk_end, void* stream);
+
 /* Kernel stages of a forward call, for hsa_forward_profiled.  A stage the
  * plan does not run records nothing (e.g. MERGE when the attend merges the
  * per-split candidate lists itself, BUCKET and COMBINE outside the chunk-major

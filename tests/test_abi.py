@@ -144,3 +144,22 @@ def test_torch_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         h.forward(x, torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16), x, torch.zeros(1, 1, 64, 128),
                   torch.zeros(1, 1, 64, 128), q_pos0=0, top_k=1)
+
+
+def test_chunk_landmarks_checks_arguments():
+    lib = h.load_library()
+    buf = FakeBuf()
+    shp = h.make_shape(batch=1, q_len=1, kv_len=64 * 10, q_pos0=0, n_q_heads=1, n_kv_heads=1,
+                       head_dim=128, top_k=1, dtype=h.DTYPE_BF16)
+    call = lambda s, k, lm, c0, c1: lib.hsa_chunk_landmarks(ctypes.byref(s) if s is not None else None,
+                                                             k, lm, c0, c1, None)
+    assert call(None, buf.ptr, buf.ptr, 0, 1) == 1
+    assert call(shp, buf.ptr, buf.ptr, -1, 1) == 2
+    assert call(shp, buf.ptr, buf.ptr, 3, 2) == 2
+    assert call(shp, buf.ptr, buf.ptr, 0, 11) == 2                 # past the last complete chunk
+    assert call(shp, buf.ptr, buf.ptr, 4, 4) == 0                  # empty range: nothing launched
+    assert call(shp, None, buf.ptr, 0, 1) == 1
+    assert call(shp, buf.ptr, ctypes.c_void_p(buf.ptr.value + 8), 0, 1) == 6
+    bad = h.make_shape(batch=1, q_len=1, kv_len=640, q_pos0=0, n_q_heads=1, n_kv_heads=1,
+                       head_dim=96, top_k=1, dtype=h.DTYPE_BF16)
+    assert call(bad, buf.ptr, buf.ptr, 0, 1) == 3

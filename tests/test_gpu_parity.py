@@ -326,3 +326,49 @@ def test_chunk_major_given_selection_with_gaps(hsa):
     got = out_to_f64(out).reshape(cfg.q_len, cfg.n_q_heads, cfg.head_dim)
     assert np.abs(got[rows] - ref).max() <= TOL["bf16"]
     assert np.all(got[7] == 0)
+
+
+# ----------------------------------------------------------------------------
+# chunk-mean landmarks (the Step 1 stand-in; KV-cache maintenance)
+# ----------------------------------------------------------------------------
+
+def _landmark_err(got_t, ref64, dtype):
+    got = out_to_f64(got_t)
+    return np.abs(got - ref64).max() if ref64.size else 0.0
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+def test_chunk_landmarks_parity(hsa, dtype, d):
+    """All complete chunks of a ragged history (trailing partial chunk ignored),
+    then a sub-range written into an existing buffer (the rest untouched)."""
+    import torch
+    cfg = small(batch=2, n_kv_heads=3, n_q_heads=3, q_len=64, kv_len=64 * 37 + 21, head_dim=d, dtype=dtype)
+    inp = W.generate(cfg)
+    k = to_device(inp.k, dtype)
+    ref = oracle.chunk_landmarks(inp.k)
+    got = hsa.chunk_landmarks(k)
+    torch.cuda.synchronize()
+    tol = TOL[dtype] if dtype == "f32" else 2.0 ** -8 * max(1.0, np.abs(ref).max())
+    assert _landmark_err(got, ref, dtype) <= tol
+    sentinel = torch.full_like(got, 7.0)
+    hsa.chunk_landmarks(k, chunk_begin=5, chunk_end=19, out=sentinel)
+    torch.cuda.synchronize()
+    s64 = out_to_f64(sentinel)
+    assert np.all(s64[:, :, :5] == 7.0) and np.all(s64[:, :, 19:] == 7.0)
+    assert np.abs(s64[:, :, 5:19] - ref[:, :, 5:19]).max() <= tol
+
+
+def test_chunk_landmarks_decode_history_sampled(hsa):
+    """The 16M-token decode history: every landmark rebuilt on the GPU, sampled
+    chunks checked against the oracle."""
+    import torch
+    cfg = W.CONFIGS[3]
+    inp = W.generate(cfg)
+    k = to_device(inp.k, cfg.dtype)
+    got = out_to_f64(hsa.chunk_landmarks(k))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    cs = np.unique(np.concatenate([rng.choice(cfg.n_chunks, 60, replace=False), [0, cfg.n_chunks - 1]]))
+    for c in cs:
+        ref = oracle.chunk_landmarks(inp.k[:, :, 64 * c:64 * c + 64])
+        assert np.abs(got[:, :, c:c + 1] - ref).max() <= 2.0 ** -8 * max(1.0, np.abs(ref).max())

@@ -17,7 +17,7 @@ import math
 import os
 import threading
 
-__all__ = ["HsaError", "HsaShape", "forward", "retrieve_topk", "chunk_attend_blend",
+__all__ = ["HsaError", "HsaShape", "forward", "retrieve_topk", "chunk_attend_blend", "chunk_landmarks",
            "workspace_size", "new_workspace", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,7 @@ MAX_TOP_K = 64
 
 EXPORTED_SYMBOLS = ("hsa_workspace_size", "hsa_workspace_init", "hsa_retrieve_topk",
                     "hsa_chunk_attend_blend", "hsa_forward", "hsa_forward_profiled",
+                    "hsa_chunk_landmarks",
                     "hsa_status_string", "hsa_version")
 
 # kernel stages (hsa_stage_t)
@@ -92,6 +93,8 @@ def _load():
             lib.hsa_forward_profiled.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                  ctypes.POINTER(vp)]
             lib.hsa_forward_profiled.restype = st
+            lib.hsa_chunk_landmarks.argtypes = [shp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
+            lib.hsa_chunk_landmarks.restype = st
             lib.hsa_status_string.argtypes = [st]
             lib.hsa_status_string.restype = ctypes.c_char_p
             lib.hsa_version.restype = ctypes.c_int32
@@ -301,4 +304,29 @@ def chunk_attend_blend(q_attn, k, v, topk_idx, topk_score, *, qk_norm: bool = Tr
                                         ws.numel(), _stream(dev))
     if st:
         raise HsaError(st, "hsa_chunk_attend_blend")
+    return out
+
+
+def chunk_landmarks(k, *, chunk_begin: int = 0, chunk_end: int | None = None, out=None):
+    """Chunk-mean landmarks of chunks [chunk_begin, chunk_end) (all complete
+    chunks by default) for k [B, Hkv, Lkv, d]; writes and returns
+    out [B, Hkv, Lkv // 64, d] (allocated if None; chunks outside the range are
+    left as they are)."""
+    torch = _torch()
+    _check(k, "k", 4)
+    B, Hkv, Lkv, d = k.shape
+    nc = Lkv // CHUNK
+    c1 = nc if chunk_end is None else int(chunk_end)
+    if out is None:
+        out = torch.empty((B, Hkv, nc, d), dtype=k.dtype, device=k.device)
+    else:
+        _check(out, "out", 4, k.dtype)
+        if tuple(out.shape) != (B, Hkv, nc, d):
+            raise ValueError("out must be [B, Hkv, Lkv // 64, d]")
+    shape = make_shape(batch=B, q_len=1, kv_len=Lkv, q_pos0=0, n_q_heads=Hkv, n_kv_heads=Hkv,
+                       head_dim=d, top_k=1, dtype=_dtype_code(k))
+    st = _load().hsa_chunk_landmarks(ctypes.byref(shape), _ptr(k), _ptr(out), int(chunk_begin), c1,
+                                     _stream(k.device))
+    if st:
+        raise HsaError(st, "hsa_chunk_landmarks")
     return out

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhsa.so")
-SOURCES = ["hsa_api.hip", "retrieve.hip", "attend.hip", "attend_chunk.hip", "attend_decode.hip"]
+SOURCES = ["hsa_api.hip", "retrieve.hip", "attend.hip", "attend_chunk.hip", "attend_decode.hip",
+           "landmarks.hip"]
 ARCH = os.environ.get("HSA_OFFLOAD_ARCH", "gfx950")
 
 

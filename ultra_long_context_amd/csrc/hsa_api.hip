@@ -352,6 +352,31 @@ HSA_EXPORT hsa_status_t hsa_forward_profiled(const hsa_shape_t* shape, const voi
                            ws_bytes, stream, mk);
 }
 
+HSA_EXPORT hsa_status_t hsa_chunk_landmarks(const hsa_shape_t* shape, const void* k, void* landmarks,
+                                            int64_t chunk_begin, int64_t chunk_end, void* stream) {
+  if (!shape) return HSA_ERR_NULL_POINTER;
+  if (shape->batch < 1 || shape->n_kv_heads < 1 || shape->kv_len < 0) return HSA_ERR_BAD_SHAPE;
+  if (shape->head_dim != 64 && shape->head_dim != 128) return HSA_ERR_UNSUPPORTED;
+  if (shape->dtype != HSA_DTYPE_F32 && shape->dtype != HSA_DTYPE_BF16) return HSA_ERR_UNSUPPORTED;
+  const int64_t Nc = shape->kv_len / HSA_CHUNK_TOKENS;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > Nc) return HSA_ERR_BAD_SHAPE;
+  const int64_t lim = INT64_C(1) << 60;
+  if (!hsa::mul_ok((int64_t)shape->batch * shape->n_kv_heads, shape->kv_len, lim) ||
+      !hsa::mul_ok((int64_t)shape->batch * shape->n_kv_heads * shape->kv_len, shape->head_dim, lim))
+    return HSA_ERR_BAD_SHAPE;
+  hsa::LandmarkArgs a;
+  a.k = k; a.landmarks = landmarks; a.Lkv = shape->kv_len; a.Nc = Nc;
+  a.c_begin = chunk_begin; a.n_chunks = chunk_end - chunk_begin;
+  a.jobs = (int64_t)shape->batch * shape->n_kv_heads * a.n_chunks;
+  if (a.jobs == 0) return HSA_OK;
+  if ((a.jobs + 3) / 4 > INT32_MAX) return HSA_ERR_BAD_SHAPE;
+  hsa_status_t st;
+  if ((st = hsa::check_ptrs({k, landmarks})) != HSA_OK) return st;
+  return hsa::launch_chunk_landmarks(a, shape->dtype == HSA_DTYPE_BF16, shape->head_dim,
+                                     static_cast<hipStream_t>(stream)) == hipSuccess
+             ? HSA_OK : HSA_ERR_DEVICE;
+}
+
 HSA_EXPORT const char* hsa_status_string(hsa_status_t status) {
   switch (status) {
     case HSA_OK: return "success";

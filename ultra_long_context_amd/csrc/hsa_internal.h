@@ -109,6 +109,14 @@ struct ChunkArgs {
   int32_t qk_norm;
 };
 
+// Chunk-mean landmarks of chunks [c_begin, c_begin + n_chunks) of every (b, kv head).
+struct LandmarkArgs {
+  const void* k;          // [B, Hkv, Lkv, D]
+  void* landmarks;        // [B, Hkv, Nc, D]
+  int64_t Lkv, Nc, c_begin, n_chunks, jobs;   // jobs = B * Hkv * n_chunks
+};
+
+hipError_t launch_chunk_landmarks(const LandmarkArgs& a, bool bf16, int D, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 int scan_wide_chunks();
