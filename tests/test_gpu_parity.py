@@ -372,3 +372,46 @@ def test_chunk_landmarks_decode_history_sampled(hsa):
     for c in cs:
         ref = oracle.chunk_landmarks(inp.k[:, :, 64 * c:64 * c + 64])
         assert np.abs(got[:, :, c:c + 1] - ref).max() <= 2.0 ** -8 * max(1.0, np.abs(ref).max())
+
+
+def test_decode_with_incremental_append(hsa):
+    """Decode steps over a growing history: each step appends 16 tokens, the
+    chunks the append completes get their landmarks (hsa_chunk_landmarks), and
+    the 16 new tokens query the history (hsa_forward).  Checked against the
+    oracle on the same landmarks."""
+    import torch
+    L0, steps, T = 64 * 40 + 24, 5, 16
+    cfg = small(batch=1, n_kv_heads=1, n_q_heads=8, q_len=T, kv_len=L0 + steps * T, top_k=8, head_dim=128)
+    inp = W.generate(cfg)
+    k_all, v_all = to_device(inp.k, "bf16"), to_device(inp.v, "bf16")
+    lm = torch.zeros((1, 1, cfg.kv_len // 64, 128), dtype=torch.bfloat16, device="cuda:0")
+    hsa.chunk_landmarks(k_all[:, :, :L0], out=lm[:, :, :L0 // 64])
+    rng = np.random.default_rng(11)
+    for s in range(steps):
+        L = L0 + (s + 1) * T                         # history after this step's append
+        nc_old, nc = (L - T) // 64, L // 64
+        k, v = k_all[:, :, :L].contiguous(), v_all[:, :, :L].contiguous()
+        if nc > nc_old:
+            view = lm[:, :, :nc].contiguous()
+            hsa.chunk_landmarks(k, chunk_begin=nc_old, chunk_end=nc, out=view)
+            lm[:, :, :nc] = view
+        q_ret = to_device(W.store(rng.standard_normal((1, T, 1, 128)), "bf16"), "bf16")
+        q_attn = to_device(W.store(rng.standard_normal((1, T, 8, 128)), "bf16"), "bf16")
+        lmk = lm[:, :, :nc].contiguous()
+        out, idx, score = hsa.forward(q_ret, lmk, q_attn, k, v, q_pos0=L - T, top_k=8, return_topk=True)
+        torch.cuda.synchronize()
+        bits = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)
+        ref_lm = oracle.chunk_landmarks(inp.k[:, :, :L])
+        got_lm = out_to_f64(lmk)
+        assert np.abs(got_lm - ref_lm).max() <= 2.0 ** -8 * max(1.0, np.abs(ref_lm).max())
+        oi, os_, _, oo = oracle.forward(bits(q_ret), bits(lmk), bits(q_attn), bits(k), bits(v),
+                                        q_pos0=L - T, top_k=8)
+        sub = replace(cfg, q_len=T, kv_len=L, q_pos0=L - T)
+        step_inp = W.HsaInputs(sub, bits(q_ret), bits(lmk), bits(q_attn), bits(k), bits(v), [])
+        rows = np.arange(T)
+        gi = idx.cpu().numpy().reshape(T, 1, 8)
+        gs = score.cpu().numpy().reshape(T, 1, 8)
+        rep = check_selection(step_inp, rows, gi, gs, oi, os_, ret_scale=oracle.default_scale(128))
+        err = check_output(step_inp, rows, out_to_f64(out).reshape(T, 8, 128), oo, atol=TOL["bf16"],
+                           rep=rep, gpu_idx=gi, qk_norm=True, attn_scale=None, ret_scale=None)
+        assert err <= TOL["bf16"]
