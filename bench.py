@@ -43,13 +43,17 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 VALU_FP32_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 FLOP (FMA) x 2.4 GHz, non-packed
 
-WORKLOADS = {"prefill_128K": 2, "decode_16M": 3}
+WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "global_32K": 1}
+# global_32K: the 32K training-window prefill with a top-K covering all 512
+# chunks (global HSA of the warm-up stage); the dense fused kernel runs it
+OVERRIDES = {"global_32K": dict(top_k=512, name="global_hsa_32K_gqa8")}
 
 # the kernel behind each (workload, stage) of the plan the library picks for it
 KERNELS = {
     ("decode_16M", "scan"): "scan_wide_kernel<true, 128>",
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
     ("decode_16M", "landmarks"): "chunk_landmark_kernel<true, 128>",
+    ("global_32K", "attend"): "attend_global_kernel<128, 8>",
     ("prefill_128K", "scan"): "scan_block_kernel<128>",
     ("prefill_128K", "bucket"): "chunk_count/scan/scatter kernels",
     ("prefill_128K", "attend"): "chunk_attend_kernel<128, 8>",
@@ -223,8 +227,12 @@ def roofline(workload, stage, ms, alg):
     """Roofline entry for one kernel stage: algorithmic bytes or FLOPs per launch
     over its measured duration."""
     kernel = KERNELS.get((workload, stage), stage)
-    prefill = workload.startswith("prefill")
-    if stage == "attend" and prefill:
+    prefill = workload.startswith("prefill") or workload.startswith("global")
+    if stage == "attend" and workload.startswith("global"):
+        units = ("mfma", alg["attend_flops"] + alg["scan_flops"],
+                 "4*G*64*d FLOP per (row, eligible chunk) x %d + 2*d per retrieval score x %d"
+                 % (alg["selections"], alg["candidates"]))
+    elif stage == "attend" and prefill:
         units = ("mfma", alg["attend_flops"], "4*G*64*d FLOP per selection x %d selections"
                  % alg["selections"])
     elif stage == "scan" and prefill:
@@ -250,7 +258,8 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     import ultra_long_context_amd as hsa
     import workloads as W
 
-    cfg = W.CONFIGS[WORKLOADS[name]]
+    from dataclasses import replace as dc_replace
+    cfg = dc_replace(W.CONFIGS[WORKLOADS[name]], **OVERRIDES.get(name, {}))
     t = time.perf_counter()
     inp = W.generate(cfg)
     log("[bench] %s: inputs generated in %.1fs" % (name, time.perf_counter() - t))
@@ -281,9 +290,13 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
                                                     top_k=cfg.top_k, out=out, stage_events=evs),
                             steps)
     log("[bench] %s: kernel stages (ms) %s" % (name, json.dumps(stage_ms)))
-    sel_out = hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=cfg.q_pos0, top_k=cfg.top_k,
-                          return_topk=True)
-    U = distinct_chunks(sel_out[1], cfg)
+    if cfg.top_k > hsa.MAX_TOP_K:          # global HSA: every eligible chunk is selected
+        sel_out = (None,)
+        U = cfg.batch * cfg.n_kv_heads * min(cfg.n_chunks, (cfg.q_pos0 + cfg.q_len - 1) // 64)
+    else:
+        sel_out = hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=cfg.q_pos0, top_k=cfg.top_k,
+                              return_topk=True)
+        U = distinct_chunks(sel_out[1], cfg)
     alg = algorithmic(cfg, U)
     del sel_out
 
@@ -403,7 +416,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workloads", default="prefill_128K,decode_16M")
+    ap.add_argument("--workloads", default="prefill_128K,decode_16M,global_32K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the 1 GiB calibration copy first (for counter passes)")
@@ -437,7 +450,7 @@ def main():
     timer = Timer()
     names = [w for w in args.workloads.split(",") if w]
     results = {}
-    for name in ["decode_16M", "prefill_128K"]:
+    for name in ["decode_16M", "global_32K", "prefill_128K"]:
         if name in names:
             results[name] = bench_workload(name, args.steps, args.warmup, timer,
                                            not args.no_cpu_baseline)

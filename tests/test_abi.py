@@ -60,7 +60,9 @@ def ws_size(shape):
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 2), (dict(q_len=0), 2), (dict(kv_len=-1), 2), (dict(q_pos0=-5), 2),
     (dict(n_q_heads=7, n_kv_heads=2), 2), (dict(n_q_heads=3, n_kv_heads=1), 3), (dict(n_q_heads=64), 3),
-    (dict(head_dim=96), 3), (dict(top_k=0), 2), (dict(top_k=65), 3), (dict(dtype=7), 3),
+    (dict(head_dim=96), 3), (dict(top_k=0), 2), (dict(top_k=65, n_q_heads=4), 3),
+    (dict(top_k=65, dtype=h.DTYPE_F32), 3), (dict(top_k=65, kv_len=1 << 20, q_pos0=1 << 19), 3),
+    (dict(dtype=7), 3),
 ])
 def test_shape_validation(kw, status):
     st, _ = ws_size(base(**kw))
@@ -103,8 +105,12 @@ def call_forward(shape, *, q=None, ws_bytes=None, ws_off=0, out=None, idx="none"
     if out is not None:
         p[5] = out
     i = s = None
+    keep = []
     if idx == "half":
         i = FakeBuf().ptr
+    elif idx == "both":
+        keep = [FakeBuf(), FakeBuf()]
+        i, s = keep[0].ptr, keep[1].ptr
     need = ws_size(shape)[1]
     return lib.hsa_forward(ctypes.byref(shape), p[0], p[1], p[2], p[3], p[4], p[5], i, s, ws.ptr,
                            need if ws_bytes is None else ws_bytes, None)
@@ -163,3 +169,22 @@ def test_chunk_landmarks_checks_arguments():
     bad = h.make_shape(batch=1, q_len=1, kv_len=640, q_pos0=0, n_q_heads=1, n_kv_heads=1,
                        head_dim=96, top_k=1, dtype=h.DTYPE_BF16)
     assert call(bad, buf.ptr, buf.ptr, 0, 1) == 3
+
+
+def test_global_top_k_planning():
+    """top_k above 64 is global HSA: only when it covers every row's eligible
+    chunks (bf16, G = 8 or 16), only through hsa_forward, without selection
+    outputs; it needs only the counter region of the workspace."""
+    st, n = ws_size(base(top_k=65))
+    assert st == 0 and n == 16384
+    st, _ = ws_size(base(top_k=4096, n_q_heads=16))
+    assert st == 0
+    lib = h.load_library()
+    shp = base(top_k=65)
+    bufs = [FakeBuf() for _ in range(4)]
+    assert lib.hsa_retrieve_topk(ctypes.byref(shp), bufs[0].ptr, bufs[1].ptr, bufs[2].ptr, bufs[3].ptr,
+                                 bufs[0].ptr, 1 << 20, None) == 3
+    assert lib.hsa_chunk_attend_blend(ctypes.byref(shp), bufs[0].ptr, bufs[1].ptr, bufs[2].ptr,
+                                      bufs[3].ptr, bufs[3].ptr, bufs[0].ptr, bufs[1].ptr, 1 << 20,
+                                      None) == 3
+    assert call_forward(shp, idx="both") == 3

@@ -415,3 +415,65 @@ def test_decode_with_incremental_append(hsa):
         err = check_output(step_inp, rows, out_to_f64(out).reshape(T, 8, 128), oo, atol=TOL["bf16"],
                            rep=rep, gpu_idx=gi, qk_norm=True, attn_scale=None, ret_scale=None)
         assert err <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------
+# global HSA: a top-K that covers every eligible chunk (warm-up stage)
+# ----------------------------------------------------------------------------
+
+def global_parity(hsa, inp, K, rows=None):
+    import torch
+    cfg = inp.cfg
+    dev = inputs_to_device(inp)
+    print("case global %s B=%d Lq=%d q_pos0=%d Lkv=%d Hq=%d Hkv=%d d=%d K=%d" % (
+        cfg.name, cfg.batch, cfg.q_len, cfg.q_pos0, cfg.kv_len, cfg.n_q_heads, cfg.n_kv_heads,
+        cfg.head_dim, K), flush=True)
+    out = hsa.forward(*dev, q_pos0=cfg.q_pos0, top_k=K, qk_norm=cfg.qk_norm)
+    torch.cuda.synchronize()
+    total = cfg.batch * cfg.q_len
+    rows = np.arange(total) if rows is None else np.asarray(rows)
+    _, _, _, oo = oracle.forward(inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v, q_pos0=cfg.q_pos0,
+                                 top_k=K, qk_norm=cfg.qk_norm, rows=rows)
+    got = out_to_f64(out).reshape(total, cfg.n_q_heads, cfg.head_dim)[rows]
+    err = np.abs(got - oo).max()
+    print("  max-abs err %.3e" % err, flush=True)
+    assert err <= TOL["bf16"]
+    return out
+
+
+@pytest.mark.parametrize("G,d", [(8, 128), (16, 128), (8, 64), (16, 64)])
+def test_global_hsa_prefill(hsa, G, d):
+    """Every eligible chunk selected (K > 64): dense in-chunk attention blended
+    by the softmax of all retrieval scores; early rows have no chunk (zero)."""
+    cfg = small(n_q_heads=G, n_kv_heads=1, head_dim=d, q_len=3000, kv_len=3000, top_k=8, seed=41 + G + d)
+    global_parity(hsa, W.generate(cfg), K=4096, rows=sample_rows(cfg, 300, seed=G))
+
+
+def test_global_hsa_appended_rows_and_batch(hsa):
+    """Appended rows (q_pos0 not chunk-aligned), two sequences, two kv heads."""
+    cfg = small(batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, q_len=700, q_pos0=2083, kv_len=2816,
+                top_k=8, seed=43)
+    global_parity(hsa, W.generate(cfg), K=65, rows=sample_rows(cfg, 300, seed=3))
+
+
+def test_global_hsa_uniform_scores_equal_chunk_mean(hsa):
+    """q_ret = 0: every score equal, so the output is the mean of the per-chunk
+    attentions (the pages' K >= #chunks invariant), through the dense path."""
+    cfg = small(n_q_heads=8, n_kv_heads=1, head_dim=128, q_len=512, kv_len=2048, q_pos0=1536, top_k=8,
+                seed=44)
+    inp = W.generate(cfg)
+    inp = replace(inp, q_ret=np.zeros_like(inp.q_ret))
+    global_parity(hsa, inp, K=100)
+
+
+def test_global_hsa_matches_sparse_path_when_k_covers(hsa):
+    """With <= 64 eligible chunks the sparse path at K = 64 selects them all:
+    both paths agree (each within the tolerance of the oracle)."""
+    import torch
+    cfg = small(n_q_heads=8, n_kv_heads=1, head_dim=128, q_len=1024, kv_len=4096, q_pos0=3072, top_k=64,
+                seed=45)
+    inp = W.generate(cfg)
+    dev = inputs_to_device(inp)
+    a = out_to_f64(hsa.forward(*dev, q_pos0=cfg.q_pos0, top_k=64))
+    b = out_to_f64(global_parity(hsa, inp, K=65))
+    assert np.abs(a - b).max() <= TOL["bf16"]

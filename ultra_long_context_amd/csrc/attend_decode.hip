@@ -28,8 +28,8 @@ constexpr int kMaxHeads = 8;          // list heads per lane: up to 512 splits
 // Exact top K of one row from its per-split lists L[s][0..K) (each sorted best
 // first, zero-padded); whole wave.  A list can only contribute if its head
 // reaches the K-th largest head, and then only entries at or above that head:
-// the heads give a bound (upper 16 key bits), the few lists above it are read
-// whole, and the surviving candidates are ranked.  Leaves the sorted selection
+// the per-lane largest heads give a bound (upper 16 key bits), the few lists
+// above it are read in batches, and the surviving candidates are ranked.  Leaves the sorted selection
 // in top[0..m) and returns m.  Loads are unconditional (indices clamped) so
 // they are all in flight together.
 template <int NH>
@@ -44,14 +44,16 @@ __device__ __forceinline__ int merge_row_lists_nh(const uint64_t* L, int n_split
     const uint64_t v = L[(int64_t)(sp < n_splits ? sp : 0) * K];
     h[i] = (i < nh && sp < n_splits) ? v : 0ull;
   }
-  uint32_t t16 = 0;                      // K heads have key >= t16 << 16
+  // K lanes whose largest head reaches t16 << 16 hold K distinct heads there,
+  // so the K-th largest head does too: one ballot per bisection step
+  uint64_t hmax = h[0];
+#pragma unroll
+  for (int i = 1; i < kMaxHeadSlots; ++i) hmax = h[i] > hmax ? h[i] : hmax;
+  const uint32_t hm16 = (uint32_t)(hmax >> 48);
+  uint32_t t16 = 0;
   for (int bit = 15; bit >= 0; --bit) {
     const uint32_t cand = t16 | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxHeadSlots; ++i)
-      if (i < nh) c += wave_count((uint32_t)(h[i] >> 48) >= cand);
-    if (c >= K) t16 = cand;
+    if (wave_count(hm16 >= cand) >= K) t16 = cand;
   }
   uint64_t lo = (uint64_t)t16 << 48;
   int n_on = 0;

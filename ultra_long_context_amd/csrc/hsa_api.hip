@@ -29,6 +29,7 @@ struct Plan {
   int32_t split_len, n_splits;
   bool wide;             // few-row scan: 16-wave workgroups, per-split lists
   bool block;            // many-row scan (bf16, K <= 32): 64 rows per workgroup
+  bool global;           // K covers every eligible chunk (K > 64): fused dense kernel
   int32_t attn_splits, slots_per_split, attn_mode;
   int64_t n_bins, max_items, n_bands;   // chunk-major attend
   size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
@@ -41,8 +42,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a >= 0 && b >= 0 && (b == 0 || a <= limit / b); }
 
 // check_positions: reject rows whose eligible chunks would reach past the
-// history (not needed when the caller supplies the selection).
-hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
+// history (not needed when the caller supplies the selection).  allow_global:
+// a top_k above 64 that covers every row's eligible chunks is planned as
+// global HSA (hsa_forward only).
+hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool allow_global = false) {
   if (!s) return HSA_ERR_NULL_POINTER;
   if (s->batch < 1 || s->q_len < 1 || s->kv_len < 0 || s->q_pos0 < 0 || s->n_q_heads < 1 ||
       s->n_kv_heads < 1 || s->top_k < 1)
@@ -51,7 +54,8 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
   const int32_t G = s->n_q_heads / s->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return HSA_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return HSA_ERR_UNSUPPORTED;
-  if (s->top_k > HSA_MAX_TOP_K) return HSA_ERR_UNSUPPORTED;
+  const bool big_k = s->top_k > HSA_MAX_TOP_K;
+  if (big_k && !allow_global) return HSA_ERR_UNSUPPORTED;
   if (s->dtype != HSA_DTYPE_F32 && s->dtype != HSA_DTYPE_BF16) return HSA_ERR_UNSUPPORTED;
   if (s->flags & ~HSA_FLAG_QK_L2NORM) return HSA_ERR_UNSUPPORTED;
   if (!(std::isfinite(s->ret_scale) && std::isfinite(s->attn_scale))) return HSA_ERR_BAD_SHAPE;
@@ -80,6 +84,17 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions) {
 
   const int64_t nmax = std::min<int64_t>(last_pos / HSA_CHUNK_TOKENS, Nc);
   p->n_max = (int32_t)nmax;
+  p->global = false;
+  if (big_k) {   // every eligible chunk selected: no top-K, no selection arrays
+    if (!p->bf16 || (G != 8 && G != 16) || s->top_k < nmax) return HSA_ERR_UNSUPPORTED;
+    p->global = true;
+    p->wide = p->block = false;
+    p->n_splits = 1;
+    p->attn_mode = 4;
+    p->off_counters = 0;
+    p->total = kCounterBytes;
+    return HSA_OK;
+  }
   // Scan plan.  Up to 2048 row blocks of 16 rows: the wide kernel (1024 chunks
   // per workgroup; with several splits a merge combines the per-split lists).
   // More row blocks than that: bf16 with K <= 32 takes the block kernel (64
@@ -254,7 +269,7 @@ using hsa::Plan;
 HSA_EXPORT hsa_status_t hsa_workspace_size(const hsa_shape_t* shape, size_t* bytes) {
   if (!bytes) return HSA_ERR_NULL_POINTER;
   Plan p;
-  const hsa_status_t st = hsa::make_plan(shape, &p, false);
+  const hsa_status_t st = hsa::make_plan(shape, &p, false, true);
   if (st != HSA_OK) return st;
   *bytes = p.total;
   return HSA_OK;
@@ -307,15 +322,27 @@ hsa_status_t forward_impl(const hsa_shape_t* shape, const void* q_ret, const voi
                           int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
                           void* stream, const Marks& mk) {
   Plan p;
-  hsa_status_t st = make_plan(shape, &p, true);
+  hsa_status_t st = make_plan(shape, &p, true, true);
   if (st != HSA_OK) return st;
   const void* lm = p.Nc > 0 ? landmarks : q_ret;
   const void* kk = p.Lkv > 0 ? k : q_attn;
   const void* vv = p.Lkv > 0 ? v : q_attn;
   if ((st = check_ptrs({q_ret, lm, q_attn, kk, vv, out})) != HSA_OK) return st;
   if ((topk_idx == nullptr) != (topk_score == nullptr)) return HSA_ERR_NULL_POINTER;
+  if (topk_idx && p.global) return HSA_ERR_UNSUPPORTED;   // the selection is every eligible chunk
   if (topk_idx && (st = check_ptrs({topk_idx, topk_score})) != HSA_OK) return st;
   if ((st = check_ws(p, ws, ws_bytes)) != HSA_OK) return st;
+  if (p.global) {
+    GlobalArgs g;
+    g.q_ret = q_ret; g.landmarks = lm; g.q_attn = q_attn; g.k = kk; g.v = vv; g.out = out;
+    g.Lq = p.Lq; g.q_pos0 = p.q_pos0; g.Lkv = p.Lkv; g.Nc = p.Nc; g.Hq = p.Hq; g.Hkv = p.Hkv;
+    g.ret_scale = p.ret_scale; g.attn_scale = p.attn_scale; g.qk_norm = p.qk_norm ? 1 : 0;
+    const hipStream_t gs = static_cast<hipStream_t>(stream);
+    if (mk.rec(kStageAttend, 0, gs) != hipSuccess || launch_attend_global(g, p.B, p.D, p.G, gs) != hipSuccess ||
+        mk.rec(kStageAttend, 1, gs) != hipSuccess)
+      return HSA_ERR_DEVICE;
+    return HSA_OK;
+  }
   char* w = static_cast<char*>(ws);
   int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(w + p.off_idx);
   float* score = topk_score ? topk_score : reinterpret_cast<float*>(w + p.off_score);

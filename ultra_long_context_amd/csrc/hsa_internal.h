@@ -117,6 +117,23 @@ struct LandmarkArgs {
 };
 
 hipError_t launch_chunk_landmarks(const LandmarkArgs& a, bool bf16, int D, hipStream_t st);
+
+// Top-K covering every eligible chunk: fused scores, in-chunk attention and
+// online blend over all eligible chunks (bf16, G = 8 or 16).
+struct GlobalArgs {
+  const void* q_ret;      // [B, Lq, Hkv, D]
+  const void* landmarks;  // [B, Hkv, Nc, D]
+  const void* q_attn;     // [B, Lq, Hq, D]
+  const void* k;          // [B, Hkv, Lkv, D]
+  const void* v;
+  void* out;              // [B, Lq, Hq, D]
+  int64_t Lq, q_pos0, Lkv, Nc;
+  int32_t Hq, Hkv;
+  float ret_scale, attn_scale;
+  int32_t qk_norm;
+};
+
+hipError_t launch_attend_global(const GlobalArgs& a, int64_t B, int D, int G, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 int scan_wide_chunks();
