@@ -48,6 +48,8 @@ def _load():
         lib.hsa_oracle_attend_blend.argtypes = [i64] * 7 + [dbl, i32, i32] + [vp] * 5 + [vp, i64, vp, vp]
         lib.hsa_oracle_raw_scores.restype = i64
         lib.hsa_oracle_raw_scores.argtypes = [i64] * 6 + [i32, vp, vp, i64, i64, vp]
+        lib.hsa_oracle_backward.restype = i32
+        lib.hsa_oracle_backward.argtypes = [i64] * 7 + [dbl, dbl, i32, i32] + [vp] * 13
         lib.hsa_oracle_chunk_landmarks.restype = i32
         lib.hsa_oracle_chunk_landmarks.argtypes = [i64] * 4 + [i32, vp, i64, i64, vp]
         lib.hsa_oracle_max_threads.restype = i32
@@ -154,6 +156,35 @@ def raw_scores(q_ret, landmarks, *, q_pos0: int, kv_len: int, flat_row: int, g: 
     if n < 0:
         raise ValueError("bad arguments")
     return raw, int(n)
+
+
+def backward(q_ret, landmarks, q_attn, k, v, dout, topk_idx, topk_score, *, qk_norm: bool = True,
+             ret_scale: float | None = None, attn_scale: float | None = None):
+    """Gradients of sum(out * dout) for a given selection topk_idx / topk_score
+    [B, Lq, Hkv, K] (scores are the s of Step 4).  All arrays in the stored
+    dtype (dout too).  Returns fp64 (dq_ret, dlandmarks, dq_attn, dk, dv)."""
+    arrs = [np.ascontiguousarray(a) for a in (q_ret, landmarks, q_attn, k, v, dout)]
+    bf = _is_bf16(arrs[0])
+    for a in arrs:
+        if _is_bf16(a) != bf:
+            raise TypeError("mixed input dtypes")
+    B, Lq, Hkv, d = arrs[0].shape
+    Hq = arrs[2].shape[2]
+    Lkv = arrs[3].shape[2]
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    sc = np.ascontiguousarray(topk_score, dtype=np.float64)
+    K = idx.shape[-1]
+    if idx.shape != (B, Lq, Hkv, K) or sc.shape != idx.shape or arrs[5].shape != arrs[2].shape:
+        raise ValueError("selection must be [B, Lq, Hkv, K] and dout like q_attn")
+    rs = default_scale(d) if ret_scale is None else float(ret_scale)
+    as_ = default_scale(d) if attn_scale is None else float(attn_scale)
+    outs = [np.empty(a.shape, np.float64) for a in (arrs[0], arrs[1], arrs[2], arrs[3], arrs[4])]
+    st = _load().hsa_oracle_backward(B, Lq, Lkv, Hq, Hkv, d, K, rs, as_, int(bool(qk_norm)), bf,
+                                     *[_ptr(a) for a in arrs], _ptr(idx), _ptr(sc),
+                                     *[_ptr(o) for o in outs])
+    if st != 0:
+        raise RuntimeError("hsa_oracle_backward failed with status %d" % st)
+    return tuple(outs)
 
 
 def chunk_landmarks(k, *, chunk_begin: int = 0, chunk_end: int | None = None):

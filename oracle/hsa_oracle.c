@@ -351,6 +351,182 @@ int64_t hsa_oracle_raw_scores(int64_t B, int64_t Lq, int64_t q_pos0, int64_t Lkv
   return n;
 }
 
+/* Gradient of x_hat = x / max(||x||, eps) (the query-key normalisation):
+ * with n = ||x|| > eps, dx = (dxh - xh (xh . dxh)) / n; below eps the divisor
+ * is the constant eps and dx = dxh / eps. */
+static void norm_backward(const double* x, int64_t d, const double* dxh, double* dx) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < d; ++i) ss += x[i] * x[i];
+  const double n = sqrt(ss);
+  if (n <= ORC_NORM_EPS) {
+    for (int64_t i = 0; i < d; ++i) dx[i] = dxh[i] / ORC_NORM_EPS;
+    return;
+  }
+  double dot = 0.0;
+  for (int64_t i = 0; i < d; ++i) dot += (x[i] / n) * dxh[i];
+  for (int64_t i = 0; i < d; ++i) dx[i] = (dxh[i] - (x[i] / n) * dot) / n;
+}
+
+/*
+ * HSA backward for a given selection: the gradients of sum(out * dout) with
+ * respect to every input of Steps 2-4.  The selection itself is discrete and
+ * carries no gradient; the gradient reaches the retrieval path through the
+ * blend weights w = softmax(s) (Step 4) and s = ret_scale * (q_ret . landmark)
+ * (Step 2), and the attention path through each chunk's softmax attention
+ * with the query-key normalisation (Step 3).  For one (b, r, g):
+ *   dw_k  = sum_h dout_h . O_k[h]          ds_k = w_k (dw_k - sum_j w_j dw_j)
+ *   dq_ret += ret_scale ds_k landmark[c_k]  dlandmark[c_k] += ret_scale ds_k q_ret
+ * and per head h and slot k, with P the in-chunk softmax and dO_k = w_k dout_h:
+ *   dv_t += P_t dO_k    dP_t = dO_k . v_t    dz_t = P_t (dP_t - sum_u P_u dP_u)
+ *   dqhat += attn_scale sum_t dz_t khat_t    dkhat_t += attn_scale dz_t qhat
+ * followed by the normalisation's gradient (norm_backward).  score is the
+ * given s of each slot (as hsa_oracle_attend_blend); idx as there.
+ * Outputs (fp64, overwritten): dq_ret [B,Lq,Hkv,d], dlm [B,Hkv,Nc,d],
+ * dq_attn [B,Lq,Hq,d], dk and dv [B,Hkv,Lkv,d].  Accumulation runs over rows
+ * in index order inside each (b, g), so results do not depend on threads.
+ */
+int hsa_oracle_backward(int64_t B, int64_t Lq, int64_t Lkv, int64_t Hq, int64_t Hkv, int64_t d,
+                        int64_t K, double ret_scale, double attn_scale, int qk_norm, int is_bf16,
+                        const void* q_ret, const void* landmarks, const void* q_attn, const void* k,
+                        const void* v, const void* dout, const int32_t* idx, const double* score,
+                        double* dq_ret, double* dlm, double* dq_attn, double* dk, double* dv) {
+  orc_problem P = make_problem(B, Lq, 0, Lkv, Hq, Hkv, d, K, ret_scale, attn_scale, qk_norm, is_bf16,
+                               q_ret, landmarks, q_attn, k, v);
+  if (check(&P) != ORC_OK || !dout || !idx || !score || !dq_ret || !dlm || !dq_attn || !dk || !dv)
+    return ORC_BAD_ARGS;
+  const int64_t G = Hq / Hkv, Nc = P.Nc;
+  int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+    const int64_t b = bg / Hkv, g = bg % Hkv;
+    double* dkh = calloc((size_t)(Lkv * d + 1), sizeof(double));      /* d khat, before the norm */
+    double* w = malloc(sizeof(double) * (size_t)K);
+    double* wdw = malloc(sizeof(double) * (size_t)K);
+    double* buf = malloc(sizeof(double) * (size_t)(8 * d + 4 * ORC_CHUNK));
+    if (!dkh || !w || !wdw || !buf) {
+#pragma omp critical
+      status = ORC_NO_MEMORY;
+      free(dkh); free(w); free(wdw); free(buf);
+      continue;
+    }
+    double *q = buf, *qh = buf + d, *dqh = buf + 2 * d, *dq = buf + 3 * d, *dob = buf + 4 * d;
+    double *kh = buf + 5 * d, *vt = buf + 6 * d, *tmp = buf + 7 * d;
+    double *pr = buf + 8 * d, *dp = pr + ORC_CHUNK, *kn = dp + ORC_CHUNK;
+    double* dv_bg = dv + bg * Lkv * d;
+    double* dlm_bg = dlm + bg * Nc * d;
+    for (int64_t i = 0; i < Lkv * d; ++i) dv_bg[i] = 0.0;
+    for (int64_t i = 0; i < Nc * d; ++i) dlm_bg[i] = 0.0;
+    for (int64_t r = 0; r < Lq; ++r) {
+      const int64_t srow = (b * Lq + r) * Hkv + g;
+      const int32_t* ix = idx + srow * K;
+      const int any = blend_weights(&P, ix, score + srow * K, w);
+      double* dqr = dq_ret + srow * d;
+      for (int64_t x = 0; x < d; ++x) dqr[x] = 0.0;
+      for (int64_t kk = 0; kk < K; ++kk) wdw[kk] = 0.0;
+      for (int64_t j = 0; j < G; ++j) {
+        const int64_t h = g * G + j;
+        const int64_t qo = ((b * Lq + r) * Hq + h) * d;
+        double ss = 0.0;
+        for (int64_t x = 0; x < d; ++x) {
+          q[x] = elem(q_attn, qo + x, is_bf16);
+          ss += q[x] * q[x];
+        }
+        double qn = 1.0;
+        if (qk_norm) {
+          qn = sqrt(ss);
+          if (qn < ORC_NORM_EPS) qn = ORC_NORM_EPS;
+        }
+        for (int64_t x = 0; x < d; ++x) {
+          qh[x] = q[x] / qn;
+          dqh[x] = 0.0;
+        }
+        for (int64_t kk = 0; kk < K && any; ++kk) {
+          const int64_t c = ix[kk];
+          if (c < 0 || c >= Nc) continue;
+          /* in-chunk softmax (Step 3), recomputed */
+          double mu = -INFINITY;
+          for (int64_t t = 0; t < ORC_CHUNK; ++t) {
+            const int64_t ko = (bg * Lkv + c * ORC_CHUNK + t) * d;
+            double kss = 0.0;
+            for (int64_t x = 0; x < d; ++x) {
+              const double kv = elem(k, ko + x, is_bf16);
+              kss += kv * kv;
+            }
+            kn[t] = 1.0;
+            if (qk_norm) {
+              kn[t] = sqrt(kss);
+              if (kn[t] < ORC_NORM_EPS) kn[t] = ORC_NORM_EPS;
+            }
+            double dot = 0.0;
+            for (int64_t x = 0; x < d; ++x) dot += qh[x] * (elem(k, ko + x, is_bf16) / kn[t]);
+            pr[t] = dot * attn_scale;
+            if (pr[t] > mu) mu = pr[t];
+          }
+          double den = 0.0;
+          for (int64_t t = 0; t < ORC_CHUNK; ++t) {
+            pr[t] = exp(pr[t] - mu);
+            den += pr[t];
+          }
+          for (int64_t t = 0; t < ORC_CHUNK; ++t) pr[t] /= den;
+          /* dO_k = w_k dout_h */
+          const int64_t oo = ((b * Lq + r) * Hq + h) * d;
+          for (int64_t x = 0; x < d; ++x) dob[x] = w[kk] * elem(dout, oo + x, is_bf16);
+          double pdp = 0.0;
+          for (int64_t t = 0; t < ORC_CHUNK; ++t) {
+            const int64_t vo = (bg * Lkv + c * ORC_CHUNK + t) * d;
+            double acc = 0.0;
+            for (int64_t x = 0; x < d; ++x) {
+              vt[x] = elem(v, vo + x, is_bf16);
+              acc += dob[x] * vt[x];
+              dv_bg[(c * ORC_CHUNK + t) * d + x] += pr[t] * dob[x];
+            }
+            dp[t] = acc;
+            pdp += pr[t] * acc;
+          }
+          wdw[kk] += pdp;                    /* w_k (dout_h . O_k[h]) */
+          for (int64_t t = 0; t < ORC_CHUNK; ++t) {
+            const double dz = pr[t] * (dp[t] - pdp) * attn_scale;
+            const int64_t ko = (bg * Lkv + c * ORC_CHUNK + t) * d;
+            for (int64_t x = 0; x < d; ++x) {
+              kh[x] = elem(k, ko + x, is_bf16) / kn[t];
+              dqh[x] += dz * kh[x];
+              dkh[(c * ORC_CHUNK + t) * d + x] += dz * qh[x];
+            }
+          }
+        }
+        if (qk_norm) norm_backward(q, d, dqh, dq);
+        else
+          for (int64_t x = 0; x < d; ++x) dq[x] = dqh[x];
+        for (int64_t x = 0; x < d; ++x) dq_attn[qo + x] = any ? dq[x] : 0.0;
+      }
+      if (!any) continue;
+      double swdw = 0.0;
+      for (int64_t kk = 0; kk < K; ++kk) swdw += wdw[kk];
+      const int64_t qro = srow * d;
+      for (int64_t kk = 0; kk < K; ++kk) {
+        const int64_t c = ix[kk];
+        if (c < 0 || c >= Nc) continue;
+        const double dr = ret_scale * (wdw[kk] - w[kk] * swdw);   /* ret_scale * ds_k */
+        const int64_t lo = (bg * Nc + c) * d;
+        for (int64_t x = 0; x < d; ++x) {
+          dqr[x] += dr * elem(landmarks, lo + x, is_bf16);
+          dlm_bg[c * d + x] += dr * elem(q_ret, qro + x, is_bf16);
+        }
+      }
+    }
+    /* keys: the normalisation's gradient after all rows */
+    for (int64_t t = 0; t < Lkv; ++t) {
+      const int64_t ko = (bg * Lkv + t) * d;
+      for (int64_t x = 0; x < d; ++x) tmp[x] = elem(k, ko + x, is_bf16);
+      if (qk_norm && t < Nc * ORC_CHUNK) norm_backward(tmp, d, dkh + t * d, dk + ko);
+      else
+        for (int64_t x = 0; x < d; ++x) dk[ko + x] = dkh[t * d + x];
+    }
+    free(dkh); free(w); free(wdw); free(buf);
+  }
+  return status;
+}
+
 /*
  * Landmark of chunk c of one (batch, kv head): the mean of the chunk's 64
  * stored keys.  Step 1 of the page gives every chunk one landmark from a learned

@@ -443,3 +443,148 @@ def test_landmarks_match_the_generators_stand_in():
     ulp = np.abs(b) * 2.0 ** -7
     assert np.all(np.abs(a - b) <= ulp)          # at most one bf16 step apart
     assert np.mean(a == b) > 0.99
+
+
+# ----------------------------------------------------------------------------
+# backward (the next step after the forward): gradients of sum(out * dout)
+# for a fixed selection
+# ----------------------------------------------------------------------------
+
+def _bwd_case(qk_norm=True, seed=21, B=1, Lq=40, Lkv=64 * 6 + 10, Hq=4, Hkv=2, d=16, K=3):
+    rng = np.random.default_rng(seed)
+    nc = Lkv // 64
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    q_ret, lm, q_attn = f(B, Lq, Hkv, d), f(B, Hkv, nc, d), f(B, Lq, Hq, d)
+    k, v, dout = f(B, Hkv, Lkv, d), f(B, Hkv, Lkv, d), f(B, Lq, Hq, d)
+    idx = np.full((B, Lq, Hkv, K), -1, np.int32)
+    for b in range(B):
+        for r in range(Lq):
+            for g in range(Hkv):
+                m = rng.integers(0, K + 1)           # 0..K used slots, some rows empty
+                idx[b, r, g, :m] = rng.choice(nc, size=m, replace=False)
+    return q_ret, lm, q_attn, k, v, dout, idx
+
+
+def _scores(q_ret, lm, idx, rs):
+    """s = ret_scale * q_ret . landmark[idx] (numpy fp64); -inf on unused slots."""
+    B, Lq, Hkv, K = idx.shape
+    s = np.full(idx.shape, -np.inf)
+    for b in range(B):
+        for g in range(Hkv):
+            L = lm[b, g].astype(np.float64)
+            for r in range(Lq):
+                ok = idx[b, r, g] >= 0
+                s[b, r, g, ok] = rs * (L[idx[b, r, g, ok]] @ q_ret[b, r, g].astype(np.float64))
+    return s
+
+
+def _torch_forward(q_ret, lm, q_attn, k, v, idx, qk_norm, rs, as_):
+    """The fixed-selection forward of Steps 2-4 in torch (fp64), for autograd."""
+    B, Lq, Hkv, K = idx.shape
+    Hq, d = q_attn.shape[2], q_attn.shape[3]
+    G = Hq // Hkv
+    nrm = lambda x: x / torch.clamp(torch.linalg.vector_norm(x, dim=-1, keepdim=True), min=1e-6)
+    outs = []
+    for b in range(B):
+        rows = []
+        for r in range(Lq):
+            heads = []
+            for g in range(Hkv):
+                ok = [kk for kk in range(K) if idx[b, r, g, kk] >= 0]
+                if not ok:
+                    heads.append(torch.zeros(G, d))
+                    continue
+                cs = [int(idx[b, r, g, kk]) for kk in ok]
+                s = torch.stack([rs * torch.dot(q_ret[b, r, g], lm[b, g, c]) for c in cs])
+                w = torch.softmax(s, 0)
+                q = q_attn[b, r, g * G:(g + 1) * G]
+                qh = nrm(q) if qk_norm else q
+                o = torch.zeros(G, d)
+                for wk, c in zip(w, cs):
+                    kc, vc = k[b, g, 64 * c:64 * c + 64], v[b, g, 64 * c:64 * c + 64]
+                    kh = nrm(kc) if qk_norm else kc
+                    p = torch.softmax(as_ * qh @ kh.T, dim=-1)
+                    o = o + wk * (p @ vc)
+                heads.append(o)
+            rows.append(torch.cat(heads, 0))
+        outs.append(torch.stack(rows))
+    return torch.stack(outs)
+
+
+@pytest.mark.parametrize("qk_norm", [True, False])
+def test_backward_matches_autograd_of_the_forward(qk_norm):
+    """torch autograd of the fixed-selection forward gives every gradient; the
+    oracle's hand-derived backward must agree (catches a dropped term of the
+    softmax or normalisation gradients, a missing blend weight, a wrong sign,
+    a transposed product, a wrong chunk offset in the scatter)."""
+    q_ret, lm, q_attn, k, v, dout, idx = _bwd_case(qk_norm=qk_norm)
+    d = q_ret.shape[-1]
+    rs, as_ = 1.0 / math.sqrt(d), 0.9
+    s = _scores(q_ret, lm, idx, rs)
+    ts = [torch.tensor(a.astype(np.float64), requires_grad=True) for a in (q_ret, lm, q_attn, k, v)]
+    out = _torch_forward(*ts, idx, qk_norm, rs, as_)
+    (out * torch.tensor(dout.astype(np.float64))).sum().backward()
+    got = oracle.backward(q_ret, lm, q_attn, k, v, dout, idx, s, qk_norm=qk_norm, ret_scale=rs, attn_scale=as_)
+    for name, g_or, t in zip(("dq_ret", "dlm", "dq_attn", "dk", "dv"), got, ts):
+        ref = t.grad.numpy()
+        assert np.abs(g_or - ref).max() <= 1e-9 * max(1.0, np.abs(ref).max()), name
+
+
+def test_backward_matches_finite_differences_of_the_oracle_forward():
+    """Central differences of the oracle's own forward (attend_blend with the
+    scores recomputed from q_ret and landmarks) at sampled coordinates."""
+    q_ret, lm, q_attn, k, v, dout, idx = _bwd_case(seed=22, Lq=12, Hq=2, Hkv=1, d=8, K=2)
+    d = q_ret.shape[-1]
+    rs = 1.0 / math.sqrt(d)
+    base = [a.copy() for a in (q_ret, lm, q_attn, k, v)]
+
+    def loss(arrs):
+        s = _scores(arrs[0], arrs[1], idx, rs)
+        B, Lq, Hkv, K = idx.shape
+        _, out = oracle.attend_blend(arrs[2], arrs[3], arrs[4], idx.reshape(B * Lq, Hkv, K),
+                                     s.reshape(B * Lq, Hkv, K))
+        return float((out.reshape(dout.shape) * dout.astype(np.float64)).sum())
+
+    grads = oracle.backward(*base, dout, idx, _scores(q_ret, lm, idx, rs))
+    rng = np.random.default_rng(5)
+    for which in range(5):
+        g = grads[which]
+        flat = np.flatnonzero(np.abs(g) > 1e-3)
+        for pos in rng.choice(flat, size=min(6, flat.size), replace=False):
+            arrs = [a.copy() for a in base]
+            x = arrs[which].reshape(-1)
+            x0 = np.float64(x[pos])
+            h = 1e-2 * max(1.0, abs(x0))
+            x[pos] = np.float32(x0 + h)
+            up, hp = loss(arrs), np.float64(x[pos]) - x0
+            x[pos] = np.float32(x0 - h)
+            dn, hm = loss(arrs), x0 - np.float64(x[pos])
+            fd = (up - dn) / (hp + hm)
+            assert abs(fd - g.reshape(-1)[pos]) <= 2e-3 * max(1.0, abs(fd)), (which, pos)
+
+
+def test_backward_invariants():
+    """Closed forms: with QK-norm the loss does not change under positive
+    rescaling of a query or key row, so those gradients are orthogonal to the
+    row; P sums to 1, so the V gradients of a (b, kv head) sum to the dout of
+    its rows that select something; a common shift of all landmarks leaves every
+    blend weight unchanged, so their gradients sum to 0."""
+    q_ret, lm, q_attn, k, v, dout, idx = _bwd_case(seed=23)
+    rs = 1.0 / math.sqrt(q_ret.shape[-1])
+    dq_ret, dlm, dq_attn, dk, dv = oracle.backward(q_ret, lm, q_attn, k, v, dout, idx,
+                                                   _scores(q_ret, lm, idx, rs))
+    assert np.abs((dq_attn * q_attn).sum(-1)).max() < 1e-10
+    nck = (k.shape[2] // 64) * 64
+    assert np.abs((dk[:, :, :nck] * k[:, :, :nck]).sum(-1)).max() < 1e-10
+    assert np.all(dk[:, :, nck:] == 0) and np.all(dv[:, :, nck:] == 0)   # partial chunk: no landmark
+    B, Lq, Hkv, K = idx.shape
+    G = q_attn.shape[2] // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            used = (idx[b, :, g] >= 0).any(-1)
+            want = dout[b, used][:, g * G:(g + 1) * G].astype(np.float64).sum((0, 1))
+            assert np.allclose(dv[b, g].sum(0), want, atol=1e-10)
+            assert np.abs(dlm[b, g].sum(0)).max() < 1e-10
+    # rows with no used slot get no gradient
+    empty = ~(idx >= 0).any(-1)
+    assert np.all(dq_ret[empty] == 0)
