@@ -252,6 +252,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_seg_fix_kernel(ChunkArgs a
         a.offsets[i] = pb + lp[u];
         a.cursor[i] = pb + lp[u];
         a.counts[i] = 0u;                        // ready for the next call
+        if (a.item_start != nullptr) a.item_start[i] = ib + li[u];
         const uint32_t ni = (c[u] + kPairs - 1) / kPairs;
         for (uint32_t jb = 0; jb < ni; ++jb) a.items[ib + li[u] + jb] = (uint64_t)i | ((uint64_t)jb << 32);
       }
@@ -532,9 +533,8 @@ hipError_t launch_dg(const ChunkArgs& a, hipStream_t st, const Marks& mk) {
 int64_t chunk_pairs_per_item() { return kPairs; }
 int64_t chunk_band_rows() { return kBandRows; }
 
-hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk) {
+hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st) {
   hipError_t e;
-  if ((e = mk.rec(kStageBucket, 0, st)) != hipSuccess) return e;
   if ((e = launch_fill_u32(a.counts, a.n_bins, 0u, st)) != hipSuccess) return e;
   const bool lds = a.Nc <= kHistMax;
   const int64_t seg = a.K <= 1 ? 1 : (int64_t)1 << (32 - __builtin_clz((unsigned)a.K - 1));
@@ -555,7 +555,13 @@ hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st,
   }
   if (lds) hipLaunchKernelGGL(chunk_scatter_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
   else hipLaunchKernelGGL(chunk_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk) {
+  hipError_t e;
+  if ((e = mk.rec(kStageBucket, 0, st)) != hipSuccess) return e;
+  if ((e = launch_bucket(a, st)) != hipSuccess) return e;
   if ((e = mk.rec(kStageBucket, 1, st)) != hipSuccess) return e;
 #define HSA_CHUNK_CASE(DD, GG) \
   if (D == DD && G == GG) return launch_dg<DD, GG>(a, st, mk);

@@ -246,6 +246,7 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
     c.items = reinterpret_cast<uint64_t*>(w + p.off_citems);
     c.n_items = reinterpret_cast<uint32_t*>(w + p.off_cnitems);
     c.seg_tot = reinterpret_cast<uint32_t*>(w + p.off_cseg);
+    c.item_start = nullptr;
     c.pairs = reinterpret_cast<uint32_t*>(w + p.off_cpairs);
     c.wts = reinterpret_cast<float*>(w + p.off_cwts);
     c.partials = reinterpret_cast<__half*>(w + p.off_cparts);

@@ -99,6 +99,7 @@ struct ChunkArgs {
   uint64_t* items;        // [max_items]   bin | block << 32
   uint32_t* n_items;      // number of valid items
   uint32_t* seg_tot;      // [2 * n_bins / Nc] pairs and items per segment of Nc bins
+  uint32_t* item_start;   // [n_bins] first work item of each bin, or nullptr
   uint32_t* pairs;        // [rows * K]    pair ids (row * K + slot), grouped by bin
   float* wts;             // [rows * K]    blend weights
   __half* partials;       // [rows * K, G, D] weighted per-chunk outputs
@@ -144,6 +145,8 @@ hipError_t launch_merge_lists(const MergeArgs& a, hipStream_t st);
 hipError_t launch_attend_decode(const DecodeArgs& a, int64_t rows, int D, int G, hipStream_t st);
 int decode_slots_per_block();
 hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk);
+// Pair bucketing alone: weights, bin counts and offsets, work items, pair ids.
+hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st);
 int64_t chunk_pairs_per_item();
 int64_t chunk_band_rows();
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
