@@ -43,7 +43,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 VALU_FP32_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 FLOP (FMA) x 2.4 GHz, non-packed
 
-WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "global_32K": 1}
+WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "global_32K": 1, "backward_32K": 1}
 # global_32K: the 32K training-window prefill with a top-K covering all 512
 # chunks (global HSA of the warm-up stage); the dense fused kernel runs it
 OVERRIDES = {"global_32K": dict(top_k=512, name="global_hsa_32K_gqa8")}
@@ -54,6 +54,9 @@ KERNELS = {
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
     ("decode_16M", "landmarks"): "chunk_landmark_kernel<true, 128>",
     ("global_32K", "attend"): "attend_global_kernel<128, 8>",
+    ("backward_32K", "bucket"): "chunk_count/scan/scatter + bin_sort kernels",
+    ("backward_32K", "attend"): "bwd_item_kernel<128, 8>",
+    ("backward_32K", "combine"): "bwd_row/bwd_chunk/bwd_landmark kernels",
     ("prefill_128K", "scan"): "scan_block_kernel<128>",
     ("prefill_128K", "bucket"): "chunk_count/scan/scatter kernels",
     ("prefill_128K", "attend"): "chunk_attend_kernel<128, 8>",
@@ -187,7 +190,8 @@ def algorithmic(cfg, U, elem=2):
     return dict(candidates=cand, selections=sel, landmark_bytes=lm_bytes, q_ret_bytes=q_ret,
                 q_attn_bytes=qa, out_bytes=qa, kv_bytes=U * 2 * 64 * d * elem,
                 bytes=lm_bytes + q_ret + 2 * qa + U * 2 * 64 * d * elem,
-                scan_flops=2 * d * cand, attend_flops=4 * cfg.group * 64 * d * sel)
+                scan_flops=2 * d * cand, attend_flops=4 * cfg.group * 64 * d * sel,
+                bwd_flops=10 * cfg.group * 64 * d * sel)
 
 
 def source_digest() -> str:
@@ -228,7 +232,13 @@ def roofline(workload, stage, ms, alg):
     over its measured duration."""
     kernel = KERNELS.get((workload, stage), stage)
     prefill = workload.startswith("prefill") or workload.startswith("global")
-    if stage == "attend" and workload.startswith("global"):
+    if stage == "attend" and workload.startswith("backward"):
+        units = ("mfma", alg["bwd_flops"], "10*G*64*d FLOP per selection x %d selections "
+                 "(S, dP, dq, dV, dk products)" % alg["selections"])
+    elif stage == "combine" and workload.startswith("backward"):
+        units = ("hbm", alg["bwd_combine_bytes"], "per-pair dq partials (G*d*4 B) + per-item dV, dk "
+                 "partials (2*64*d*4 B) read, fp32 gradients written")
+    elif stage == "attend" and workload.startswith("global"):
         units = ("mfma", alg["attend_flops"] + alg["scan_flops"],
                  "4*G*64*d FLOP per (row, eligible chunk) x %d + 2*d per retrieval score x %d"
                  % (alg["selections"], alg["candidates"]))
@@ -253,6 +263,92 @@ def roofline(workload, stage, ms, alg):
                 kernel_ms=ms, algorithmic_per_launch=amount, algorithmic_units=how)
 
 
+def bench_backward(name, cfg, steps, warmup, timer, cpu_baseline):
+    """One step = hsa_backward over the whole batch for the forward's selection."""
+    import torch
+    import ultra_long_context_amd as hsa
+    import workloads as W
+
+    t = time.perf_counter()
+    inp = W.generate(cfg)
+    dout_np = W.cotangent(cfg)
+    log("[bench] %s: inputs generated in %.1fs" % (name, time.perf_counter() - t))
+    q_ret, lm, q_attn, k, v = [to_dev(a, cfg.dtype) for a in (inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v)]
+    dout = to_dev(dout_np, cfg.dtype)
+    _, idx, sc = hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=cfg.q_pos0, top_k=cfg.top_k, return_topk=True)
+    f = dict(dtype=torch.float32, device="cuda:0")
+    grads = tuple(torch.empty(t_.shape, **f) for t_ in (q_ret, lm, q_attn, k, v))
+
+    def step():
+        hsa.backward(q_ret, lm, q_attn, k, v, idx, sc, dout, out=grads)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    eager = [g.clone() for g in grads]
+    g_step = timer.capture(step)
+    g_step.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(grads, eager)):
+        raise RuntimeError("graph replay differs from the eager backward")
+    log("[bench] %s: warmup done, graph replay matches eager bit for bit" % name)
+    ms_mean, ms_med, wall_ms = timer.time(g_step, steps)
+    log("[bench] %s: %.4f ms/step (median %.4f, wall incl. flush %.3f)" % (name, ms_mean, ms_med, wall_ms))
+    warm_mean, _, _ = timer.time(g_step, steps, flush=False)
+    stage_ms = timer.stages(lambda evs: hsa.backward(q_ret, lm, q_attn, k, v, idx, sc, dout, out=grads,
+                                                     stage_events=evs), steps)
+    log("[bench] %s: kernel stages (ms) %s" % (name, json.dumps(stage_ms)))
+    U = distinct_chunks(idx, cfg)
+    alg = algorithmic(cfg, U)
+    n_pairs = int((idx >= 0).sum().item())
+    items = n_pairs // 64 + U          # upper bound on work items: one partial block per used bin
+    d, G = cfg.head_dim, cfg.group
+    alg["bwd_combine_bytes"] = (n_pairs * G * d * 4 + items * 2 * 64 * d * 4
+                                + 4 * (q_ret.numel() + lm.numel() + q_attn.numel() + k.numel() + v.numel()))
+    # compulsory bytes: bf16 inputs (selected chunks' K/V once), the selection,
+    # fp32 gradients written once
+    grads_bytes = 4 * sum(g.numel() for g in grads)
+    alg["bwd_bytes"] = (alg["q_ret_bytes"] + alg["landmark_bytes"] + 2 * alg["q_attn_bytes"] + alg["kv_bytes"]
+                        + idx.numel() * 8 + grads_bytes)
+    qtok = cfg.batch * cfg.q_len
+    res = dict(workload=name, config=cfg, value=qtok / (ms_mean / 1e3), ms_per_step=ms_mean,
+               ms_median=ms_med, wall_ms_per_step=wall_ms, warm_ms_per_step=warm_mean,
+               stage_ms=stage_ms, alg=alg, U=U)
+    dom = max(stage_ms, key=stage_ms.get)
+    res["roofline"] = roofline(name, dom, stage_ms[dom], alg)
+    res["hbm_frac_whole_step"] = (alg["bwd_bytes"] / 8e12) / (ms_mean / 1e3)
+    if cpu_baseline:
+        res["cpu_baseline"] = oracle_backward_baseline(cfg, inp, dout_np, idx.cpu().numpy(), sc.cpu().numpy())
+    del q_ret, lm, q_attn, k, v, dout, grads, eager, inp
+    torch.cuda.empty_cache()
+    return res
+
+
+def oracle_backward_baseline(cfg, inp, dout, idx, sc, budget_s=15.0):
+    """fp64 oracle backward on every s-th query row (with the whole K/V history)."""
+    import oracle
+    total = cfg.batch * cfg.q_len
+
+    def run(rows):
+        r = np.asarray(rows)
+        t = time.perf_counter()
+        oracle.backward(inp.q_ret[:, r], inp.landmarks, inp.q_attn[:, r], inp.k, inp.v, dout[:, r],
+                        idx[:, r], sc[:, r], qk_norm=cfg.qk_norm)
+        return time.perf_counter() - t
+
+    probe = np.linspace(0, cfg.q_len - 1, num=min(cfg.q_len, 64), dtype=np.int64)
+    per_row = run(probe) / len(probe)
+    n = int(max(64, min(cfg.q_len, budget_s / max(per_row, 1e-9))))
+    stride = max(1, cfg.q_len // n)
+    rows = np.arange(0, cfg.q_len, stride, dtype=np.int64)
+    dt = run(rows)
+    threads = min(oracle.max_threads(), cfg.batch * cfg.n_kv_heads)   # parallel over (batch, kv head)
+    log("[bench] oracle backward: %d rows in %.1fs on %d threads" % (len(rows), dt, threads))
+    return dict(value=cfg.batch * len(rows) / dt, unit="query-tokens/s", cores=threads, kind="oracle",
+                sample="%d of %d query rows (every %d-th row of each sequence, all heads), %.1f s" % (
+                    cfg.batch * len(rows), total, stride, dt))
+
+
 def bench_workload(name, steps, warmup, timer, cpu_baseline):
     import torch
     import ultra_long_context_amd as hsa
@@ -260,6 +356,8 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
 
     from dataclasses import replace as dc_replace
     cfg = dc_replace(W.CONFIGS[WORKLOADS[name]], **OVERRIDES.get(name, {}))
+    if name.startswith("backward"):
+        return bench_backward(name, cfg, steps, warmup, timer, cpu_baseline)
     t = time.perf_counter()
     inp = W.generate(cfg)
     log("[bench] %s: inputs generated in %.1fs" % (name, time.perf_counter() - t))
@@ -416,7 +514,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workloads", default="prefill_128K,decode_16M,global_32K")
+    ap.add_argument("--workloads", default="prefill_128K,decode_16M,global_32K,backward_32K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the 1 GiB calibration copy first (for counter passes)")
@@ -450,7 +548,7 @@ def main():
     timer = Timer()
     names = [w for w in args.workloads.split(",") if w]
     results = {}
-    for name in ["decode_16M", "global_32K", "prefill_128K"]:
+    for name in ["decode_16M", "global_32K", "backward_32K", "prefill_128K"]:
         if name in names:
             results[name] = bench_workload(name, args.steps, args.warmup, timer,
                                            not args.no_cpu_baseline)

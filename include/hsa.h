@@ -127,6 +127,34 @@ hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret, const void
                          int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Backward of Steps 2-4 for a given selection: the gradients of
+ * sum(out * dout) with respect to q_ret, landmarks, q_attn, k and v, where out
+ * is what hsa_chunk_attend_blend computes from the same selection.  The
+ * selection (Step 2's top-K) is piecewise constant and carries no gradient;
+ * the gradient reaches q_ret and the landmarks through the softmax blend
+ * weights of the retrieval scores (Steps 2 and 4 of "How It Works
+ * (Technically)"), and q_attn, k, v through each chunk's softmax attention
+ * (Step 3), including the query-key L2 normalisation when the flag is set
+ * (gradient of x / max(|x|, 1e-6)).
+ * bf16 inputs only (HSA_ERR_UNSUPPORTED otherwise), top_k <= 64.
+ *   topk_idx, topk_score [B, Lq, Hkv, top_k] as for hsa_chunk_attend_blend
+ *                (slots outside [0, Nc) are unused).
+ *   dout         [B, Lq, Hq, d] bf16.
+ *   dq_ret       [B, Lq, Hkv, d] fp32, written.
+ *   dlandmarks   [B, Hkv, Nc, d] fp32, written (zero for unselected chunks).
+ *   dq_attn      [B, Lq, Hq, d] fp32, written (zero for rows with no used slot).
+ *   dk, dv       [B, Hkv, kv_len, d] fp32, written (zero for unselected chunks
+ *                and the trailing partial chunk).
+ * Every sum runs in a fixed order, so results repeat bit for bit.  Pointers
+ * 16-byte aligned, workspace 256-byte aligned and at least
+ * hsa_backward_workspace_size() bytes; asynchronous on `stream`. */
+hsa_status_t hsa_backward_workspace_size(const hsa_shape_t* shape, size_t* bytes);
+hsa_status_t hsa_backward(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                          const void* q_attn, const void* k, const void* v,
+                          const int32_t* topk_idx, const float* topk_score, const void* dout,
+                          float* dq_ret, float* dlandmarks, float* dq_attn, float* dk, float* dv,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Landmarks of chunks [chunk_begin, chunk_end) of every (batch, kv head): the
  * mean of each chunk's 64 keys, accumulated in fp32 and stored in the shape's
  * dtype (bf16: round to nearest even).  Step 1 of "How It Works (Technically)"
@@ -167,6 +195,17 @@ hsa_status_t hsa_forward_profiled(const hsa_shape_t* shape, const void* q_ret,
                                   const void* v, void* out, int32_t* topk_idx, float* topk_score,
                                   void* ws, size_t ws_bytes, void* stream,
                                   void* const* stage_events);
+
+/* hsa_backward with stage events as for hsa_forward_profiled: BUCKET = pair
+ * bucketing and the per-bin sort, ATTEND = the per-item MFMA kernel,
+ * COMBINE = the per-row, per-chunk and per-landmark reductions (SCAN and MERGE
+ * record nothing).  Outputs are those of hsa_backward. */
+hsa_status_t hsa_backward_profiled(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                                   const void* q_attn, const void* k, const void* v,
+                                   const int32_t* topk_idx, const float* topk_score,
+                                   const void* dout, float* dq_ret, float* dlandmarks,
+                                   float* dq_attn, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                   void* stream, void* const* stage_events);
 
 /* Static description of a status code. */
 const char* hsa_status_string(hsa_status_t status);

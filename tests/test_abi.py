@@ -188,3 +188,37 @@ def test_global_top_k_planning():
                                       bufs[3].ptr, bufs[3].ptr, bufs[0].ptr, bufs[1].ptr, 1 << 20,
                                       None) == 3
     assert call_forward(shp, idx="both") == 3
+
+
+def test_backward_checks_arguments():
+    lib = h.load_library()
+    n = ctypes.c_size_t(0)
+    bsize = lambda s: (lib.hsa_backward_workspace_size(ctypes.byref(s), ctypes.byref(n)), n.value)
+    st, need = bsize(base())
+    assert st == 0 and need > 0 and need % 256 == 0
+    assert bsize(base(dtype=h.DTYPE_F32))[0] == 3                     # bf16 only
+    assert bsize(base(top_k=65))[0] == 3                              # no global-HSA backward
+    assert bsize(base(head_dim=96))[0] == 3
+    assert lib.hsa_backward_workspace_size(ctypes.byref(base()), None) == 1
+    # larger problems need more workspace (per-pair and per-item buffers)
+    assert bsize(base(q_len=4096, kv_len=8192, q_pos0=4096))[1] > need
+
+    s = base()
+    bufs = [FakeBuf() for _ in range(13)]
+    ws = FakeBuf()
+
+    def call(ptrs=None, ws_ptr=None, ws_bytes=None):
+        p = [b.ptr for b in bufs] if ptrs is None else ptrs
+        return lib.hsa_backward(ctypes.byref(s), *p, ws.ptr if ws_ptr is None else ws_ptr,
+                                need if ws_bytes is None else ws_bytes, None)
+
+    for i in range(13):                                               # every pointer is required
+        p = [b.ptr for b in bufs]
+        p[i] = ctypes.c_void_p(0)
+        assert call(p) == 1, i
+    p = [b.ptr for b in bufs]
+    p[8] = ctypes.c_void_p(p[8].value + 4)                             # dout misaligned
+    assert call(p) == 6
+    assert call(ws_ptr=ctypes.c_void_p(ws.ptr.value + 64)) == 6
+    assert call(ws_bytes=need - 256) == 4
+    assert lib.hsa_backward(None, *[b.ptr for b in bufs], ws.ptr, need, None) == 1

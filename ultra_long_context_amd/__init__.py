@@ -18,7 +18,7 @@ import os
 import threading
 
 __all__ = ["HsaError", "HsaShape", "forward", "retrieve_topk", "chunk_attend_blend", "chunk_landmarks",
-           "workspace_size", "new_workspace", "library_path", "load_library", "EXPORTED_SYMBOLS"]
+           "backward", "backward_workspace_size", "workspace_size", "new_workspace", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhsa.so")
@@ -32,7 +32,8 @@ MAX_TOP_K = 64
 
 EXPORTED_SYMBOLS = ("hsa_workspace_size", "hsa_workspace_init", "hsa_retrieve_topk",
                     "hsa_chunk_attend_blend", "hsa_forward", "hsa_forward_profiled",
-                    "hsa_chunk_landmarks",
+                    "hsa_chunk_landmarks", "hsa_backward_workspace_size", "hsa_backward",
+                    "hsa_backward_profiled",
                     "hsa_status_string", "hsa_version")
 
 # kernel stages (hsa_stage_t)
@@ -95,6 +96,12 @@ def _load():
             lib.hsa_forward_profiled.restype = st
             lib.hsa_chunk_landmarks.argtypes = [shp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
             lib.hsa_chunk_landmarks.restype = st
+            lib.hsa_backward_workspace_size.argtypes = [shp, ctypes.POINTER(sz)]
+            lib.hsa_backward_workspace_size.restype = st
+            lib.hsa_backward.argtypes = [shp] + [vp] * 13 + [vp, sz, vp]
+            lib.hsa_backward.restype = st
+            lib.hsa_backward_profiled.argtypes = [shp] + [vp] * 13 + [vp, sz, vp, ctypes.POINTER(vp)]
+            lib.hsa_backward_profiled.restype = st
             lib.hsa_status_string.argtypes = [st]
             lib.hsa_status_string.restype = ctypes.c_char_p
             lib.hsa_version.restype = ctypes.c_int32
@@ -116,6 +123,14 @@ def workspace_size(shape: HsaShape) -> int:
     st = _load().hsa_workspace_size(ctypes.byref(shape), ctypes.byref(n))
     if st:
         raise HsaError(st, "hsa_workspace_size")
+    return int(n.value)
+
+
+def backward_workspace_size(shape: HsaShape) -> int:
+    n = ctypes.c_size_t(0)
+    st = _load().hsa_backward_workspace_size(ctypes.byref(shape), ctypes.byref(n))
+    if st:
+        raise HsaError(st, "hsa_backward_workspace_size")
     return int(n.value)
 
 
@@ -188,6 +203,15 @@ def _event_handle(ev) -> int:
     return ev.cuda_event
 
 
+def _stage_array(stage_events):
+    evs = (ctypes.c_void_p * (2 * len(STAGES)))()
+    for name, (e0, e1) in stage_events.items():
+        s = STAGES.index(name)
+        evs[2 * s] = _event_handle(e0)
+        evs[2 * s + 1] = _event_handle(e1)
+    return evs
+
+
 def forward(q_ret, landmarks, q_attn, k, v, *, q_pos0: int, top_k: int, qk_norm: bool = True,
             ret_scale: float | None = None, attn_scale: float | None = None,
             return_topk: bool = False, out=None, workspace=None, stage_events=None):
@@ -231,12 +255,7 @@ def forward(q_ret, landmarks, q_attn, k, v, *, q_pos0: int, top_k: int, qk_norm:
         if st:
             raise HsaError(st, "hsa_forward")
     else:
-        evs = (ctypes.c_void_p * (2 * len(STAGES)))()
-        for name, (e0, e1) in stage_events.items():
-            s = STAGES.index(name)
-            evs[2 * s] = _event_handle(e0)
-            evs[2 * s + 1] = _event_handle(e1)
-        st = _load().hsa_forward_profiled(*args, evs)
+        st = _load().hsa_forward_profiled(*args, _stage_array(stage_events))
         if st:
             raise HsaError(st, "hsa_forward_profiled")
     return (out, idx, score) if return_topk else out
@@ -329,4 +348,65 @@ def chunk_landmarks(k, *, chunk_begin: int = 0, chunk_end: int | None = None, ou
                                      _stream(k.device))
     if st:
         raise HsaError(st, "hsa_chunk_landmarks")
+    return out
+
+
+_bwd_ws_cache = {}
+
+
+def backward(q_ret, landmarks, q_attn, k, v, topk_idx, topk_score, dout, *, qk_norm: bool = True,
+             ret_scale: float | None = None, attn_scale: float | None = None, out=None,
+             workspace=None, stage_events=None):
+    """Gradients of sum(out * dout) for the HSA output computed from the given
+    selection (Steps 2-4; the selection itself carries no gradient).
+
+    Inputs as for forward / chunk_attend_blend (bf16), dout [B, Lq, Hq, d] bf16.
+    Returns (dq_ret, dlandmarks, dq_attn, dk, dv), fp32, shaped like their
+    inputs; `out` may supply them.  workspace: a uint8 GPU tensor of at least
+    backward_workspace_size() bytes (cached per device if None).  stage_events:
+    as for forward (stages "bucket", "attend", "combine"; hsa_backward_profiled).
+    """
+    torch = _torch()
+    for t, n in ((q_ret, "q_ret"), (landmarks, "landmarks"), (q_attn, "q_attn"), (k, "k"), (v, "v"),
+                 (dout, "dout")):
+        _check(t, n, 4, torch.bfloat16)
+    _check(topk_idx, "topk_idx", 4, torch.int32)
+    _check(topk_score, "topk_score", 4, torch.float32)
+    B, Lq, Hkv, d = q_ret.shape
+    Hq, Lkv, K = q_attn.shape[2], k.shape[2], topk_idx.shape[3]
+    if (tuple(landmarks.shape) != (B, Hkv, Lkv // CHUNK, d) or tuple(q_attn.shape) != (B, Lq, Hq, d)
+            or tuple(k.shape) != (B, Hkv, Lkv, d) or v.shape != k.shape or dout.shape != q_attn.shape
+            or tuple(topk_idx.shape) != (B, Lq, Hkv, K) or topk_score.shape != topk_idx.shape):
+        raise ValueError("inconsistent HSA backward shapes")
+    shape = make_shape(batch=B, q_len=Lq, kv_len=Lkv, q_pos0=0, n_q_heads=Hq, n_kv_heads=Hkv,
+                       head_dim=d, top_k=K, dtype=DTYPE_BF16, qk_norm=qk_norm, ret_scale=ret_scale,
+                       attn_scale=attn_scale)
+    dev = q_ret.device
+    need = backward_workspace_size(shape)
+    if workspace is None:
+        key = dev.index if dev.index is not None else torch.cuda.current_device()
+        workspace = _bwd_ws_cache.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            _bwd_ws_cache[key] = workspace
+    if out is None:
+        f = dict(dtype=torch.float32, device=dev)
+        out = (torch.empty(q_ret.shape, **f), torch.empty(landmarks.shape, **f),
+               torch.empty(q_attn.shape, **f), torch.empty(k.shape, **f), torch.empty(v.shape, **f))
+    names = ("dq_ret", "dlandmarks", "dq_attn", "dk", "dv")
+    for t, n, ref in zip(out, names, (q_ret, landmarks, q_attn, k, v)):
+        _check(t, n, 4, torch.float32)
+        if t.shape != ref.shape:
+            raise ValueError("%s must have shape %s" % (n, tuple(ref.shape)))
+    args = (ctypes.byref(shape), _ptr(q_ret), _ptr(landmarks), _ptr(q_attn), _ptr(k), _ptr(v),
+            _ptr(topk_idx), _ptr(topk_score), _ptr(dout), *[_ptr(t) for t in out], _ptr(workspace),
+            workspace.numel(), _stream(dev))
+    if stage_events is None:
+        st = _load().hsa_backward(*args)
+        if st:
+            raise HsaError(st, "hsa_backward")
+    else:
+        st = _load().hsa_backward_profiled(*args, _stage_array(stage_events))
+        if st:
+            raise HsaError(st, "hsa_backward_profiled")
     return out

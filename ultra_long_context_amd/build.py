@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhsa.so")
 SOURCES = ["hsa_api.hip", "retrieve.hip", "attend.hip", "attend_chunk.hip", "attend_decode.hip",
-           "landmarks.hip", "attend_global.hip"]
+           "landmarks.hip", "attend_global.hip", "backward.hip"]
 ARCH = os.environ.get("HSA_OFFLOAD_ARCH", "gfx950")
 
 

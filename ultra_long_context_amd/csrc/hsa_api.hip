@@ -1,5 +1,6 @@
 // hsa_api.hip -- C ABI of the HSA forward (see include/hsa.h): argument checks,
 // work planning, workspace layout and kernel launch order.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -403,6 +404,135 @@ HSA_EXPORT hsa_status_t hsa_chunk_landmarks(const hsa_shape_t* shape, const void
   return hsa::launch_chunk_landmarks(a, shape->dtype == HSA_DTYPE_BF16, shape->head_dim,
                                      static_cast<hipStream_t>(stream)) == hipSuccess
              ? HSA_OK : HSA_ERR_DEVICE;
+}
+
+namespace hsa {
+namespace {
+
+struct BwdPlan {
+  Plan p;
+  size_t off_counts, off_offsets, off_cursor, off_items, off_nitems, off_seg, off_istart, off_pairs,
+      off_wts, off_wdw, off_draw, off_dqp, off_itemp, total;
+};
+
+hsa_status_t make_bwd_plan(const hsa_shape_t* s, BwdPlan* b) {
+  hsa_status_t st = make_plan(s, &b->p, false);
+  if (st != HSA_OK) return st;
+  const Plan& p = b->p;
+  if (!p.bf16) return HSA_ERR_UNSUPPORTED;
+  const int64_t n_pairs = p.rows * p.K, n_bg = p.rows / p.Lq;
+  if (n_pairs >= INT32_MAX || p.n_bins + 1 >= INT32_MAX || p.max_items >= INT32_MAX ||
+      n_bg * (p.Nc + 1) >= INT32_MAX)
+    return HSA_ERR_BAD_SHAPE;
+  const size_t nb = (size_t)p.n_bins, np = (size_t)n_pairs, D = (size_t)p.D;
+  size_t off = 0;
+  b->off_counts = off; off = align_up(off + nb * 4, 256);
+  b->off_offsets = off; off = align_up(off + (nb + 1) * 4, 256);
+  b->off_cursor = off; off = align_up(off + nb * 4, 256);
+  b->off_items = off; off = align_up(off + (size_t)p.max_items * 8, 256);
+  b->off_nitems = off; off = align_up(off + 4, 256);
+  b->off_seg = off; off = align_up(off + (p.Nc > 0 ? nb / (size_t)p.Nc : 0) * 8, 256);
+  b->off_istart = off; off = align_up(off + nb * 4, 256);
+  b->off_pairs = off; off = align_up(off + np * 4, 256);
+  b->off_wts = off; off = align_up(off + np * 4, 256);
+  b->off_wdw = off; off = align_up(off + np * 4, 256);
+  b->off_draw = off; off = align_up(off + np * 4, 256);
+  b->off_dqp = off; off = align_up(off + np * p.G * D * 4, 256);
+  b->off_itemp = off; off = align_up(off + (size_t)p.max_items * 2 * HSA_CHUNK_TOKENS * D * 4, 256);
+  b->total = std::max<size_t>(off, 256);
+  return HSA_OK;
+}
+
+}  // namespace
+}  // namespace hsa
+
+HSA_EXPORT hsa_status_t hsa_backward_workspace_size(const hsa_shape_t* shape, size_t* bytes) {
+  if (!bytes) return HSA_ERR_NULL_POINTER;
+  hsa::BwdPlan b;
+  const hsa_status_t st = hsa::make_bwd_plan(shape, &b);
+  if (st != HSA_OK) return st;
+  *bytes = b.total;
+  return HSA_OK;
+}
+
+namespace hsa {
+namespace {
+
+hsa_status_t backward_impl(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                           const void* q_attn, const void* k, const void* v, const int32_t* topk_idx,
+                           const float* topk_score, const void* dout, float* dq_ret, float* dlandmarks,
+                           float* dq_attn, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream,
+                           const Marks& mk) {
+  hsa::BwdPlan b;
+  hsa_status_t st = hsa::make_bwd_plan(shape, &b);
+  if (st != HSA_OK) return st;
+  const Plan& p = b.p;
+  // empty tensors may come as NULL: stand in a pointer that is never read
+  const void* lm = p.Nc > 0 ? landmarks : q_ret;
+  const void* dlm = p.Nc > 0 ? static_cast<const void*>(dlandmarks) : dq_ret;
+  const void* kk = p.Lkv > 0 ? k : q_attn;
+  const void* vv = p.Lkv > 0 ? v : q_attn;
+  const void* dkk = p.Lkv > 0 ? static_cast<const void*>(dk) : dq_attn;
+  const void* dvv = p.Lkv > 0 ? static_cast<const void*>(dv) : dq_attn;
+  if ((st = hsa::check_ptrs({q_ret, lm, q_attn, kk, vv, topk_idx, topk_score, dout, dq_ret, dlm, dq_attn,
+                             dkk, dvv})) != HSA_OK)
+    return st;
+  if (!ws) return HSA_ERR_NULL_POINTER;
+  if (!hsa::aligned(ws, 256)) return HSA_ERR_MISALIGNED;
+  if (ws_bytes < b.total) return HSA_ERR_WORKSPACE_TOO_SMALL;
+  char* w = static_cast<char*>(ws);
+  hsa::BwdArgs a;
+  hsa::ChunkArgs& c = a.c;
+  c.q_attn = q_attn; c.k = kk; c.v = vv; c.idx = topk_idx; c.score = topk_score; c.out = nullptr;
+  c.counts = reinterpret_cast<uint32_t*>(w + b.off_counts);
+  c.offsets = reinterpret_cast<uint32_t*>(w + b.off_offsets);
+  c.cursor = reinterpret_cast<uint32_t*>(w + b.off_cursor);
+  c.items = reinterpret_cast<uint64_t*>(w + b.off_items);
+  c.n_items = reinterpret_cast<uint32_t*>(w + b.off_nitems);
+  c.seg_tot = reinterpret_cast<uint32_t*>(w + b.off_seg);
+  c.item_start = reinterpret_cast<uint32_t*>(w + b.off_istart);
+  c.pairs = reinterpret_cast<uint32_t*>(w + b.off_pairs);
+  c.wts = reinterpret_cast<float*>(w + b.off_wts);
+  c.partials = nullptr;
+  c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
+  c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
+  c.band_rows = hsa::chunk_band_rows(); c.n_bands = p.n_bands;
+  c.attn_scale = p.attn_scale; c.qk_norm = p.qk_norm ? 1 : 0;
+  a.q_ret = q_ret; a.landmarks = lm; a.dout = dout;
+  a.dq_ret = dq_ret; a.dlandmarks = dlandmarks; a.dq_attn = dq_attn; a.dk = dk; a.dv = dv;
+  a.wdw = reinterpret_cast<float*>(w + b.off_wdw);
+  a.draw = reinterpret_cast<float*>(w + b.off_draw);
+  a.dq_part = reinterpret_cast<float*>(w + b.off_dqp);
+  a.item_part = reinterpret_cast<float*>(w + b.off_itemp);
+  a.ret_scale = p.ret_scale;
+  return hsa::launch_backward(a, p.D, p.G, static_cast<hipStream_t>(stream), mk) == hipSuccess
+             ? HSA_OK : HSA_ERR_DEVICE;
+}
+
+}  // namespace
+}  // namespace hsa
+
+HSA_EXPORT hsa_status_t hsa_backward(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                                     const void* q_attn, const void* k, const void* v,
+                                     const int32_t* topk_idx, const float* topk_score,
+                                     const void* dout, float* dq_ret, float* dlandmarks,
+                                     float* dq_attn, float* dk, float* dv, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return hsa::backward_impl(shape, q_ret, landmarks, q_attn, k, v, topk_idx, topk_score, dout, dq_ret,
+                            dlandmarks, dq_attn, dk, dv, ws, ws_bytes, stream, hsa::Marks{});
+}
+
+HSA_EXPORT hsa_status_t hsa_backward_profiled(const hsa_shape_t* shape, const void* q_ret,
+                                              const void* landmarks, const void* q_attn, const void* k,
+                                              const void* v, const int32_t* topk_idx,
+                                              const float* topk_score, const void* dout, float* dq_ret,
+                                              float* dlandmarks, float* dq_attn, float* dk, float* dv,
+                                              void* ws, size_t ws_bytes, void* stream,
+                                              void* const* stage_events) {
+  hsa::Marks mk;
+  mk.ev = stage_events;
+  return hsa::backward_impl(shape, q_ret, landmarks, q_attn, k, v, topk_idx, topk_score, dout, dq_ret,
+                            dlandmarks, dq_attn, dk, dv, ws, ws_bytes, stream, mk);
 }
 
 HSA_EXPORT const char* hsa_status_string(hsa_status_t status) {

@@ -110,6 +110,28 @@ struct ChunkArgs {
   int32_t qk_norm;
 };
 
+// Backward for a given selection (bf16 inputs, fp32 gradients).  The pair
+// bucketing of the chunk-major forward is reused through `c` (item_start set).
+struct BwdArgs {
+  ChunkArgs c;
+  const void* q_ret;      // [B, Lq, Hkv, D]
+  const void* landmarks;  // [B, Hkv, Nc, D]
+  const void* dout;       // [B, Lq, Hq, D]
+  float* dq_ret;          // [B, Lq, Hkv, D]
+  float* dlandmarks;      // [B, Hkv, Nc, D]
+  float* dq_attn;         // [B, Lq, Hq, D]
+  float* dk;              // [B, Hkv, Lkv, D]
+  float* dv;              // [B, Hkv, Lkv, D]
+  float* wdw;             // [rows * K]   w_k * dL/dw_k per pair
+  float* draw;            // [rows * K]   dL/d(q_ret . landmark) per pair
+  float* dq_part;         // [rows * K, G, D]  per-pair gradient of the normalised query
+  float* item_part;       // [max_items, 2, 64, D]  per-item dV and dkhat of the chunk's keys
+  float ret_scale;
+};
+
+hipError_t launch_backward(const BwdArgs& a, int D, int G, hipStream_t st, const Marks& mk);
+int64_t bwd_pairs_per_item();
+
 // Chunk-mean landmarks of chunks [c_begin, c_begin + n_chunks) of every (b, kv head).
 struct LandmarkArgs {
   const void* k;          // [B, Hkv, Lkv, D]

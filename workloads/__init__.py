@@ -40,7 +40,7 @@ CHUNK = 64
 BLOCK_TOKENS = 65536
 BLOCK_ELEMS = 1 << 23
 
-T_QRET, T_QATTN, T_K, T_V, T_NOISE, T_NEEDLE = range(6)
+T_QRET, T_QATTN, T_K, T_V, T_NOISE, T_NEEDLE, T_DOUT = range(7)
 
 
 @dataclass(frozen=True)
@@ -246,6 +246,14 @@ def generate(cfg: HsaConfig, seed: int | None = None, mode: str = "normal") -> H
     else:
         raise ValueError(mode)
     return HsaInputs(cfg, q_ret, landmarks, q_attn, k, v, needles)
+
+
+def cotangent(cfg: HsaConfig, seed: int | None = None) -> np.ndarray:
+    """Output cotangent dout [B, Lq, Hq, d] for the backward: stored N(0,1) values
+    drawn like q_attn from their own stream."""
+    seed = cfg.seed if seed is None else seed
+    B, Lq, Hq, d = cfg.batch, cfg.q_len, cfg.n_q_heads, cfg.head_dim
+    return _normal_rows(seed, T_DOUT, B * Lq, Hq * d, cfg.dtype).reshape(B, Lq, Hq, d)
 
 
 def _plant_needles(cfg: HsaConfig, seed: int, q_ret_store: np.ndarray, lm: np.ndarray) -> list:
