@@ -13,14 +13,15 @@
 //            norms in LDS; per 16-head-row tile (one wave): S^T = K Q^T and
 //            dP^T = V dO_w^T on MFMA (dO_w = w dout), P, w dw = sum P dP,
 //            dz = P (dP - sum P dP); dqhat^T = K^T g^T (g = attn dz / |k|)
-//            written per pair; P^T, h^T (h = attn dz / |q|), dO_w^T and q^T
-//            staged in LDS, then each wave accumulates 16 keys of
+//            stored per pair in bf16; P^T, h^T (h = attn dz / |q|), dO_w^T and
+//            q^T staged in LDS, then each wave accumulates 16 keys of
 //            dV = P^T dO_w and dkhat = h^T q over the item's head-rows.
+//   slot     per (row, slot): ds = w dw - w sum(w dw), times ret_scale.
+//   dq       per (row, head): dq = normalisation's gradient of the summed
+//            dqhat; per row: dq_ret = sum over slots of ds landmark.
 //   chunk    per chunk: the items' dV and dkhat summed in order; dk is the
 //            normalisation's gradient of dkhat.
-//   row      per row: dq = normalisation's gradient of the summed dqhat;
-//            ds = w dw - w sum(w dw); dq_ret = ret_scale sum ds landmark.
-//   lm       per chunk: dlandmark = ret_scale sum over its pairs ds q_ret.
+//   landmark per chunk: dlandmark = sum over its pairs of ds q_ret.
 #include "hsa_device.h"
 #include "hsa_internal.h"
 
@@ -38,6 +39,17 @@ __global__ __launch_bounds__(256) void bin_sort_kernel(BwdArgs a) {
   const int64_t bin = blockIdx.x;
   const uint32_t o0 = a.c.offsets[bin], n = a.c.offsets[bin + 1] - o0;
   if (n <= 1 || n > kSortCap) return;       // larger bins keep their order (not expected)
+  if (n <= 256) {                           // rank sort: pair ids in a bin are distinct
+    const uint32_t x = threadIdx.x < n ? a.c.pairs[o0 + threadIdx.x] : 0xFFFFFFFFu;
+    v[threadIdx.x] = x;
+    __syncthreads();
+    if (threadIdx.x < n) {
+      uint32_t r = 0;
+      for (uint32_t j = 0; j < n; ++j) r += v[j] < x;
+      a.c.pairs[o0 + r] = x;
+    }
+    return;
+  }
   int np = 1;
   while (np < (int)n) np <<= 1;
   for (int i = threadIdx.x; i < np; i += 256) v[i] = i < (int)n ? a.c.pairs[o0 + i] : 0xFFFFFFFFu;
@@ -149,21 +161,31 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
   }
   const float as = c.attn_scale;
   const int n_tiles = (n_pairs + PT - 1) / PT;
+  // q and dout rows of this wave's tile (16 head-rows), loaded one tile ahead
+  uint4 xr[KSTEP], yr[KSTEP];
+  auto tile_off = [&](int tile) -> int64_t {
+    const int pm = tile * PT + ma / G;
+    return tile < n_tiles && pm < n_pairs ? qoff_s[pm] + (int64_t)(ma % G) * D : 0;
+  };
+  {
+    const int64_t off = tile_off(w);
+#pragma unroll
+    for (int t = 0; t < KSTEP; ++t) {
+      xr[t] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(c.q_attn) + off + 8 * jg + 32 * t);
+      yr[t] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.dout) + off + 8 * jg + 32 * t);
+    }
+  }
   for (int t0 = 0; t0 < n_tiles; t0 += 4) {
     // ---- phase A: this wave's tile of 16 head-rows -------------------------
     const int tile = t0 + w;
     const int pm = tile * PT + ma / G, hd = ma % G;
     const bool live = tile < n_tiles && pm < n_pairs;
-    const int64_t off = live ? qoff_s[pm] + (int64_t)hd * D : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(c.q_attn) + off + 8 * jg;
-    const uint16_t* op = reinterpret_cast<const uint16_t*>(a.dout) + off + 8 * jg;
     const float wp = live ? w_s[pm] : 0.f;
     bf16x8 qa[KSTEP], da[KSTEP];
     float qss = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) {
-      uint4 x = *reinterpret_cast<const uint4*>(qp + 32 * t);
-      uint4 y = *reinterpret_cast<const uint4*>(op + 32 * t);
+      uint4 x = xr[t], y = yr[t];
       if (!live) x = y = make_uint4(0, 0, 0, 0);
       qa[t] = __builtin_bit_cast(bf16x8, x);
       const uint32_t qw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
@@ -184,6 +206,14 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) {
         qt[(32 * t + 8 * jg + e) * HROW + 16 * w + ma] = qe[e];
         dt[(32 * t + 8 * jg + e) * HROW + 16 * w + ma] = de[e];
+      }
+    }
+    if (t0 + 4 < n_tiles) {   // next tile's rows, in flight during this one
+      const int64_t off = tile_off(t0 + 4 + w);
+#pragma unroll
+      for (int t = 0; t < KSTEP; ++t) {
+        xr[t] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(c.q_attn) + off + 8 * jg + 32 * t);
+        yr[t] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.dout) + off + 8 * jg + 32 * t);
       }
     }
     qss += __shfl_xor(qss, 16, kWave);
@@ -260,7 +290,7 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
         gb[nt >> 1][4 * (nt & 1) + i] = (__bf16)(dz * rkl[nt][i]);
       }
     // dqhat^T = K^T g^T: lane holds dims 16*nt + 4*jg + i of head-row ma
-    float* dq = a.dq_part + (live ? ((int64_t)pid_s[pm] * G + hd) * D : 0) + 4 * jg;
+    uint16_t* dq = a.dq_part + (live ? ((int64_t)pid_s[pm] * G + hd) * D : 0) + 4 * jg;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       floatx4 o = {0.f, 0.f, 0.f, 0.f};
@@ -269,7 +299,11 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
         const uint4 ka = *reinterpret_cast<const uint4*>(&kt[(16 * nt + ma) * TROW + 32 * st + 8 * jg]);
         o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), gb[st], o, 0, 0, 0);
       }
-      if (live) *reinterpret_cast<float4*>(dq + 16 * nt) = make_float4(o[0], o[1], o[2], o[3]);
+      if (live) {
+        const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
+        *reinterpret_cast<uint2*>(dq + 16 * nt) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      }
       if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
@@ -305,153 +339,229 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
 }
 
 // --- per chunk: dV, dK --------------------------------------------------------
-// One workgroup per (batch, kv head, chunk); thread t owns key t / 4 and 32
-// dims.  Chunk index Nc stands for the trailing partial chunk (zero).
+// A key's D / 4 threads each own 4 dims; a workgroup takes 256 / (D / 4) keys
+// of one chunk and sums the items of the chunk's bins (band by band, item by
+// item) for them.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   const ChunkArgs& c = a.c;
-  constexpr int DPT = D / 4;                 // dims per thread
-  const int64_t bg = blockIdx.x / (c.Nc + 1), chunk = blockIdx.x % (c.Nc + 1);
-  const int tid = threadIdx.x, key = tid >> 2, d0 = (tid & 3) * DPT;
-  if (chunk == c.Nc) {                       // tail tokens without a landmark
-    for (int64_t t = c.Nc * kChunk + key; t < c.Lkv; t += 64)
-      for (int x = 0; x < DPT; ++x) {
-        a.dk[(bg * c.Lkv + t) * D + d0 + x] = 0.f;
-        a.dv[(bg * c.Lkv + t) * D + d0 + x] = 0.f;
-      }
-    return;
-  }
-  float sv[DPT], sk[DPT];
-#pragma unroll
-  for (int x = 0; x < DPT; ++x) sv[x] = sk[x] = 0.f;
+  constexpr int TPK = D / 4, KPB = 256 / TPK, BPC = kChunk / KPB;
+  const int64_t blk = blockIdx.x, bgc = blk / BPC, bg = bgc / c.Nc, chunk = bgc % c.Nc;
+  const int tid = threadIdx.x, kl = (int)(blk % BPC) * KPB + tid / TPK, x4 = 4 * (tid % TPK);
+  float4 sv = make_float4(0.f, 0.f, 0.f, 0.f), sk = sv;
+  const int64_t poff = (int64_t)kl * D + x4;
   for (int64_t band = 0; band < c.n_bands; ++band) {
     const int64_t bin = (bg * c.n_bands + band) * c.Nc + chunk;
     const uint32_t n = c.offsets[bin + 1] - c.offsets[bin];
-    const uint32_t i0 = c.item_start[bin], ni = (n + kBP - 1) / kBP;
-    for (uint32_t it = i0; it < i0 + ni; ++it) {
-      const float* pv = a.item_part + (int64_t)it * 2 * kChunk * D + key * D + d0;
-      const float* pk = pv + kChunk * D;
+    const uint32_t i0 = c.item_start[bin], i1 = i0 + (n + kBP - 1) / kBP;
+    for (uint32_t it = i0; it < i1; it += 4) {     // 4 items in flight, summed in item order
+      float4 v4[4], k4[4];
 #pragma unroll
-      for (int x = 0; x < DPT; x += 4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(pv + x);
-        const float4 k4 = *reinterpret_cast<const float4*>(pk + x);
-        sv[x] += v4.x; sv[x + 1] += v4.y; sv[x + 2] += v4.z; sv[x + 3] += v4.w;
-        sk[x] += k4.x; sk[x + 1] += k4.y; sk[x + 2] += k4.z; sk[x + 3] += k4.w;
+      for (int u = 0; u < 4; ++u) {
+        const float* pv = a.item_part + (int64_t)min(it + u, i1 - 1) * 2 * kChunk * D + poff;
+        v4[u] = *reinterpret_cast<const float4*>(pv);
+        k4[u] = *reinterpret_cast<const float4*>(pv + kChunk * D);
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (it + u < i1) {
+          sv.x += v4[u].x; sv.y += v4[u].y; sv.z += v4[u].z; sv.w += v4[u].w;
+          sk.x += k4[u].x; sk.y += k4[u].y; sk.z += k4[u].z; sk.w += k4[u].w;
+        }
     }
   }
-  const int64_t row = bg * c.Lkv + chunk * kChunk + key;
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(c.k) + row * D + d0;
-  float kx[DPT], ss = 0.f, dot = 0.f;
+  const int64_t row = bg * c.Lkv + chunk * kChunk + kl;
+  const uint2 kr = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(c.k) + row * D + x4);
+  const float kx[4] = {__uint_as_float(kr.x << 16), __uint_as_float(kr.x & 0xFFFF0000u),
+                       __uint_as_float(kr.y << 16), __uint_as_float(kr.y & 0xFFFF0000u)};
+  const float dk4[4] = {sk.x, sk.y, sk.z, sk.w};
+  float ss = 0.f, dot = 0.f;
 #pragma unroll
-  for (int x = 0; x < DPT; ++x) {
-    kx[x] = bf16_to_f32(kp[x]);
+  for (int x = 0; x < 4; ++x) {
     ss += kx[x] * kx[x];
-    dot += kx[x] * sk[x];
+    dot += kx[x] * dk4[x];
   }
-  ss += __shfl_xor(ss, 1, kWave);
-  ss += __shfl_xor(ss, 2, kWave);
-  dot += __shfl_xor(dot, 1, kWave);
-  dot += __shfl_xor(dot, 2, kWave);
+#pragma unroll
+  for (int o = 1; o < TPK; o <<= 1) {
+    ss += __shfl_xor(ss, o, kWave);
+    dot += __shfl_xor(dot, o, kWave);
+  }
   // dkhat -> dk: (dkh - khat (khat . dkh)) / |k|, or dkh / eps below eps
   const float n = sqrtf(ss);
-  float* dko = a.dk + row * D + d0;
-  float* dvo = a.dv + row * D + d0;
+  float g[4];
 #pragma unroll
-  for (int x = 0; x < DPT; ++x) {
-    float g = sk[x];
-    if (c.qk_norm) g = n > 1e-6f ? (sk[x] - kx[x] * (dot / (n * n))) / n : sk[x] * 1e6f;
-    dko[x] = g;
-    dvo[x] = sv[x];
+  for (int x = 0; x < 4; ++x) {
+    g[x] = dk4[x];
+    if (c.qk_norm) g[x] = n > 1e-6f ? (dk4[x] - kx[x] * (dot / (n * n))) / n : dk4[x] * 1e6f;
+  }
+  *reinterpret_cast<float4*>(a.dk + row * D + x4) = make_float4(g[0], g[1], g[2], g[3]);
+  *reinterpret_cast<float4*>(a.dv + row * D + x4) = sv;
+}
+
+// Keys of the trailing partial chunk take no part (no landmark): zero.
+__global__ __launch_bounds__(256) void bwd_tail_kernel(BwdArgs a, int D) {
+  const ChunkArgs& c = a.c;
+  const int64_t bg = blockIdx.y, n = (c.Lkv - c.Nc * kChunk) * D;
+  const int64_t base = (bg * c.Lkv + c.Nc * kChunk) * D;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    a.dk[base + i] = 0.f;
+    a.dv[base + i] = 0.f;
   }
 }
 
-// --- per row: dq_attn, ds, dq_ret ---------------------------------------------
-// One wave per (row, kv head); lane k < K holds slot k.
-template <int D, int G>
-__global__ __launch_bounds__(64) void bwd_row_kernel(BwdArgs a) {
+// --- per slot: dL/ds --------------------------------------------------------------
+// One lane per slot (segments of a power of two >= K lanes per row):
+// draw_k = ret_scale (w_k dw_k - w_k sum_j w_j dw_j), zero for unused slots.
+__global__ __launch_bounds__(256) void bwd_slot_kernel(BwdArgs a) {
   const ChunkArgs& c = a.c;
-  const int64_t row = blockIdx.x;            // (b*Lq + r)*Hkv + g
-  const int lane = threadIdx.x, K = c.K;
-  const int g = (int)(row % c.Hkv);
-  const int64_t br = row / c.Hkv;
-  const int32_t ci = lane < K ? c.idx[row * K + lane] : -1;
-  const bool valid = ci >= 0 && (int64_t)ci < c.Nc;
-  const float wk = valid ? c.wts[row * K + lane] : 0.f;
-  const float wdw = valid ? a.wdw[row * K + lane] : 0.f;
-  const float swdw = wave_sum(wdw);
-  const float dr = valid ? a.ret_scale * (wdw - wk * swdw) : 0.f;   // ret_scale * ds_k
-  if (lane < K) a.draw[row * K + lane] = dr;
-  const uint64_t vmask = __ballot(valid);
-  // dq_ret = sum_k dr_k landmark[c_k] (slot order); lanes split the dims
-  const uint16_t* lmb = reinterpret_cast<const uint16_t*>(a.landmarks) + ((br / c.Lq) * c.Hkv + g) * c.Nc * D;
-  float* dqr = a.dq_ret + row * D;
-  for (int x = lane; x < D; x += 64) {
-    float acc = 0.f;
-    for (int k = 0; k < K; ++k) {
-      if (!((vmask >> k) & 1ull)) continue;
-      const int32_t ck = __shfl(ci, k, kWave);
-      const float drk = __shfl(dr, k, kWave);
-      acc += drk * bf16_to_f32(lmb[(int64_t)ck * D + x]);
+  const int K = c.K, S = K <= 1 ? 1 : 1 << (32 - __clz(K - 1));
+  const int64_t row = (int64_t)blockIdx.x * (256 / S) + threadIdx.x / S;
+  const int k = threadIdx.x & (S - 1);
+  const bool active = row < c.rows && k < K;
+  int32_t ci = -1;
+  if (active) ci = c.idx[row * K + k];
+  const bool valid = active && ci >= 0 && (int64_t)ci < c.Nc;
+  const float wdw = valid ? a.wdw[row * K + k] : 0.f;
+  const float wk = valid ? c.wts[row * K + k] : 0.f;
+  float sum = wdw;
+  for (int o = 1; o < S; o <<= 1) sum += __shfl_xor(sum, o, kWave);
+  if (active) a.draw[row * K + k] = valid ? a.ret_scale * (wdw - wk * sum) : 0.f;
+}
+
+// --- per row: dq_attn and dq_ret -----------------------------------------------
+// D / 4 threads per output row, each owning 4 dims.  Blocks [0, n_attn) take
+// the head-rows (row, head) of dq_attn: the pairs' dqhat summed in slot order,
+// then the normalisation's gradient; the rest take the rows of dq_ret:
+// sum over slots of draw_k * landmark[c_k].
+template <int D, int G>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, uint32_t n_attn) {
+  const ChunkArgs& c = a.c;
+  constexpr int TPH = D / 4, HPB = 256 / TPH;
+  const int K = c.K, tid = threadIdx.x, x4 = 4 * (tid % TPH);
+  if (blockIdx.x < n_attn) {
+    const int64_t u = (int64_t)blockIdx.x * HPB + tid / TPH;     // (row, head)
+    const bool in = u < c.rows * G;
+    const int64_t row = in ? u / G : 0;
+    const int hd = (int)(u % G);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      uint2 v[8];
+      bool ok[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = min(k0 + e, K - 1);
+        const int32_t ci = c.idx[row * K + k];
+        ok[e] = k0 + e < K && ci >= 0 && (int64_t)ci < c.Nc;
+        v[e] = *reinterpret_cast<const uint2*>(a.dq_part + ((row * K + k) * G + hd) * D + x4);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ok[e]) {
+          acc.x += __uint_as_float(v[e].x << 16);
+          acc.y += __uint_as_float(v[e].x & 0xFFFF0000u);
+          acc.z += __uint_as_float(v[e].y << 16);
+          acc.w += __uint_as_float(v[e].y & 0xFFFF0000u);
+        }
     }
-    dqr[x] = acc;
-  }
-  // dq_attn per head: normalisation's gradient of sum_k dqhat_k (slot order)
-  for (int hd = 0; hd < G; ++hd) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(c.q_attn) + (br * c.Hq + (int64_t)g * G + hd) * D;
-    float dqh[D / 64 > 0 ? D / 64 : 1], qv[D / 64 > 0 ? D / 64 : 1];
+    const int64_t qrow = (row / c.Hkv) * c.Hq + (int64_t)(row % c.Hkv) * G + hd;
+    const uint2 qr = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(c.q_attn) + qrow * D + x4);
+    const float qx[4] = {__uint_as_float(qr.x << 16), __uint_as_float(qr.x & 0xFFFF0000u),
+                         __uint_as_float(qr.y << 16), __uint_as_float(qr.y & 0xFFFF0000u)};
+    const float dq4[4] = {acc.x, acc.y, acc.z, acc.w};
     float ss = 0.f, dot = 0.f;
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) {
-      const int x = lane + 64 * u;
-      float acc = 0.f;
-      for (int k = 0; k < K; ++k)
-        if ((vmask >> k) & 1ull) acc += a.dq_part[((row * K + k) * G + hd) * D + x];
-      dqh[u] = acc;
-      qv[u] = bf16_to_f32(qp[x]);
-      ss += qv[u] * qv[u];
-      dot += qv[u] * acc;
+    for (int x = 0; x < 4; ++x) {
+      ss += qx[x] * qx[x];
+      dot += qx[x] * dq4[x];
     }
-    ss = wave_sum(ss);
-    dot = wave_sum(dot);
-    const float n = sqrtf(ss);
-    float* dqo = a.dq_attn + (br * c.Hq + (int64_t)g * G + hd) * D;
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) {
-      float gq = dqh[u];
-      if (c.qk_norm) gq = n > 1e-6f ? (dqh[u] - qv[u] * (dot / (n * n))) / n : dqh[u] * 1e6f;
-      dqo[lane + 64 * u] = vmask ? gq : 0.f;
+    for (int o = 1; o < TPH; o <<= 1) {
+      ss += __shfl_xor(ss, o, kWave);
+      dot += __shfl_xor(dot, o, kWave);
+    }
+    const float n = sqrtf(ss);
+    float g[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      g[x] = dq4[x];
+      if (c.qk_norm) g[x] = n > 1e-6f ? (dq4[x] - qx[x] * (dot / (n * n))) / n : dq4[x] * 1e6f;
+    }
+    if (in) *reinterpret_cast<float4*>(a.dq_attn + qrow * D + x4) = make_float4(g[0], g[1], g[2], g[3]);
+    return;
+  }
+  const int64_t row = (int64_t)(blockIdx.x - n_attn) * HPB + tid / TPH;   // (b*Lq + r)*Hkv + g
+  if (row >= c.rows) return;
+  const int g = (int)(row % c.Hkv);
+  const int64_t b = row / c.Hkv / c.Lq;
+  const uint16_t* lmb = reinterpret_cast<const uint16_t*>(a.landmarks) + (b * c.Hkv + g) * c.Nc * D + x4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    uint2 l[8];
+    float dr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = min(k0 + e, K - 1);
+      const int32_t ci = c.idx[row * K + k];
+      const bool ok = k0 + e < K && ci >= 0 && (int64_t)ci < c.Nc;
+      dr[e] = ok ? a.draw[row * K + k] : 0.f;
+      l[e] = *reinterpret_cast<const uint2*>(lmb + (int64_t)(ok ? ci : 0) * D);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc.x += dr[e] * __uint_as_float(l[e].x << 16);
+      acc.y += dr[e] * __uint_as_float(l[e].x & 0xFFFF0000u);
+      acc.z += dr[e] * __uint_as_float(l[e].y << 16);
+      acc.w += dr[e] * __uint_as_float(l[e].y & 0xFFFF0000u);
     }
   }
+  *reinterpret_cast<float4*>(a.dq_ret + row * D + x4) = acc;
 }
 
 // --- per chunk: dlandmark -------------------------------------------------------
+// D / 8 threads per pair, each owning 8 dims; 256 / (D / 8) groups take the
+// chunk's pairs round robin, then the groups' sums are added in group order.
 template <int D>
-__global__ __launch_bounds__(D) void bwd_landmark_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_landmark_kernel(BwdArgs a) {
   const ChunkArgs& c = a.c;
+  constexpr int TPP = D / 8, NG = 256 / TPP;
+  __shared__ float red[NG][D + 4];
   const int64_t bg = blockIdx.x / c.Nc, chunk = blockIdx.x % c.Nc;
-  const int x = threadIdx.x;
-  const uint16_t* qr = reinterpret_cast<const uint16_t*>(a.q_ret) + x;
-  float acc = 0.f;
+  const int tid = threadIdx.x, grp = tid / TPP, x8 = 8 * (tid % TPP);
+  const uint16_t* qr = reinterpret_cast<const uint16_t*>(a.q_ret) + x8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int64_t band = 0; band < c.n_bands; ++band) {
     const int64_t bin = (bg * c.n_bands + band) * c.Nc + chunk;
     const uint32_t p0 = c.offsets[bin], p1 = c.offsets[bin + 1];
-    for (uint32_t p = p0; p < p1; p += 8) {   // 8 pairs in flight, summed in pair order
-      uint32_t pid[8];
-      float dr[8], qv[8];
+    for (uint32_t p = p0 + grp; p < p1; p += 4 * NG) {   // four pairs in flight, in order
+      uint32_t pid[4];
+      float dr[4];
+      uint4 q[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pid[u] = c.pairs[min(p + u, p1 - 1)];
+      for (int u = 0; u < 4; ++u) pid[u] = c.pairs[min(p + u * NG, p1 - 1)];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        dr[u] = a.draw[pid[u]];
-        qv[u] = bf16_to_f32(qr[(int64_t)(pid[u] / (uint32_t)c.K) * D]);   // row (b*Lq + r)*Hkv + g
+      for (int u = 0; u < 4; ++u) {
+        dr[u] = p + u * NG < p1 ? a.draw[pid[u]] : 0.f;
+        q[u] = *reinterpret_cast<const uint4*>(qr + (int64_t)(pid[u] / (uint32_t)c.K) * D);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (p + u < p1) acc += dr[u] * qv[u];
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t wq[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += dr[u] * __uint_as_float(wq[e] << 16);
+          acc[2 * e + 1] += dr[u] * __uint_as_float(wq[e] & 0xFFFF0000u);
+        }
+      }
     }
   }
-  a.dlandmarks[(bg * c.Nc + chunk) * D + x] = acc;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) red[grp][x8 + x] = acc[x];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int gi = 0; gi < NG; ++gi) s += red[gi][tid];
+    a.dlandmarks[(bg * c.Nc + chunk) * D + tid] = s;
+  }
 }
 
 }  // namespace
@@ -471,12 +581,27 @@ hipError_t launch_bwd_dg(const BwdArgs& a, hipStream_t st, const Marks& mk) {
   }
   if ((e = mk.rec(kStageAttend, 1, st)) != hipSuccess) return e;
   if ((e = mk.rec(kStageCombine, 0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_row_kernel<D, G>), dim3((unsigned)a.c.rows), dim3(64), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chunk_kernel<D>), dim3((unsigned)(n_bg * (a.c.Nc + 1))), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    const int64_t S = a.c.K <= 1 ? 1 : (int64_t)1 << (32 - __builtin_clz((unsigned)a.c.K - 1));
+    hipLaunchKernelGGL(bwd_slot_kernel, dim3((unsigned)((a.c.rows + 256 / S - 1) / (256 / S))), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    constexpr int64_t HPB = 256 / (D / 4);
+    const int64_t n_attn = (a.c.rows * G + HPB - 1) / HPB, n_ret = (a.c.rows + HPB - 1) / HPB;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)(n_attn + n_ret)), dim3(256), 0, st, a,
+                       (uint32_t)n_attn);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.c.Nc > 0) {
-    hipLaunchKernelGGL((bwd_landmark_kernel<D>), dim3((unsigned)(n_bg * a.c.Nc)), dim3(D), 0, st, a);
+    constexpr int64_t BPC = kChunk / (256 / (D / 4));
+    hipLaunchKernelGGL((bwd_chunk_kernel<D>), dim3((unsigned)(n_bg * a.c.Nc * BPC)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_landmark_kernel<D>), dim3((unsigned)(n_bg * a.c.Nc)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.c.Lkv > a.c.Nc * kChunk) {
+    hipLaunchKernelGGL(bwd_tail_kernel, dim3(8, (unsigned)n_bg), dim3(256), 0, st, a, D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return mk.rec(kStageCombine, 1, st);

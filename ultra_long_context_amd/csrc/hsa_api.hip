@@ -437,7 +437,7 @@ hsa_status_t make_bwd_plan(const hsa_shape_t* s, BwdPlan* b) {
   b->off_wts = off; off = align_up(off + np * 4, 256);
   b->off_wdw = off; off = align_up(off + np * 4, 256);
   b->off_draw = off; off = align_up(off + np * 4, 256);
-  b->off_dqp = off; off = align_up(off + np * p.G * D * 4, 256);
+  b->off_dqp = off; off = align_up(off + np * p.G * D * 2, 256);
   b->off_itemp = off; off = align_up(off + (size_t)p.max_items * 2 * HSA_CHUNK_TOKENS * D * 4, 256);
   b->total = std::max<size_t>(off, 256);
   return HSA_OK;
@@ -502,7 +502,7 @@ hsa_status_t backward_impl(const hsa_shape_t* shape, const void* q_ret, const vo
   a.dq_ret = dq_ret; a.dlandmarks = dlandmarks; a.dq_attn = dq_attn; a.dk = dk; a.dv = dv;
   a.wdw = reinterpret_cast<float*>(w + b.off_wdw);
   a.draw = reinterpret_cast<float*>(w + b.off_draw);
-  a.dq_part = reinterpret_cast<float*>(w + b.off_dqp);
+  a.dq_part = reinterpret_cast<uint16_t*>(w + b.off_dqp);
   a.item_part = reinterpret_cast<float*>(w + b.off_itemp);
   a.ret_scale = p.ret_scale;
   return hsa::launch_backward(a, p.D, p.G, static_cast<hipStream_t>(stream), mk) == hipSuccess

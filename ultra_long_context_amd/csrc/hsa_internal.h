@@ -124,7 +124,7 @@ struct BwdArgs {
   float* dv;              // [B, Hkv, Lkv, D]
   float* wdw;             // [rows * K]   w_k * dL/dw_k per pair
   float* draw;            // [rows * K]   dL/d(q_ret . landmark) per pair
-  float* dq_part;         // [rows * K, G, D]  per-pair gradient of the normalised query
+  uint16_t* dq_part;      // [rows * K, G, D]  per-pair gradient of the normalised query (bf16)
   float* item_part;       // [max_items, 2, 64, D]  per-item dV and dkhat of the chunk's keys
   float ret_scale;
 };
