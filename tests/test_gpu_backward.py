@@ -3,10 +3,10 @@ fp64 oracle's backward, for a selection the oracle's forward made.
 
 Tolerance: for each gradient tensor, max |gpu - oracle| <= 2e-2 * max |oracle|
 and ||gpu - oracle||_2 <= 6e-3 * ||oracle||_2.  The kernels take bf16 inputs,
-round the MFMA operands P, w*dout, dz/|q| and dz/|k| to bf16 (relative error
-2^-9 each) and accumulate in fp32, so a gradient entry carries a relative error
-of about 1e-3 per rounded factor; a dropped term or a wrong index moves the
-result by O(1) of the gradient's scale.
+round the MFMA operands P, w*dout, dz/|q| and dz/|k| and the per-pair query
+gradients to bf16 (relative error up to 2^-9 each) and accumulate in fp32, so a
+gradient entry carries a relative error of about 1e-3 per rounded factor; a
+dropped term or a wrong index moves the result by O(1) of the gradient's scale.
 """
 import numpy as np
 import pytest
