@@ -25,6 +25,12 @@ peaks by its algorithmic work per launch:
   profiles/ (null when none exists or the kernel sources changed since).
 cpu_baseline: the fp64 oracle on a bounded, stratified sample of query rows of the
 same workload, timed on this host's cores (test infrastructure, not the product).
+
+Further workloads (--workloads): global_32K (top-K covering all 512 chunks of the
+32K window: global HSA), backward_32K (hsa_backward on the 32K window for the
+forward's selection; roofline on the per-item MFMA kernel, 10*G*64*d FLOP per
+selection), crossover (HSA forward vs dense causal SDPA from 4K to 1M tokens,
+opt-in; also against dense attention at the bf16 MFMA peak).
 """
 from __future__ import annotations
 
@@ -349,6 +355,73 @@ def oracle_backward_baseline(cfg, inp, dout, idx, sc, budget_s=15.0):
                     cfg.batch * len(rows), total, stride, dt))
 
 
+CROSSOVER_LENGTHS = (4096, 8192, 16384, 32768, 65536, 131072, 262144, 524288, 1048576)
+
+
+def bench_crossover(steps, warmup, timer, lengths=CROSSOVER_LENGTHS):
+    """HSA forward against dense causal attention (torch SDPA, flash or
+    memory-efficient backend only) on the 32K training window's head layout
+    (B=1, 8 q heads / 1 kv head, d=128, top-K 8) at growing L = Lq = Lkv.
+    Inputs: seeded N(0,1) bf16 drawn on the GPU; landmarks = chunk means
+    (hsa_chunk_landmarks).  Each side is a captured graph timed cold."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import ultra_long_context_amd as hsa
+
+    rows = []
+    for L in lengths:
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(L)
+        rnd = lambda *shape: torch.randn(*shape, generator=gen, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
+        q_ret, q_attn = rnd(1, L, 1, 128), rnd(1, L, 8, 128)
+        k, v = rnd(1, 1, L, 128), rnd(1, 1, L, 128)
+        lm = hsa.chunk_landmarks(k)
+        out = torch.empty_like(q_attn)
+
+        def hsa_step():
+            hsa.forward(q_ret, lm, q_attn, k, v, q_pos0=0, top_k=8, out=out)
+
+        for _ in range(warmup):
+            hsa_step()
+        hsa_ms, _, _ = timer.time(timer.capture(hsa_step), steps)
+        # dense comparator: [B, H, L, d] with the kv head repeated for the 8 q heads
+        qd = q_attn.permute(0, 2, 1, 3).contiguous()
+        kd = k.expand(1, 8, L, 128).contiguous()
+        vd = v.expand(1, 8, L, 128).contiguous()
+        del q_ret, q_attn, k, v, lm, out
+        dense_ms, backend = None, None
+        for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+            try:
+                with sdpa_kernel([be]):
+                    def dense_step():
+                        F.scaled_dot_product_attention(qd, kd, vd, is_causal=True)
+                    for _ in range(warmup):
+                        dense_step()
+                    torch.cuda.synchronize()
+                    dense_ms, _, _ = timer.time(timer.capture(dense_step), steps)
+                backend = be.name.lower()
+                break
+            except RuntimeError as e:
+                log("[bench] crossover L=%d: SDPA %s unavailable (%s)" % (L, be.name, str(e).splitlines()[0]))
+        del qd, kd, vd
+        torch.cuda.empty_cache()
+        # dense causal attention at the bf16 MFMA peak: 2*L^2*d FLOP per q head
+        bound_ms = 2.0 * L * L * 128 * 8 / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+        rows.append(dict(L=L, hsa_ms=hsa_ms, dense_ms=dense_ms, dense_backend=backend,
+                         hsa_over_dense=None if dense_ms is None else hsa_ms / dense_ms,
+                         dense_mfma_bound_ms=bound_ms))
+        log("[bench] crossover L=%d: hsa %.4f ms, dense %s ms (%s)" % (
+            L, hsa_ms, "n/a" if dense_ms is None else "%.4f" % dense_ms, backend))
+    faster = [r["L"] for r in rows if r["dense_ms"] is not None and r["hsa_ms"] < r["dense_ms"]]
+    faster_bound = [r["L"] for r in rows if r["hsa_ms"] < r["dense_mfma_bound_ms"]]
+    return dict(workload="crossover_gqa8_d128_k8", rows=rows,
+                crossover_L=min(faster) if faster else None,
+                crossover_L_vs_mfma_bound=min(faster_bound) if faster_bound else None,
+                note="smallest L at which the HSA forward is faster than dense causal SDPA "
+                     "(measured) and than dense causal attention at the bf16 MFMA peak")
+
+
 def bench_workload(name, steps, warmup, timer, cpu_baseline):
     import torch
     import ultra_long_context_amd as hsa
@@ -548,6 +621,13 @@ def main():
     timer = Timer()
     names = [w for w in args.workloads.split(",") if w]
     results = {}
+    crossover = None
+    if "crossover" in names:
+        names.remove("crossover")
+        crossover = bench_crossover(args.steps, args.warmup, timer)
+        if not names:
+            print(json.dumps(crossover), flush=True)
+            return
     for name in ["decode_16M", "global_32K", "backward_32K", "prefill_128K"]:
         if name in names:
             results[name] = bench_workload(name, args.steps, args.warmup, timer,
@@ -586,6 +666,8 @@ def main():
         if "cpu_baseline" in r:
             sub["cpu_baseline"] = r["cpu_baseline"]
         line[name] = sub
+    if crossover is not None:
+        line["crossover"] = crossover
     print(json.dumps(line), flush=True)
 
 
