@@ -200,12 +200,27 @@ def algorithmic(cfg, U, elem=2):
                 bwd_flops=10 * cfg.group * 64 * d * sel)
 
 
-def source_digest() -> str:
-    """sha256 over the library's kernel sources (traffic figures go stale with them)."""
+# source file of each kernel family; a kernel's traffic figure goes stale when
+# its file or a shared header changes
+KERNEL_FILES = {
+    "scan_wide_kernel": "retrieve.hip", "scan_block_kernel": "retrieve.hip", "scan_topk_kernel": "retrieve.hip",
+    "attend_decode_kernel": "attend_decode.hip", "merge_lists_kernel": "attend_decode.hip",
+    "chunk_attend_kernel": "attend_chunk.hip", "chunk_combine_kernel": "attend_chunk.hip",
+    "attend_global_kernel": "attend_global.hip", "chunk_landmark_kernel": "landmarks.hip",
+    "bwd_item_kernel": "backward.hip", "bwd_dq_kernel": "backward.hip",
+}
+SHARED_HEADERS = ("hsa_device.h", "hsa_internal.h")
+
+
+def source_digest(kernel: str = "") -> str:
+    """sha256 over the kernel's source file and the shared device headers (all
+    kernel sources for an unknown kernel)."""
     import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "ultra_long_context_amd", "csrc")
-    for f in sorted(os.listdir(src)):
+    fam = KERNEL_FILES.get(kernel.split("<")[0])
+    files = sorted(os.listdir(src)) if fam is None else [fam, *SHARED_HEADERS]
+    for f in files:
         if f.endswith((".hip", ".h")):
             with open(os.path.join(src, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
@@ -228,7 +243,7 @@ def measured_traffic(workload, kernel):
             if ":" in line and not line.startswith("#"):
                 k_, v_ = line.split(":", 1)
                 kv[k_.strip()] = v_.strip()
-    if kv.get("source_digest") != source_digest():
+    if kv.get("source_digest") != source_digest(kernel):
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -554,7 +569,7 @@ def pmc_summary(fetch_csv, write_csv, workload, kernel, command):
         "# command: %s" % command,
         "kernel: %s" % kernel,
         "workload: %s" % workload,
-        "source_digest: %s" % source_digest(),
+        "source_digest: %s" % source_digest(kernel),
         "fetch_dispatches: %d" % nf,
         "write_dispatches: %d" % nw,
         "FETCH_SIZE_KiB_per_dispatch: %.1f" % f_k,
