@@ -29,6 +29,26 @@ namespace hsa {
 namespace {
 
 constexpr int kBP = 64;                     // pairs per work item (as the forward)
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// LDS transpose load (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j passes the address of X[r0 + j / 4][c0 + 4 (j % 4)] (8 bytes of a
+// row-major bf16 array) and lane t receives X[r0 + e][c0 + t], e = 0..3: four
+// consecutive rows of one column, the k-run of an MFMA operand.
+__device__ __forceinline__ uint2 lds_tr4(const uint16_t* p) {
+  const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(p));
+  return __builtin_bit_cast(uint2, x);
+}
+
+// MFMA operand of rows r0..r0+7 (k) at column c0 + lane % 16 from a row-major
+// [k][n] bf16 array with row stride `ld`: two transpose loads.
+__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* base, int ld, int r0, int c0, int ma) {
+  const uint16_t* p = base + (r0 + (ma >> 2)) * ld + c0 + 4 * (ma & 3);
+  const uint2 lo = lds_tr4(p), hi = lds_tr4(p + 4 * ld);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
 constexpr float kLog2eB = 1.4426950408889634f;
 
 // --- sort each bin's pair ids ascending (bitonic in LDS) --------------------
@@ -77,17 +97,20 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
   constexpr int KROW = D + 8;               // K, V rows (bf16)
   constexpr int TROW = kChunk + 8;          // K^T rows (permuted keys)
-  constexpr int HROW = 64 + 8;              // staged [key or dim][64 head-rows]
+  constexpr int PROW = kChunk + 16;          // staged P, h rows [head-row][key]
+  constexpr int QROW = D + 16;              // staged q, dO_w rows [head-row][dim]
   constexpr int PT = 16 / G;                // pairs per 16-head-row tile
   constexpr int KSTEP = D / 32, NT = D / 16;
   __shared__ __align__(16) uint16_t ks[kChunk * KROW];
   __shared__ __align__(16) uint16_t vs[kChunk * KROW];
   __shared__ __align__(16) uint16_t kt[D * TROW];
   __shared__ float rk[kChunk];
-  __shared__ __align__(16) uint16_t ps[kChunk * HROW];   // P^T   [key][hr]
-  __shared__ __align__(16) uint16_t hs[kChunk * HROW];   // h^T   [key][hr]
-  __shared__ __align__(16) uint16_t dt[D * HROW];        // dO_w^T [dim][hr]
-  __shared__ __align__(16) uint16_t qt[D * HROW];        // q^T   [dim][hr]
+  // phase B operands of the 64 head-rows of 4 tiles, row-major (read back
+  // transposed): P and h [hr][key], dO_w and q [hr][dim]
+  __shared__ __align__(16) uint16_t ps[64 * PROW];
+  __shared__ __align__(16) uint16_t hs[64 * PROW];
+  __shared__ __align__(16) uint16_t ds_[64 * QROW];
+  __shared__ __align__(16) uint16_t qs[64 * QROW];
   __shared__ uint32_t pid_s[kBP];
   __shared__ float w_s[kBP];
   __shared__ int64_t qoff_s[kBP];
@@ -198,15 +221,11 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
                            (__bf16)(__uint_as_float(yw[q] & 0xFFFF0000u) * wp)};
         dw4[q] = __builtin_bit_cast(uint32_t, o2);
       }
-      da[t] = __builtin_bit_cast(bf16x8, make_uint4(dw4[0], dw4[1], dw4[2], dw4[3]));
-      // stage q^T and dO_w^T for phase B: [dim][head-row]
-      const uint16_t* qe = reinterpret_cast<const uint16_t*>(&qa[t]);
-      const uint16_t* de = reinterpret_cast<const uint16_t*>(&da[t]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qt[(32 * t + 8 * jg + e) * HROW + 16 * w + ma] = qe[e];
-        dt[(32 * t + 8 * jg + e) * HROW + 16 * w + ma] = de[e];
-      }
+      const uint4 dw = make_uint4(dw4[0], dw4[1], dw4[2], dw4[3]);
+      da[t] = __builtin_bit_cast(bf16x8, dw);
+      // stage q and dO_w rows for phase B
+      *reinterpret_cast<uint4*>(&qs[(16 * w + ma) * QROW + 32 * t + 8 * jg]) = x;
+      *reinterpret_cast<uint4*>(&ds_[(16 * w + ma) * QROW + 32 * t + 8 * jg]) = dw;
     }
     if (t0 + 4 < n_tiles) {   // next tile's rows, in flight during this one
       const int64_t off = tile_off(t0 + 4 + w);
@@ -280,15 +299,22 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
     // g = attn dz |k|^-1 (for dqhat), h = attn dz |q|^-1 (for dkhat), dz = P (dP - pdp)
     bf16x8 gb[2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < 4; ++nt) {
+      float hv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float dz = sv[nt][i] * (dp[nt][i] - pdp) * as;
-        const int key = 16 * nt + 4 * jg + i;
-        ps[key * HROW + 16 * w + ma] = __builtin_bit_cast(uint16_t, (__bf16)sv[nt][i]);
-        hs[key * HROW + 16 * w + ma] = __builtin_bit_cast(uint16_t, (__bf16)(dz * rq));
+        hv[i] = dz * rq;
         gb[nt >> 1][4 * (nt & 1) + i] = (__bf16)(dz * rkl[nt][i]);
       }
+      // P and h rows of head-row 16w + ma, keys 16nt + 4jg .. +3
+      const bf16x2 p01 = {(__bf16)sv[nt][0], (__bf16)sv[nt][1]}, p23 = {(__bf16)sv[nt][2], (__bf16)sv[nt][3]};
+      const bf16x2 h01 = {(__bf16)hv[0], (__bf16)hv[1]}, h23 = {(__bf16)hv[2], (__bf16)hv[3]};
+      *reinterpret_cast<uint2*>(&ps[(16 * w + ma) * PROW + 16 * nt + 4 * jg]) =
+          make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+      *reinterpret_cast<uint2*>(&hs[(16 * w + ma) * PROW + 16 * nt + 4 * jg]) =
+          make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+    }
     // dqhat^T = K^T g^T: lane holds dims 16*nt + 4*jg + i of head-row ma
     uint16_t* dq = a.dq_part + (live ? ((int64_t)pid_s[pm] * G + hd) * D : 0) + 4 * jg;
 #pragma unroll
@@ -308,20 +334,21 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
     }
     __syncthreads();
     // ---- phase B: keys 16w .. 16w+15 over the 64 staged head-rows ----------
+    // A = P^T / h^T (key x head-row), B = dO_w / q (head-row x dim), both read
+    // transposed from the row-major staging
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int st = 0; st < 2; ++st) {
+      const int r0 = 32 * st + 8 * jg;
+      const bf16x8 pa = lds_operand_tr(ps, PROW, r0, 16 * w, ma);
+      const bf16x8 ha = lds_operand_tr(hs, PROW, r0, 16 * w, ma);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const uint4 pa = *reinterpret_cast<const uint4*>(&ps[(16 * w + ma) * HROW + 32 * st + 8 * jg]);
-        const uint4 ha = *reinterpret_cast<const uint4*>(&hs[(16 * w + ma) * HROW + 32 * st + 8 * jg]);
-        const uint4 db = *reinterpret_cast<const uint4*>(&dt[(16 * nt + ma) * HROW + 32 * st + 8 * jg]);
-        const uint4 qb = *reinterpret_cast<const uint4*>(&qt[(16 * nt + ma) * HROW + 32 * st + 8 * jg]);
-        dv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pa), __builtin_bit_cast(bf16x8, db),
-                                                         dv[nt], 0, 0, 0);
-        dk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ha), __builtin_bit_cast(bf16x8, qb),
-                                                         dk[nt], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 db = lds_operand_tr(ds_, QROW, r0, 16 * nt, ma);
+        const bf16x8 qb = lds_operand_tr(qs, QROW, r0, 16 * nt, ma);
+        dv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, db, dv[nt], 0, 0, 0);
+        dk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, qb, dk[nt], 0, 0, 0);
+        if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
-      if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   }
