@@ -184,3 +184,29 @@ def test_backward_training_window_sampled(hsa):
         compare([z, got[1][:, :, c], z, got[3][:, :, sl], got[4][:, :, sl]],
                 [z, ref[1][:, :, c], z, ref[3][:, :, sl], ref[4][:, :, sl]],
                 " (chunk %d, %d rows)" % (c, rows_c.size))
+
+
+def test_backward_without_complete_chunks(hsa):
+    """A history shorter than one chunk: nothing can be selected, every
+    gradient is zero (the partial chunk's keys included)."""
+    import torch
+    cfg = small(q_len=64, q_pos0=0, kv_len=37, n_needles=0, top_k=4)
+    inp = W.generate(cfg)
+    idx = np.full((1, cfg.q_len, 1, cfg.top_k), -1, np.int32)
+    idx[0, ::3, 0, 0] = 0                       # chunk 0 does not exist (Nc = 0): unused
+    sc = np.zeros(idx.shape, np.float32)
+    dout = W.cotangent(cfg)
+    got = gpu_backward(hsa, inp, dout, idx, sc)
+    for name, g in zip(NAMES, got):
+        assert np.all(g == 0), name
+
+
+def test_backward_duplicate_slots(hsa):
+    """A given selection may name one chunk in two slots of a row: two pairs,
+    as in the oracle."""
+    cfg = small(q_len=300, top_k=6)
+
+    def edit(idx):
+        idx[0, ::7, 0, 1] = idx[0, ::7, 0, 0]
+
+    full_parity(hsa, cfg, edit)

@@ -421,8 +421,10 @@ hsa_status_t make_bwd_plan(const hsa_shape_t* s, BwdPlan* b) {
   const Plan& p = b->p;
   if (!p.bf16) return HSA_ERR_UNSUPPORTED;
   const int64_t n_pairs = p.rows * p.K, n_bg = p.rows / p.Lq;
+  // grid sizes: per-row kernels take (rows * G + rows) / 8 workgroups at most,
+  // per-chunk kernels 8 per chunk
   if (n_pairs >= INT32_MAX || p.n_bins + 1 >= INT32_MAX || p.max_items >= INT32_MAX ||
-      n_bg * (p.Nc + 1) >= INT32_MAX)
+      n_bg * (p.Nc + 1) >= INT32_MAX / 8 || p.rows * (p.G + 1) / 8 >= INT32_MAX)
     return HSA_ERR_BAD_SHAPE;
   const size_t nb = (size_t)p.n_bins, np = (size_t)n_pairs, D = (size_t)p.D;
   size_t off = 0;
