@@ -118,6 +118,58 @@ def test_decode_shape_split_merge(hsa):
     parity(hsa, W.generate(cfg))
 
 
+def test_split_merge_one_list_holds_the_top_k(hsa):
+    """All scores tie (q_ret = 0): the first 32 chunks win, all from the first
+    split's list, so the merge must read that list past its first entries."""
+    cfg = W.shrink(W.CONFIGS[3], kv_len=1 << 20)
+    inp = W.generate(cfg)
+    inp.q_ret[:] = 0
+    _, _, (_, idx, _) = parity(hsa, inp)
+    assert np.all(idx.cpu().numpy() == np.arange(cfg.top_k))
+
+
+def test_split_merge_clustered_winners(hsa):
+    """Every row shares one retrieval query and 20 boosted chunks inside one
+    1024-chunk split: that split's list contributes 20 of the 32 winners."""
+    cfg = W.shrink(W.CONFIGS[3], kv_len=1 << 20)
+    inp = W.generate(cfg)
+    q = W.to_f64(inp.q_ret[0, 0], cfg.dtype)                     # [Hkv, d]
+    inp.q_ret[:] = inp.q_ret[0:1, 0:1]
+    lm = W.to_f64(inp.landmarks, cfg.dtype)
+    u = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    lm[0, :, 2048:2068, :] += 6.0 * cfg.sigma_l * u[:, None, :]
+    inp.landmarks[:] = W.store(lm, cfg.dtype)
+    _, _, (_, idx, _) = parity(hsa, inp)
+    sel = idx.cpu().numpy()
+    assert np.all(((sel >= 2048) & (sel < 2068)).sum(-1) == 20)
+
+
+@pytest.mark.parametrize("K", [3, 4, 5])
+def test_split_merge_small_top_k(hsa, K):
+    """K at and around the merge's first-entries depth."""
+    cfg = W.shrink(W.CONFIGS[3], kv_len=1 << 20, top_k=K)
+    parity(hsa, W.generate(cfg))
+
+
+def test_split_merge_retrieve_entry(hsa):
+    """The standalone merge kernel (hsa_retrieve_topk with several splits)."""
+    import torch
+    cfg = W.shrink(W.CONFIGS[3], kv_len=1 << 20)
+    inp = W.generate(cfg)
+    inp.q_ret[:, ::2] = 0
+    q_ret, lm = (to_device(a, cfg.dtype) for a in (inp.q_ret, inp.landmarks))
+    idx, score = hsa.retrieve_topk(q_ret, lm, q_pos0=cfg.q_pos0, top_k=cfg.top_k)
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.q_len)
+    oi, os_, _, _ = oracle.forward(inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v, q_pos0=cfg.q_pos0,
+                                   top_k=cfg.top_k, with_output=False)
+    gi = idx.cpu().numpy().reshape(cfg.q_len, cfg.n_kv_heads, cfg.top_k)
+    gs = score.cpu().numpy().reshape(cfg.q_len, cfg.n_kv_heads, cfg.top_k)
+    rs = oracle.default_scale(cfg.head_dim)
+    check_selection(inp, rows, gi, gs, oi, os_, ret_scale=rs)
+    assert np.all(gi[::2] == np.arange(cfg.top_k))
+
+
 def test_chunked_prefill_shape_cut(hsa):
     cfg = W.shrink(W.CONFIGS[4], q_len=512, kv_len=65536 + 512)
     inp = W.generate(cfg)

@@ -24,38 +24,94 @@ constexpr int kSlotsPerBlock = 4;       // one wave per slot
 constexpr int kThreads = 64 * kSlotsPerBlock;
 constexpr int kMergeCap = 512;
 constexpr int kMaxHeads = 8;          // list heads per lane: up to 512 splits
+constexpr int kMaxBlocks = kMaxTopK / kSlotsPerBlock;   // slot blocks of a row
 
-// Exact top K of one row from its per-split lists L[s][0..K) (each sorted best
-// first, zero-padded); whole wave.  A list can only contribute if its head
-// reaches the K-th largest head, and then only entries at or above that head:
-// the per-lane largest heads give a bound (upper 16 key bits), the few lists
-// above it are read in batches, and the surviving candidates are ranked.  Leaves the sorted selection
-// in top[0..m) and returns m.  Loads are unconditional (indices clamped) so
-// they are all in flight together.
+// Exact top K of one row from its per-split lists, entry-major: entry j of
+// split s at L[j * n_splits + s], each list sorted best first and zero-padded;
+// whole wave.  Leaves the sorted selection in top[0..m) and returns m.
+//
+// Fast path (one round of loads): the first kFirst entries of every list are
+// loaded together; the heads bound the K-th largest key from below (the K-th
+// largest of the lanes' largest heads: K lanes hold a key there), the loaded
+// entries at or above the bound are ranked, and the result is exact unless
+// some list's last loaded entry still reaches the K-th selected key (then a
+// later entry of that list could belong to the top K).  In that case the full
+// merge below runs: a list can only contribute if its head reaches the K-th
+// largest head, and then only entries at or above that head; those lists are
+// read in batches and the surviving candidates ranked.  Loads are
+// unconditional (indices clamped) so they are all in flight together.
+constexpr int kFirst = 4;
+
 template <int NH>
 __device__ __forceinline__ int merge_row_lists_nh(const uint64_t* L, int n_splits, int K, uint64_t* C,
                                                   uint64_t* top, int* act, int lane) {
   constexpr int kMaxHeadSlots = NH;                  // list heads per lane
   const int nh = (n_splits + kWave - 1) / kWave;      // <= NH
+  const int ne = K < kFirst ? K : kFirst;
+  uint64_t f[kFirst][kMaxHeadSlots];
+#pragma unroll
+  for (int j = 0; j < kFirst; ++j)
+#pragma unroll
+    for (int i = 0; i < kMaxHeadSlots; ++i) {
+      const int sp = lane + kWave * i;
+      const uint64_t v = L[(int64_t)(j < ne ? j : 0) * n_splits + (sp < n_splits ? sp : 0)];
+      f[j][i] = (j < ne && i < nh && sp < n_splits) ? v : 0ull;
+    }
+  // the K-th largest lane maximum of the heads: K lanes hold a key at or above
+  // it, so it bounds the row's K-th largest key from below (0 if fewer)
+  uint64_t hmax = f[0][0];
+#pragma unroll
+  for (int i = 1; i < kMaxHeadSlots; ++i) hmax = f[0][i] > hmax ? f[0][i] : hmax;
+  C[lane] = hmax;
+  const int hrank = lds_rank(C, kWave, hmax);
+  const uint64_t kmask_h = __ballot(hmax != 0ull && hrank == K - 1);
+  const uint64_t lo_heads = kmask_h != 0ull ? shfl_u64(hmax, (int)__builtin_ctzll(kmask_h)) : 0ull;
+  {
+    uint64_t lo = lo_heads;
+    int n_on = 0;
+#pragma unroll
+    for (int j = 0; j < kFirst; ++j)
+#pragma unroll
+      for (int i = 0; i < kMaxHeadSlots; ++i) n_on += wave_count(f[j][i] != 0ull && f[j][i] >= lo);
+    if (n_on > kWave) {                 // exact K-th of the loaded entries: K survive
+      uint64_t flat[kFirst * kMaxHeadSlots];
+#pragma unroll
+      for (int j = 0; j < kFirst; ++j)
+#pragma unroll
+        for (int i = 0; i < kMaxHeadSlots; ++i) flat[j * kMaxHeadSlots + i] = f[j][i];
+      lo = wave_kth_regs<kFirst * kMaxHeadSlots>(flat, kFirst * kMaxHeadSlots, K);
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kFirst; ++j)
+#pragma unroll
+      for (int i = 0; i < kMaxHeadSlots; ++i) {
+        const bool keep = f[j][i] != 0ull && f[j][i] >= lo;
+        const uint64_t mask = __ballot(keep);
+        if (keep) C[cnt + __popcll(mask & lanemask_lt())] = f[j][i];
+        cnt += __popcll(mask);
+      }
+    if (cnt <= kWave) {
+      const uint64_t mine = lane < cnt ? C[lane] : 0ull;
+      const int rank = lds_rank(C, cnt, mine);
+      const int m = cnt < K ? cnt : K;
+      // K-th selected key (with fewer than K, any nonzero entry would still enter)
+      const uint64_t kmask = __ballot(lane < cnt && rank == K - 1);
+      const uint64_t kth = (m == K && kmask != 0ull) ? shfl_u64(mine, (int)__builtin_ctzll(kmask)) : 1ull;
+      bool open = false;
+#pragma unroll
+      for (int i = 0; i < kMaxHeadSlots; ++i) open = open || f[kFirst - 1][i] >= kth;
+      if (ne == K || !__any(open)) {
+        if (lane < cnt && rank < K) top[rank] = mine;
+        return m;
+      }
+    }
+  }
+  // ---- full merge ------------------------------------------------------------
   uint64_t h[kMaxHeadSlots];
 #pragma unroll
-  for (int i = 0; i < kMaxHeadSlots; ++i) {
-    const int sp = lane + kWave * i;
-    const uint64_t v = L[(int64_t)(sp < n_splits ? sp : 0) * K];
-    h[i] = (i < nh && sp < n_splits) ? v : 0ull;
-  }
-  // K lanes whose largest head reaches t16 << 16 hold K distinct heads there,
-  // so the K-th largest head does too: one ballot per bisection step
-  uint64_t hmax = h[0];
-#pragma unroll
-  for (int i = 1; i < kMaxHeadSlots; ++i) hmax = h[i] > hmax ? h[i] : hmax;
-  const uint32_t hm16 = (uint32_t)(hmax >> 48);
-  uint32_t t16 = 0;
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t cand = t16 | (1u << bit);
-    if (wave_count(hm16 >= cand) >= K) t16 = cand;
-  }
-  uint64_t lo = (uint64_t)t16 << 48;
+  for (int i = 0; i < kMaxHeadSlots; ++i) h[i] = f[0][i];
+  uint64_t lo = lo_heads;
   int n_on = 0;
 #pragma unroll
   for (int i = 0; i < kMaxHeadSlots; ++i)
@@ -71,12 +127,12 @@ __device__ __forceinline__ int merge_row_lists_nh(const uint64_t* L, int n_split
     na += __popcll(mask);
   }
   const int my_list = lane < na ? act[lane] : -1;
-  const uint64_t* lp = L + (int64_t)(my_list >= 0 ? my_list : 0) * K;
+  const uint64_t* lp = L + (my_list >= 0 ? my_list : 0);
   int cnt = 0;
   for (int q0 = 0; q0 < K; q0 += 16) {
     uint64_t e[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) e[q] = lp[q0 + q < K ? q0 + q : K - 1];
+    for (int q = 0; q < 16; ++q) e[q] = lp[(int64_t)(q0 + q < K ? q0 + q : K - 1) * n_splits];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       if (my_list < 0 || q0 + q >= K) e[q] = 0ull;
@@ -96,9 +152,9 @@ __device__ __forceinline__ int merge_row_lists_nh(const uint64_t* L, int n_split
     // lists are sorted: one whose last entry here is below the bound is done
     if (!__any(e[15] != 0ull && e[15] >= lo)) break;
   }
-  if (cnt <= kWave) {                    // one candidate per lane: rank in registers
+  if (cnt <= kWave) {                    // one candidate per lane
     const uint64_t mine = lane < cnt ? C[lane] : 0ull;
-    const int rank = wave_rank_lanes(mine, cnt);
+    const int rank = lds_rank(C, cnt, mine);
     if (lane < cnt && rank < K) top[rank] = mine;
     return cnt < K ? cnt : K;
   }
@@ -119,9 +175,9 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   constexpr int KSTEP = D / 32;
   constexpr int NT = D / 16;
-  constexpr int VROW = kChunk + 8;     // bf16 elements per V^T row
+  constexpr int VROW = D + 16;         // bf16 elements per staged V row (row-major)
   constexpr int PROW = kChunk + 8;
-  __shared__ __align__(16) uint16_t vt[kSlotsPerBlock][D * VROW];
+  __shared__ __align__(16) uint16_t vs[kSlotsPerBlock][kChunk * VROW];
   __shared__ __align__(16) uint16_t ps[kSlotsPerBlock][16 * PROW];
   __shared__ uint64_t cand[kMergeCap];
   __shared__ uint64_t top[kMaxTopK];
@@ -207,16 +263,9 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int dg = 0; dg < D / 8; ++dg) vx[dg] = *reinterpret_cast<const uint4*>(vp + lane * D + 8 * dg);
-    // V^T into LDS
+    // V rows into LDS (read back transposed as the B operand of P V)
 #pragma unroll
-    for (int dg = 0; dg < D / 8; ++dg) {
-      const uint32_t wv[4] = {vx[dg].x, vx[dg].y, vx[dg].z, vx[dg].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        vt[w][(8 * dg + 2 * q) * VROW + lane] = (uint16_t)(wv[q] & 0xFFFFu);
-        vt[w][(8 * dg + 2 * q + 1) * VROW + lane] = (uint16_t)(wv[q] >> 16);
-      }
-    }
+    for (int dg = 0; dg < D / 8; ++dg) *reinterpret_cast<uint4*>(&vs[w][lane * VROW + 8 * dg]) = vx[dg];
     // norms: lane holds 32 dims of query row ma and of key 16*nt + ma
     float qss = 0.f, kss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -296,8 +345,8 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint4 bv = *reinterpret_cast<const uint4*>(&vt[w][(16 * nt + ma) * VROW + 32 * st + 8 * jg]);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8[st], __builtin_bit_cast(bf16x8, bv), o[nt], 0, 0, 0);
+        const bf16x8 bv = lds_operand_tr(vs[w], VROW, 32 * st + 8 * jg, 16 * nt, ma);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8[st], bv, o[nt], 0, 0, 0);
       }
   }
   // --- sum the 4 waves' outputs; lane holds O[4*jg + i][16*nt + ma] ----------
@@ -325,12 +374,29 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   if (tid == 0) last = arrive(&a.counters[row]) == (uint32_t)(n_blk - 1);
   __syncthreads();
   if (!last) return;
+  // each thread adds 4 consecutive outputs over the blocks, in block order,
+  // with every block's 16 bytes in flight at once
   const float* pb = a.partials + row * n_blk * (int64_t)(G * D);
-  for (int e = tid; e < G * D; e += kThreads) {
-    float v = 0.f;
-#pragma unroll 16
-    for (int p = 0; p < n_blk; ++p) v += fetch(&pb[(int64_t)p * G * D + e]);
-    op[e] = f32_to_bf16(v);
+  for (int e0 = 4 * tid; e0 < G * D; e0 += 4 * kThreads) {
+    uint64_t lo[kMaxBlocks], hi[kMaxBlocks];
+#pragma unroll
+    for (int p = 0; p < kMaxBlocks; ++p) {
+      const uint64_t* q = reinterpret_cast<const uint64_t*>(pb + (int64_t)(p < n_blk ? p : 0) * G * D + e0);
+      lo[p] = fetch(q);
+      hi[p] = fetch(q + 1);
+    }
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kMaxBlocks; ++p)
+      if (p < n_blk) {
+        v[0] += __uint_as_float((uint32_t)lo[p]);
+        v[1] += __uint_as_float((uint32_t)(lo[p] >> 32));
+        v[2] += __uint_as_float((uint32_t)hi[p]);
+        v[3] += __uint_as_float((uint32_t)(hi[p] >> 32));
+      }
+    const uint32_t b01 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    const uint32_t b23 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(op + e0) = make_uint2(b01, b23);
   }
   if (tid == 0) reset_counter(&a.counters[row]);
 }

@@ -29,26 +29,6 @@ namespace hsa {
 namespace {
 
 constexpr int kBP = 64;                     // pairs per work item (as the forward)
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-
-// LDS transpose load (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// lane j passes the address of X[r0 + j / 4][c0 + 4 (j % 4)] (8 bytes of a
-// row-major bf16 array) and lane t receives X[r0 + e][c0 + t], e = 0..3: four
-// consecutive rows of one column, the k-run of an MFMA operand.
-__device__ __forceinline__ uint2 lds_tr4(const uint16_t* p) {
-  const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) short4v*)(p));
-  return __builtin_bit_cast(uint2, x);
-}
-
-// MFMA operand of rows r0..r0+7 (k) at column c0 + lane % 16 from a row-major
-// [k][n] bf16 array with row stride `ld`: two transpose loads.
-__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* base, int ld, int r0, int c0, int ma) {
-  const uint16_t* p = base + (r0 + (ma >> 2)) * ld + c0 + 4 * (ma & 3);
-  const uint2 lo = lds_tr4(p), hi = lds_tr4(p + 4 * ld);
-  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
 constexpr float kLog2eB = 1.4426950408889634f;
 
 // --- sort each bin's pair ids ascending (bitonic in LDS) --------------------

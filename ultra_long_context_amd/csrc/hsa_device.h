@@ -235,16 +235,17 @@ __device__ __forceinline__ int wave_keep_top(uint64_t* arr, int n, int K, int la
   return off;
 }
 
-// Rank of each lane's candidate e among the candidates of lanes [0, n) (one
-// per lane, unique nonzero keys; n wave-uniform): the number of them above e.
-// Lanes are read with v_readlane, so no memory round trip is involved.
-__device__ __forceinline__ int wave_rank_lanes(uint64_t e, int n) {
-  const uint32_t lo = (uint32_t)e, hi = (uint32_t)(e >> 32);
+// Rank of e among arr[0..n) in LDS (unique nonzero keys, n wave-uniform): the
+// number of entries above it.  Every lane reads the same addresses (broadcast),
+// eight entries in flight per step.
+__device__ __forceinline__ int lds_rank(const uint64_t* arr, int n, uint64_t e) {
   int rank = 0;
-  for (int o = 0; o < n; ++o) {
-    const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, o) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)lo, o);
-    rank += x > e;
+  for (int i0 = 0; i0 < n; i0 += 8) {
+    uint64_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = arr[i0 + u < n ? i0 + u : n - 1];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rank += (i0 + u < n && x[u] > e) ? 1 : 0;
   }
   return rank;
 }
@@ -252,12 +253,29 @@ __device__ __forceinline__ int wave_rank_lanes(uint64_t e, int n) {
 // Rank-sorts arr[0..m) (m <= 64, unique keys) into dst[0..m), best first.
 // dst must not alias arr.
 __device__ __forceinline__ void wave_rank_sort(const uint64_t* arr, int m, uint64_t* dst, int lane) {
-  if (lane < m) {
-    const uint64_t e = arr[lane];
-    int rank = 0;
-    for (int i = 0; i < m; ++i) rank += arr[i] > e;
-    dst[rank] = e;
-  }
+  const uint64_t e = lane < m ? arr[lane] : 0ull;
+  const int rank = lds_rank(arr, m, e);
+  if (lane < m) dst[rank] = e;
+}
+
+// LDS transpose load (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j passes the address of X[r0 + j / 4][c0 + 4 (j % 4)] (8 bytes of a
+// row-major bf16 array) and lane t receives X[r0 + e][c0 + t], e = 0..3: four
+// consecutive rows of one column, the k-run of an MFMA operand.
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr4(const uint16_t* p) {
+  const short4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
+  return __builtin_bit_cast(uint2, x);
+}
+
+// MFMA operand (v_mfma_f32_16x16x32_bf16, A or B) of rows r0..r0+7 (the k
+// index) at column c0 + lane % 16 of a row-major [k][n] bf16 array in LDS with
+// row stride `ld` elements: two transpose loads.  Lane group lane / 16 passes
+// its own r0.
+__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* base, int ld, int r0, int c0, int ma) {
+  const uint16_t* p = base + (r0 + (ma >> 2)) * ld + c0 + 4 * (ma & 3);
+  const uint2 lo = lds_tr4(p), hi = lds_tr4(p + 4 * ld);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
 }  // namespace hsa

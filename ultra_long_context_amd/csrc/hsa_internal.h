@@ -29,7 +29,7 @@ struct ScanArgs {
   const void* landmarks;  // [B, Hkv, Nc, D]
   int32_t* out_idx;       // [B, Lq, Hkv, K]
   float* out_score;       // [B, Lq, Hkv, K]
-  uint64_t* lists;        // [B*Lq*Hkv, n_splits, K] per-split sorted candidates (wide, n_splits > 1)
+  uint64_t* lists;        // [B*Lq*Hkv, K, n_splits] per-split sorted candidates, entry-major (wide, n_splits > 1)
   int64_t Lq, q_pos0, Nc;
   int32_t Hkv, K;
   int32_t n_max;          // max eligible chunks over all rows
@@ -40,7 +40,7 @@ struct ScanArgs {
 
 // Merge of per-split sorted candidate lists into the final selection.
 struct MergeArgs {
-  const uint64_t* lists;  // [rows, n_splits, K]
+  const uint64_t* lists;  // [rows, K, n_splits] (entry-major)
   int32_t* out_idx;       // [rows, K]
   float* out_score;       // [rows, K]
   int64_t rows;
@@ -53,7 +53,7 @@ struct DecodeArgs {
   const void* q_attn;
   const void* k;
   const void* v;
-  const uint64_t* lists;     // per-split sorted candidates [rows, n_splits, K], or nullptr
+  const uint64_t* lists;     // per-split sorted candidates [rows, K, n_splits], or nullptr
   const int32_t* idx_in;     // given selection when lists == nullptr
   const float* score_in;
   int32_t* idx_out;          // final selection written by slot block 0 (merged path; may be null)

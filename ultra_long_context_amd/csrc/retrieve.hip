@@ -288,7 +288,9 @@ __global__ __launch_bounds__(64) void scan_topk_kernel(ScanArgs a) {
 // lane maximum bounds the row's K-th key from below, and the few keys at or
 // above it are cut to the exact top K.  With one split the workgroup writes the
 // final selection; otherwise it writes one sorted list per row and split, which
-// a merge (merge_lists_kernel, or the decode attend's prologue) combines.
+// a merge (merge_lists_kernel, or the decode attend's prologue) combines.  The
+// lists of a row are stored entry-major ([entry][split]), so the first entries
+// of every split are contiguous.
 // ---------------------------------------------------------------------------
 constexpr int kWideWaves = 16;
 constexpr int kWideChunksPerWave = 64;
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
   const int64_t row_flat = (b * a.Lq + rw) * a.Hkv + g;
   if (n <= kWave) {                 // one candidate per lane: rank them in registers
     const uint64_t e = lane < n ? C[lane] : 0ull;
-    const int rank = wave_rank_lanes(e, n);
+    const int rank = lds_rank(C, n, e);
     const int m = n < K ? n : K;
     if (!rw_ok) return;
     if (a.n_splits == 1) {
@@ -469,9 +471,10 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
         score[lane] = -INFINITY;
       }
     } else {
-      uint64_t* list = a.lists + (row_flat * a.n_splits + s) * K;
-      if (lane < n && rank < K) list[rank] = e;
-      if (lane >= m && lane < K) list[lane] = 0ull;
+      // entry-major lists: entry j of split s at [row][j][s]
+      uint64_t* list = a.lists + row_flat * a.n_splits * K + s;
+      if (lane < n && rank < K) list[(int64_t)rank * a.n_splits] = e;
+      if (lane >= m && lane < K) list[(int64_t)lane * a.n_splits] = 0ull;
     }
     return;
   }
@@ -482,7 +485,8 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
                                a.ret_scale);
     return;
   }
-  if (rw_ok && lane < K) a.lists[(row_flat * a.n_splits + s) * K + lane] = lane < m ? top[w][lane] : 0ull;
+  if (rw_ok && lane < K)
+    a.lists[row_flat * a.n_splits * K + (int64_t)lane * a.n_splits + s] = lane < m ? top[w][lane] : 0ull;
 }
 
 // ---------------------------------------------------------------------------
