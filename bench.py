@@ -23,6 +23,8 @@ peaks by its algorithmic work per launch:
   traffic: HBM bytes per launch from two rocprofv3 counter passes (FETCH_SIZE,
   WRITE_SIZE) scaled by a 1 GiB calibration copy, read from the summary under
   profiles/ (null when none exists or the kernel sources changed since).
+step_roofline: the whole step against t_roof = max(compulsory bytes / 8 TB/s,
+MFMA FLOPs / 2.5 PFLOP/s); frac = t_roof / ms_per_step.
 cpu_baseline: the fp64 oracle on a bounded, stratified sample of query rows of the
 same workload, timed on this host's cores (test infrastructure, not the product).
 
@@ -284,6 +286,16 @@ def roofline(workload, stage, ms, alg):
                 kernel_ms=ms, algorithmic_per_launch=amount, algorithmic_units=how)
 
 
+def step_roofline(nbytes, flops, ms):
+    """Whole-step roofline: t_roof = max(bytes / HBM peak, FLOPs / bf16 MFMA peak)
+    over the measured step time."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    t_roof = max(t_hbm, t_mfma)
+    return dict(bound="hbm" if t_hbm >= t_mfma else "mfma", t_roof_ms=t_roof, t_hbm_ms=t_hbm,
+                t_mfma_ms=t_mfma, frac=t_roof / ms)
+
+
 def bench_backward(name, cfg, steps, warmup, timer, cpu_baseline):
     """One step = hsa_backward over the whole batch for the forward's selection."""
     import torch
@@ -338,6 +350,7 @@ def bench_backward(name, cfg, steps, warmup, timer, cpu_baseline):
     dom = max(stage_ms, key=stage_ms.get)
     res["roofline"] = roofline(name, dom, stage_ms[dom], alg)
     res["hbm_frac_whole_step"] = (alg["bwd_bytes"] / 8e12) / (ms_mean / 1e3)
+    res["step_roofline"] = step_roofline(alg["bwd_bytes"], alg["bwd_flops"], ms_mean)
     if cpu_baseline:
         res["cpu_baseline"] = oracle_backward_baseline(cfg, inp, dout_np, idx.cpu().numpy(), sc.cpu().numpy())
     del q_ret, lm, q_attn, k, v, dout, grads, eager, inp
@@ -493,6 +506,7 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     dom = max(stage_ms, key=stage_ms.get)
     res["roofline"] = roofline(name, dom, stage_ms[dom], alg)
     res["hbm_frac_whole_step"] = (alg["bytes"] / 8e12) / (ms_mean / 1e3)
+    res["step_roofline"] = step_roofline(alg["bytes"], alg["scan_flops"] + alg["attend_flops"], ms_mean)
     if name == "decode_16M":
         # KV-cache maintenance beside the step: every chunk-mean landmark of the
         # history rebuilt from K (hsa_chunk_landmarks), an HBM stream
@@ -665,6 +679,7 @@ def main():
         "roofline": m["roofline"],
         "wall_ms_per_step": m["wall_ms_per_step"], "warm_ms_per_step": m["warm_ms_per_step"],
         "hbm_frac_whole_step": m["hbm_frac_whole_step"],
+        "step_roofline": m["step_roofline"],
         "stage_ms": m["stage_ms"],
     }
     if "cpu_baseline" in m:
@@ -673,7 +688,7 @@ def main():
         if name == main_name:
             continue
         sub = {k: r[k] for k in ("value", "ms_per_step", "ms_median", "wall_ms_per_step",
-                                 "warm_ms_per_step", "roofline", "hbm_frac_whole_step",
+                                 "warm_ms_per_step", "roofline", "hbm_frac_whole_step", "step_roofline",
                                  "landmark_rebuild") if k in r}
         sub["unit"] = "query-tokens/s"
         sub["config"] = cfg_dict(r["config"])
