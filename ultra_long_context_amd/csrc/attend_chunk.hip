@@ -308,12 +308,12 @@ __device__ __forceinline__ float sumsq8(uint4 x, float acc) {
 template <int D, int G>
 __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   constexpr int KROW = D + 8;          // bf16 elements per K row in LDS (16-byte pad)
-  constexpr int VROW = kChunk + 8;     // bf16 elements per V^T row
+  constexpr int VROW = D + 16;         // bf16 elements per V row in LDS (read back transposed)
   constexpr int PT = 16 / G;           // pairs per MFMA tile (16 head-rows)
   constexpr int KSTEP = D / 32;        // MFMA K-steps over the head dimension
   constexpr int NT = D / 16;           // output dimension tiles
   __shared__ __align__(16) uint16_t ks[kChunk * KROW];
-  __shared__ __align__(16) uint16_t vt[D * VROW];
+  __shared__ __align__(16) uint16_t vs[kChunk * VROW];
   __shared__ float rk[kChunk];
   __shared__ uint32_t pid_s[kPairs];
   __shared__ float w_s[kPairs];
@@ -333,9 +333,9 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   const int64_t bg = bgb / a.n_bands;
   const int g = (int)(bg % a.Hkv);
 
-  // pair ids and blend weights of the item; K (row-major) and V^T in LDS.
-  // V^T columns are permuted inside each 32-key block (key 16h + 4q + r sits
-  // at 8q + 4h + r) so that the P.V operands line up with the S^T accumulators.
+  // pair ids and blend weights of the item; K and V (row-major) in LDS.  The
+  // P.V operand is read from V with LDS transpose loads in the key order of
+  // the S^T accumulators, so P^T feeds P.V from registers.
   if (tid < n_pairs) {
     const uint32_t pid = a.pairs[p_begin + tid];
     pid_s[tid] = pid;
@@ -348,41 +348,18 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     const uint4* kp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k) + base);
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v) + base;
     constexpr int NK = kChunk * D / 8 / 256;          // 16-byte K pieces per thread
-    constexpr int NV = (16 * (D / 8) + 255) / 256;    // (4 keys x 8 dims) V blocks per thread
-    uint4 kx[NK], vx[NV][4];
+    const uint4* vp4 = reinterpret_cast<const uint4*>(vp);
+    uint4 kx[NK], vx[NK];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kx[i] = kp[tid + 256 * i];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int u = tid + 256 * i, kq = u & 15, dg = u >> 4;
-      if (dg < D / 8) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vx[i][r] = *reinterpret_cast<const uint4*>(vp + (4 * kq + r) * D + 8 * dg);
-      }
+    for (int i = 0; i < NK; ++i) {
+      kx[i] = kp[tid + 256 * i];
+      vx[i] = vp4[tid + 256 * i];
     }
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       const int e = (tid + 256 * i) * 8;
       *reinterpret_cast<uint4*>(&ks[(e / D) * KROW + e % D]) = kx[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int u = tid + 256 * i, kq = u & 15, dg = u >> 4;
-      if (dg < D / 8) {
-        const int q8 = kq & 7;                           // 4-key group inside the 32-key block
-        const int col = 32 * (kq >> 3) + 8 * (q8 & 3) + 4 * (q8 >> 2);
-        const uint32_t* r0 = reinterpret_cast<const uint32_t*>(&vx[i][0]);
-        const uint32_t* r1 = reinterpret_cast<const uint32_t*>(&vx[i][1]);
-        const uint32_t* r2 = reinterpret_cast<const uint32_t*>(&vx[i][2]);
-        const uint32_t* r3 = reinterpret_cast<const uint32_t*>(&vx[i][3]);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const int wd = d >> 1, sh = (d & 1) * 16;
-          const uint32_t e0 = (r0[wd] >> sh) & 0xFFFFu, e1 = (r1[wd] >> sh) & 0xFFFFu;
-          const uint32_t e2 = (r2[wd] >> sh) & 0xFFFFu, e3 = (r3[wd] >> sh) & 0xFFFFu;
-          *reinterpret_cast<uint2*>(&vt[(8 * dg + d) * VROW + col]) = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-        }
-      }
+      *reinterpret_cast<uint4*>(&vs[(e / D) * VROW + e % D]) = vx[i];
     }
   }
   __syncthreads();
@@ -469,8 +446,9 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
       floatx4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint4 va = *reinterpret_cast<const uint4*>(&vt[(16 * nt + ma) * VROW + 32 * st + 8 * jg]);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[st], o, 0, 0, 0);
+        // A = V^T: dims 16nt.., keys 32st + 4jg + 0..3 and 32st + 16 + 4jg + 0..3
+        const bf16x8 va = lds_operand_tr2(vs, VROW, 32 * st + 4 * jg, 32 * st + 16 + 4 * jg, 16 * nt, ma);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[st], o, 0, 0, 0);
       }
       if (live) {
         const half2v h01 = {(_Float16)o[0], (_Float16)o[1]}, h23 = {(_Float16)o[2], (_Float16)o[3]};

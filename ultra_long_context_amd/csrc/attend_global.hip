@@ -31,11 +31,11 @@ constexpr float kLog2eG = 1.4426950408889634f;
 template <int D, int G>
 __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) {
   constexpr int R = 256 / G;                   // query rows per workgroup
-  constexpr int KROW = D + 8, VROW = kChunk + 8, LROW = D + 8;
+  constexpr int KROW = D + 8, VROW = D + 16, LROW = D + 8;
   constexpr int KSTEP = D / 32, NT = D / 16;
   constexpr int TPR = 16 / G;                  // rows per 16-head-row tile (G = 8: 2, G = 16: 1)
   __shared__ __align__(16) uint16_t ks[2][kChunk * KROW];
-  __shared__ __align__(16) uint16_t vt[2][D * VROW];
+  __shared__ __align__(16) uint16_t vs[2][kChunk * VROW];   // V rows, read back transposed
   __shared__ float rk[2][kChunk];
   __shared__ __align__(16) uint16_t lt[kGTile * LROW];
   __shared__ float sc[R][kGTile + 1];          // base-2 retrieval scores, -inf past the row's chunks
@@ -84,8 +84,9 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
   const float rq = (a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f) * a.attn_scale * kLog2eG;
 
   // K / V staging: each thread one 16-byte piece of K and one of V (8 dims of
-  // one key); V goes to V^T with the key permuted inside its 32-key block
-  // (key 16h + 4q + r at 8q + 4h + r) so that P^T feeds P.V from registers
+  // one key), both row-major; the P.V operand is read from V with LDS
+  // transpose loads in the key order of the S^T accumulators, so P^T feeds
+  // P.V from registers
   constexpr int NKP = kChunk * D / 8;          // 16-byte pieces per chunk
   uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
   auto load_kv = [&](int c) {
@@ -113,14 +114,7 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
       ss += dpp_f<0x141>(ss);              // half-row mirror: 8 lanes
       if constexpr (D == 128) ss += dpp_f<0x140>(ss);   // row mirror: 16 lanes
       if (d0 == 0) rk[bi][key] = a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
-      const int kp = key & 31;
-      const int col = 32 * (key >> 5) + 8 * ((kp & 15) >> 2) + 4 * (kp >> 4) + (kp & 3);
-      const uint32_t wd[4] = {vx.x, vx.y, vx.z, vx.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        vt[bi][(d0 + 2 * q) * VROW + col] = (uint16_t)(wd[q] & 0xFFFFu);
-        vt[bi][(d0 + 2 * q + 1) * VROW + col] = (uint16_t)(wd[q] >> 16);
-      }
+      *reinterpret_cast<uint4*>(&vs[bi][key * VROW + d0]) = vx;
     }
   };
   floatx4 acc[NT];
@@ -231,8 +225,9 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint4 va = *reinterpret_cast<const uint4*>(&vt[cb][(16 * nt + ma) * VROW + 32 * st + 8 * jg]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb[st], acc[nt], 0, 0, 0);
+        // A = V^T: dims 16nt.., keys 32st + 4jg + 0..3 and 32st + 16 + 4jg + 0..3
+        const bf16x8 va = lds_operand_tr2(vs[cb], VROW, 32 * st + 4 * jg, 32 * st + 16 + 4 * jg, 16 * nt, ma);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[st], acc[nt], 0, 0, 0);
       }
       if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the V^T operands in flight
     }

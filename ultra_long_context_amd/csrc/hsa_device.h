@@ -268,14 +268,17 @@ __device__ __forceinline__ uint2 lds_tr4(const uint16_t* p) {
   return __builtin_bit_cast(uint2, x);
 }
 
-// MFMA operand (v_mfma_f32_16x16x32_bf16, A or B) of rows r0..r0+7 (the k
-// index) at column c0 + lane % 16 of a row-major [k][n] bf16 array in LDS with
-// row stride `ld` elements: two transpose loads.  Lane group lane / 16 passes
-// its own r0.
-__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* base, int ld, int r0, int c0, int ma) {
-  const uint16_t* p = base + (r0 + (ma >> 2)) * ld + c0 + 4 * (ma & 3);
-  const uint2 lo = lds_tr4(p), hi = lds_tr4(p + 4 * ld);
+// MFMA operand (v_mfma_f32_16x16x32_bf16, A or B) at column c0 + lane % 16 of
+// a row-major [k][n] bf16 array in LDS with row stride `ld` elements: its
+// eight k entries are rows ra..ra+3 then rb..rb+3 (two transpose loads; each
+// lane group lane / 16 passes its own ra, rb).  lds_operand_tr: rows r0..r0+7.
+__device__ __forceinline__ bf16x8 lds_operand_tr2(const uint16_t* base, int ld, int ra, int rb, int c0, int ma) {
+  const int off = (ma >> 2) * ld + c0 + 4 * (ma & 3);
+  const uint2 lo = lds_tr4(base + ra * ld + off), hi = lds_tr4(base + rb * ld + off);
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* base, int ld, int r0, int c0, int ma) {
+  return lds_operand_tr2(base, ld, r0, r0 + 4, c0, ma);
 }
 
 }  // namespace hsa
