@@ -204,12 +204,15 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
     // --- online blend over chunks (Step 4) -----------------------------------
     const float sr = sc[rloc][c % kGTile];
     float f = 0.f;                             // this chunk's factor on O_c
+    float al = 1.0f;                           // rescale of the running sum
     if (sr != -INFINITY) {
       const float mn = fmaxf(m, sr);
-      const float al = __builtin_amdgcn_exp2f(m - mn);   // m = -inf first: 0
+      al = __builtin_amdgcn_exp2f(m - mn);     // m = -inf first: 0
       f = __builtin_amdgcn_exp2f(sr - mn);
       l = l * al + f;
       m = mn;
+    }
+    if (__any(al != 1.0f)) {                   // the running maximum rose for some row
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
