@@ -471,15 +471,28 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs a) {
   const int64_t row = t / (G * J);
   const int h = (int)((t / J) % G), j = (int)(t % J);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < a.K; ++k) {
-    const int32_t c = a.idx[row * a.K + k];
-    if (c < 0 || (int64_t)c >= a.Nc) continue;
-    const uint4 u = *reinterpret_cast<const uint4*>(&a.partials[((row * a.K + k) * G + h) * D + 8 * j]);
-    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+  const int K = a.K;
+  // slots in batches of 8 with every load in flight (indices clamped, unused
+  // slots skipped when adding), added in slot order
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    uint4 u[8];
+    bool ok[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += __half2float(__ushort_as_half((unsigned short)(wd[q] & 0xFFFFu)));
-      acc[2 * q + 1] += __half2float(__ushort_as_half((unsigned short)(wd[q] >> 16)));
+    for (int e = 0; e < 8; ++e) {
+      const int k = k0 + e < K ? k0 + e : K - 1;
+      const int32_t c = a.idx[row * K + k];
+      ok[e] = k0 + e < K && c >= 0 && (int64_t)c < a.Nc;
+      u[e] = *reinterpret_cast<const uint4*>(&a.partials[((row * K + k) * G + h) * D + 8 * j]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!ok[e]) continue;
+      const uint32_t wd[4] = {u[e].x, u[e].y, u[e].z, u[e].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __half2float(__ushort_as_half((unsigned short)(wd[q] & 0xFFFFu)));
+        acc[2 * q + 1] += __half2float(__ushort_as_half((unsigned short)(wd[q] >> 16)));
+      }
     }
   }
   uint4 o;
