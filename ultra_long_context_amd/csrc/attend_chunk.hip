@@ -5,13 +5,13 @@
 // With many rows the same chunk is selected by many (row, slot) pairs, while the
 // pairs of one row point at unrelated chunks.  Gathering per row would move a
 // chunk's 2*64*d values once per pair; here the pairs are bucketed by chunk so a
-// workgroup stages one chunk's K and V^T in LDS once and runs every pair that
+// workgroup stages one chunk's K and V in LDS once and runs every pair that
 // selected it on MFMA tiles:
 //   count    per row: blend weights w_k (softmax of the selected scores) and a
 //            histogram of pairs per (batch, kv head, chunk) bin;
-//   scan     bin offsets and the list of work items (bin, block of kPairs pairs);
+//   scan     bin offsets and the list of work items (bin, block of pairs_per_item pairs);
 //   scatter  pair ids into their bins;
-//   attend   per work item: K (row-major) and V^T in LDS, key norms once; per
+//   attend   per work item: K and V (row-major) in LDS, key norms once; per
 //            tile of 16 head-rows (16/G pairs x G heads): S = Q K^T on
 //            v_mfma_f32_16x16x32_bf16, in-chunk softmax across the tile's rows,
 //            P (times w_k, rounded to bf16) V on MFMA, fp16 partial per pair;
@@ -24,7 +24,8 @@
 namespace hsa {
 namespace {
 
-constexpr int kPairs = 64;   // pairs per work item
+constexpr int kMaxPairs = 128;   // pairs per work item at most (ChunkArgs::pairs_per_item)
+constexpr int kFwdPairs = 128;   // forward work items: K and V staged once per 128 pairs
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Bins are (batch, kv head, band of band_rows query rows, chunk): items of one
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) void chunk_count_kernel(ChunkArgs a) {
 // global atomics drop from one per pair to one per (workgroup, chunk).  Used
 // when the chunks of one (batch, kv head) fit the LDS histogram.
 constexpr int kBucketRows = 1024;
-constexpr int kBandRows = 8192;          // a multiple of kBucketRows
+constexpr int kBandRows = 16384;         // forward bins; a multiple of kBucketRows
 constexpr int kHistMax = 16384;
 constexpr int kBucketBatch = 4;          // row passes whose loads are issued together
 
@@ -181,6 +182,7 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t& a, uint32_t& b, 
 }
 
 __global__ __launch_bounds__(kScanThreads) void chunk_seg_scan_kernel(ChunkArgs a) {
+  const uint32_t ppi = (uint32_t)a.pairs_per_item;
   __shared__ uint32_t sp[kScanThreads], si[kScanThreads];
   const int t = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * a.Nc, n = a.Nc;
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_seg_scan_kernel(ChunkArgs 
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       tp += c[u];
-      ti += (c[u] + kPairs - 1) / kPairs;
+      ti += (c[u] + ppi - 1) / ppi;
     }
   }
   uint32_t rp = tp, ri = ti, tot_p, tot_i;
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_seg_scan_kernel(ChunkArgs 
         a.offsets[base + i0 + u] = rp;
         a.cursor[base + i0 + u] = ri;
         rp += c[u];
-        ri += (c[u] + kPairs - 1) / kPairs;
+        ri += (c[u] + ppi - 1) / ppi;
       }
     }
   }
@@ -221,6 +223,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_seg_scan_kernel(ChunkArgs 
 }
 
 __global__ __launch_bounds__(kScanThreads) void chunk_seg_fix_kernel(ChunkArgs a) {
+  const uint32_t ppi = (uint32_t)a.pairs_per_item;
   __shared__ uint32_t sp[kScanThreads], si[kScanThreads];
   const int t = threadIdx.x;
   const int64_t seg = blockIdx.x;
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kScanThreads) void chunk_seg_fix_kernel(ChunkArgs a
         a.cursor[i] = pb + lp[u];
         a.counts[i] = 0u;                        // ready for the next call
         if (a.item_start != nullptr) a.item_start[i] = ib + li[u];
-        const uint32_t ni = (c[u] + kPairs - 1) / kPairs;
+        const uint32_t ni = (c[u] + ppi - 1) / ppi;
         for (uint32_t jb = 0; jb < ni; ++jb) a.items[ib + li[u] + jb] = (uint64_t)i | ((uint64_t)jb << 32);
       }
     }
@@ -315,9 +318,9 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   __shared__ __align__(16) uint16_t ks[kChunk * KROW];
   __shared__ __align__(16) uint16_t vs[kChunk * VROW];
   __shared__ float rk[kChunk];
-  __shared__ uint32_t pid_s[kPairs];
-  __shared__ float w_s[kPairs];
-  __shared__ int64_t qoff_s[kPairs];   // element offset of the pair's G attention queries
+  __shared__ uint32_t pid_s[kMaxPairs];
+  __shared__ float w_s[kMaxPairs];
+  __shared__ int64_t qoff_s[kMaxPairs];   // element offset of the pair's G attention queries
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const uint32_t item_i = blockIdx.x;
@@ -325,8 +328,8 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   const uint64_t item = a.items[item_i];
   const int64_t bin = (int64_t)(item & 0xFFFFFFFFull);
   const uint32_t blk = (uint32_t)(item >> 32);
-  const uint32_t p_begin = a.offsets[bin] + blk * kPairs;
-  const uint32_t p_end = min(p_begin + (uint32_t)kPairs, a.offsets[bin + 1]);
+  const uint32_t p_begin = a.offsets[bin] + blk * (uint32_t)a.pairs_per_item;
+  const uint32_t p_end = min(p_begin + (uint32_t)a.pairs_per_item, a.offsets[bin + 1]);
   const int n_pairs = (int)(p_end - p_begin);
   const int64_t bgb = bin / a.Nc;                // (batch, kv head) * n_bands + band
   const int64_t c = bin - bgb * a.Nc;
@@ -521,7 +524,7 @@ hipError_t launch_dg(const ChunkArgs& a, hipStream_t st, const Marks& mk) {
 
 }  // namespace
 
-int64_t chunk_pairs_per_item() { return kPairs; }
+int64_t chunk_pairs_per_item() { return kFwdPairs; }
 int64_t chunk_band_rows() { return kBandRows; }
 
 hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st) {

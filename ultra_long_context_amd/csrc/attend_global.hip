@@ -10,12 +10,12 @@
 //   m' = max(m, s_c),  l' = l 2^(m-m') + 2^(s_c-m'),  acc' = acc 2^(m-m') + 2^(s_c-m') O_c,
 // out = acc / l (scores in base 2).  A workgroup of 16 waves owns 256/G
 // consecutive query rows of one (batch, kv head) (16 head-rows per wave) and
-// streams their eligible chunks: each chunk's K (row-major) and V^T (permuted
-// as in the chunk-major attend) are staged in LDS once for all 256 head-rows,
-// double-buffered so the next chunk's loads are in flight during the current
-// one; S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16 with P
-// (times the chunk's blend factor, over the in-chunk sum, rounded to bf16) fed
-// from registers.  Retrieval scores of the block's rows come 64 chunks at a
+// streams their eligible chunks: each chunk's K and V (row-major) are staged in
+// LDS once for all 256 head-rows, double-buffered so the next chunk's loads are
+// in flight during the current one; S^T = K Q^T and O^T += V^T P^T run on
+// v_mfma_f32_16x16x32_bf16, V^T read with LDS transpose loads, with P (times
+// the chunk's blend factor, over the in-chunk sum, rounded to bf16) fed from
+// registers.  Retrieval scores of the block's rows come 64 chunks at a
 // time from the same MFMA, landmarks as the A operand.
 #include "hsa_device.h"
 #include "hsa_internal.h"

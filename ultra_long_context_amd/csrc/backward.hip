@@ -574,6 +574,7 @@ __global__ __launch_bounds__(256) void bwd_landmark_kernel(BwdArgs a) {
 }  // namespace
 
 int64_t bwd_pairs_per_item() { return kBP; }
+int64_t bwd_band_rows() { return 8192; }   // a bin holds <= 8192 pairs: sortable in LDS
 
 namespace {
 

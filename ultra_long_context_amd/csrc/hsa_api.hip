@@ -254,6 +254,7 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
     c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
     c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
     c.band_rows = chunk_band_rows(); c.n_bands = p.n_bands;
+    c.pairs_per_item = (int32_t)chunk_pairs_per_item();
     c.attn_scale = p.attn_scale; c.qk_norm = p.qk_norm ? 1 : 0;
     return launch_attend_chunk(c, p.D, p.G, st, mk) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
   }
@@ -418,7 +419,12 @@ struct BwdPlan {
 hsa_status_t make_bwd_plan(const hsa_shape_t* s, BwdPlan* b) {
   hsa_status_t st = make_plan(s, &b->p, false);
   if (st != HSA_OK) return st;
-  const Plan& p = b->p;
+  Plan& p = b->p;
+  // backward bins and work items: smaller bands (every bin sortable in LDS)
+  // and at most bwd_pairs_per_item() pairs per item
+  p.n_bands = (p.Lq + bwd_band_rows() - 1) / bwd_band_rows();
+  p.n_bins = p.rows / p.Lq * p.n_bands * p.Nc;
+  p.max_items = (p.rows * p.K + bwd_pairs_per_item() - 1) / bwd_pairs_per_item() + p.n_bins;
   if (!p.bf16) return HSA_ERR_UNSUPPORTED;
   const int64_t n_pairs = p.rows * p.K, n_bg = p.rows / p.Lq;
   // grid sizes: per-row kernels take (rows * G + rows) / 8 workgroups at most,
@@ -498,7 +504,8 @@ hsa_status_t backward_impl(const hsa_shape_t* shape, const void* q_ret, const vo
   c.partials = nullptr;
   c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
   c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
-  c.band_rows = hsa::chunk_band_rows(); c.n_bands = p.n_bands;
+  c.band_rows = hsa::bwd_band_rows(); c.n_bands = p.n_bands;
+  c.pairs_per_item = (int32_t)hsa::bwd_pairs_per_item();
   c.attn_scale = p.attn_scale; c.qk_norm = p.qk_norm ? 1 : 0;
   a.q_ret = q_ret; a.landmarks = lm; a.dout = dout;
   a.dq_ret = dq_ret; a.dlandmarks = dlandmarks; a.dq_attn = dq_attn; a.dk = dk; a.dv = dv;

@@ -105,6 +105,7 @@ struct ChunkArgs {
   __half* partials;       // [rows * K, G, D] weighted per-chunk outputs
   int64_t rows, Lq, Lkv, Nc, n_bins, max_items;
   int64_t band_rows, n_bands;   // bins split the query rows of a (batch, kv head) into bands
+  int32_t pairs_per_item;       // work item size, at most 128 pairs
   int32_t Hq, Hkv, K;
   float attn_scale;
   int32_t qk_norm;
@@ -169,8 +170,9 @@ int decode_slots_per_block();
 hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk);
 // Pair bucketing alone: weights, bin counts and offsets, work items, pair ids.
 hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st);
-int64_t chunk_pairs_per_item();
-int64_t chunk_band_rows();
+int64_t chunk_pairs_per_item();   // forward work items
+int64_t chunk_band_rows();        // forward bins
+int64_t bwd_band_rows();          // backward bins (each bin sortable in LDS)
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 
 }  // namespace hsa
