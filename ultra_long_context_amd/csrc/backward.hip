@@ -50,6 +50,40 @@ __global__ __launch_bounds__(256) void bin_sort_kernel(BwdArgs a) {
     }
     return;
   }
+  // larger bins: place every pair at its query row's offset inside the band
+  // (the pair ids of one bin differ in their row unless a row names the chunk
+  // in two slots), then compact in row order; a repeated row falls back to a
+  // bitonic sort
+  __shared__ uint32_t cnt[256];
+  __shared__ int dup;
+  const int64_t band = (bin / a.c.Nc) % a.c.n_bands, r0 = band * a.c.band_rows;
+  if (a.c.band_rows <= kSortCap) {
+    for (int i = threadIdx.x; i < kSortCap; i += 256) v[i] = 0xFFFFFFFFu;
+    if (threadIdx.x == 0) dup = 0;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n; i += 256) {
+      const uint32_t pid = a.c.pairs[o0 + i];
+      const int64_t r = ((int64_t)(pid / (uint32_t)a.c.K) / a.c.Hkv) % a.c.Lq;
+      if (atomicCAS(&v[r - r0], 0xFFFFFFFFu, pid) != 0xFFFFFFFFu) dup = 1;
+    }
+    __syncthreads();
+    if (!dup) {
+      constexpr int PER = kSortCap / 256;
+      uint32_t c = 0;
+#pragma unroll 8
+      for (int j = 0; j < PER; ++j) c += v[threadIdx.x * PER + j] != 0xFFFFFFFFu;
+      cnt[threadIdx.x] = c;
+      __syncthreads();
+      uint32_t base = 0;
+      for (uint32_t t = 0; t < threadIdx.x; ++t) base += cnt[t];
+      for (int j = 0; j < PER; ++j) {
+        const uint32_t x = v[threadIdx.x * PER + j];
+        if (x != 0xFFFFFFFFu) a.c.pairs[o0 + base++] = x;
+      }
+      return;
+    }
+    __syncthreads();
+  }
   int np = 1;
   while (np < (int)n) np <<= 1;
   for (int i = threadIdx.x; i < np; i += 256) v[i] = i < (int)n ? a.c.pairs[o0 + i] : 0xFFFFFFFFu;
