@@ -108,23 +108,23 @@ __global__ __launch_bounds__(256) void bin_sort_kernel(BwdArgs a) {
 
 // --- per work item ------------------------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
   constexpr int KROW = D + 8;               // K, V rows (bf16)
-  constexpr int TROW = kChunk + 8;          // K^T rows (permuted keys)
   constexpr int PROW = kChunk + 16;          // staged P, h rows [head-row][key]
   constexpr int QROW = D + 16;              // staged q, dO_w rows [head-row][dim]
   constexpr int PT = 16 / G;                // pairs per 16-head-row tile
   constexpr int KSTEP = D / 32, NT = D / 16;
+  constexpr int HR = 32;                    // head-rows staged per phase B round (2 tiles)
+  // under 80 KiB of LDS: two workgroups per CU
   __shared__ __align__(16) uint16_t ks[kChunk * KROW];
   __shared__ __align__(16) uint16_t vs[kChunk * KROW];
-  __shared__ __align__(16) uint16_t kt[D * TROW];
   __shared__ float rk[kChunk];
-  // phase B operands of the 64 head-rows of 4 tiles, row-major (read back
+  // phase B operands of 32 head-rows (2 tiles), row-major (read back
   // transposed): P and h [hr][key], dO_w and q [hr][dim]
-  __shared__ __align__(16) uint16_t ps[64 * PROW];
-  __shared__ __align__(16) uint16_t hs[64 * PROW];
-  __shared__ __align__(16) uint16_t ds_[64 * QROW];
-  __shared__ __align__(16) uint16_t qs[64 * QROW];
+  __shared__ __align__(16) uint16_t ps[HR * PROW];
+  __shared__ __align__(16) uint16_t hs[HR * PROW];
+  __shared__ __align__(16) uint16_t ds_[HR * QROW];
+  __shared__ __align__(16) uint16_t qs[HR * QROW];
   __shared__ uint32_t pid_s[kBP];
   __shared__ float w_s[kBP];
   __shared__ int64_t qoff_s[kBP];
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
     const int64_t qrow = (int64_t)(pid / (uint32_t)c.K) / c.Hkv;
     qoff_s[tid] = (qrow * c.Hq + (int64_t)g * G) * D;
   }
-  {  // K and V row-major, K^T with keys permuted inside 32-key blocks, key norms
+  {  // K and V row-major, key norms
     const int64_t base = (bg * c.Lkv + chunk * kChunk) * D;
     const uint16_t* kp = reinterpret_cast<const uint16_t*>(c.k) + base;
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(c.v) + base;
@@ -160,14 +160,6 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
       const uint4 vx = *reinterpret_cast<const uint4*>(vp + e);
       *reinterpret_cast<uint4*>(&ks[key * KROW + d0]) = kx;
       *reinterpret_cast<uint4*>(&vs[key * KROW + d0]) = vx;
-      const int kq = key & 31;
-      const int col = 32 * (key >> 5) + 8 * ((kq & 15) >> 2) + 4 * (kq >> 4) + (kq & 3);
-      const uint32_t wd[4] = {kx.x, kx.y, kx.z, kx.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        kt[(d0 + 2 * q) * TROW + col] = (uint16_t)(wd[q] & 0xFFFFu);
-        kt[(d0 + 2 * q + 1) * TROW + col] = (uint16_t)(wd[q] >> 16);
-      }
     }
   }
   __syncthreads();
@@ -219,6 +211,7 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
     const bool live = tile < n_tiles && pm < n_pairs;
     const float wp = live ? w_s[pm] : 0.f;
     bf16x8 qa[KSTEP], da[KSTEP];
+    uint4 qst[KSTEP], dst[KSTEP];             // this tile's q and dO_w rows for phase B
     float qss = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) {
@@ -237,9 +230,8 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
       }
       const uint4 dw = make_uint4(dw4[0], dw4[1], dw4[2], dw4[3]);
       da[t] = __builtin_bit_cast(bf16x8, dw);
-      // stage q and dO_w rows for phase B
-      *reinterpret_cast<uint4*>(&qs[(16 * w + ma) * QROW + 32 * t + 8 * jg]) = x;
-      *reinterpret_cast<uint4*>(&ds_[(16 * w + ma) * QROW + 32 * t + 8 * jg]) = dw;
+      qst[t] = x;
+      dst[t] = dw;
     }
     if (t0 + 4 < n_tiles) {   // next tile's rows, in flight during this one
       const int64_t off = tile_off(t0 + 4 + w);
@@ -312,6 +304,7 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
     }
     // g = attn dz |k|^-1 (for dqhat), h = attn dz |q|^-1 (for dkhat), dz = P (dP - pdp)
     bf16x8 gb[2];
+    uint2 pst[4], hst[4];                     // this tile's P and h rows for phase B
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       float hv[4];
@@ -321,23 +314,23 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
         hv[i] = dz * rq;
         gb[nt >> 1][4 * (nt & 1) + i] = (__bf16)(dz * rkl[nt][i]);
       }
-      // P and h rows of head-row 16w + ma, keys 16nt + 4jg .. +3
+      // P and h of head-row ma, keys 16nt + 4jg .. +3
       const bf16x2 p01 = {(__bf16)sv[nt][0], (__bf16)sv[nt][1]}, p23 = {(__bf16)sv[nt][2], (__bf16)sv[nt][3]};
       const bf16x2 h01 = {(__bf16)hv[0], (__bf16)hv[1]}, h23 = {(__bf16)hv[2], (__bf16)hv[3]};
-      *reinterpret_cast<uint2*>(&ps[(16 * w + ma) * PROW + 16 * nt + 4 * jg]) =
-          make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
-      *reinterpret_cast<uint2*>(&hs[(16 * w + ma) * PROW + 16 * nt + 4 * jg]) =
-          make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+      pst[nt] = make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
+      hst[nt] = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
     }
-    // dqhat^T = K^T g^T: lane holds dims 16*nt + 4*jg + i of head-row ma
+    // dqhat^T = K^T g^T: lane holds dims 16*nt + 4*jg + i of head-row ma.  The
+    // A operand K^T comes from the row-major keys by transpose loads, in the
+    // key order of g (keys 32st + 4jg + 0..3 and 32st + 16 + 4jg + 0..3)
     uint16_t* dq = a.dq_part + (live ? ((int64_t)pid_s[pm] * G + hd) * D : 0) + 4 * jg;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       floatx4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(&kt[(16 * nt + ma) * TROW + 32 * st + 8 * jg]);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), gb[st], o, 0, 0, 0);
+        const bf16x8 ka = lds_operand_tr2(ks, KROW, 32 * st + 4 * jg, 32 * st + 16 + 4 * jg, 16 * nt, ma);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, gb[st], o, 0, 0, 0);
       }
       if (live) {
         const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
@@ -346,13 +339,26 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
       }
       if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    // ---- phase B: keys 16w .. 16w+15 over the 64 staged head-rows ----------
-    // A = P^T / h^T (key x head-row), B = dO_w / q (head-row x dim), both read
-    // transposed from the row-major staging
+    // ---- phase B: keys 16w .. 16w+15 over the 4 tiles' head-rows, two tiles
+    // (32 head-rows) per round.  A = P^T / h^T (key x head-row), B = dO_w / q
+    // (head-row x dim), both read transposed from the row-major staging.
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int r0 = 32 * st + 8 * jg;
+    for (int half = 0; half < 2; ++half) {
+      if ((w >> 1) == half) {
+        const int r = 16 * (w & 1) + ma;
+#pragma unroll
+        for (int t = 0; t < KSTEP; ++t) {
+          *reinterpret_cast<uint4*>(&qs[r * QROW + 32 * t + 8 * jg]) = qst[t];
+          *reinterpret_cast<uint4*>(&ds_[r * QROW + 32 * t + 8 * jg]) = dst[t];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          *reinterpret_cast<uint2*>(&ps[r * PROW + 16 * nt + 4 * jg]) = pst[nt];
+          *reinterpret_cast<uint2*>(&hs[r * PROW + 16 * nt + 4 * jg]) = hst[nt];
+        }
+      }
+      __syncthreads();
+      const int r0 = 8 * jg;
       const bf16x8 pa = lds_operand_tr(ps, PROW, r0, 16 * w, ma);
       const bf16x8 ha = lds_operand_tr(hs, PROW, r0, 16 * w, ma);
 #pragma unroll
@@ -363,8 +369,8 @@ __global__ __launch_bounds__(256) void bwd_item_kernel(BwdArgs a) {
         dk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, qb, dk[nt], 0, 0, 0);
         if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   // item partials: lane holds keys 16w + 4*jg + i, dims 16*nt + ma
   float* pv = a.item_part + (int64_t)item_i * 2 * kChunk * D;
