@@ -28,7 +28,9 @@ MFMA FLOPs / 2.5 PFLOP/s); frac = t_roof / ms_per_step.
 cpu_baseline: the fp64 oracle on a bounded, stratified sample of query rows of the
 same workload, timed on this host's cores (test infrastructure, not the product).
 
-Further workloads (--workloads): global_32K (top-K covering all 512 chunks of the
+Further workloads (--workloads): chunked_1M (8,192 new rows appended to a
+1,048,576-token history, 32 q / 4 kv heads, top-K 32; HBM-bound: roofline in
+bytes), global_32K (top-K covering all 512 chunks of the
 32K window: global HSA), backward_32K (hsa_backward on the 32K window for the
 forward's selection; roofline on the per-item MFMA kernel, 10*G*64*d FLOP per
 selection), crossover (HSA forward vs dense causal SDPA from 4K to 1M tokens,
@@ -51,7 +53,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 VALU_FP32_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 FLOP (FMA) x 2.4 GHz, non-packed
 
-WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "global_32K": 1, "backward_32K": 1}
+WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "global_32K": 1, "backward_32K": 1, "chunked_1M": 4}
 # global_32K: the 32K training-window prefill with a top-K covering all 512
 # chunks (global HSA of the warm-up stage); the dense fused kernel runs it
 OVERRIDES = {"global_32K": dict(top_k=512, name="global_hsa_32K_gqa8")}
@@ -62,6 +64,11 @@ KERNELS = {
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
     ("decode_16M", "landmarks"): "chunk_landmark_kernel<true, 128>",
     ("global_32K", "attend"): "attend_global_kernel<128, 8>",
+    ("chunked_1M", "scan"): "scan_wide_kernel<true, 128>",
+    ("chunked_1M", "merge"): "merge_lists_kernel",
+    ("chunked_1M", "bucket"): "chunk_count/scan/scatter kernels",
+    ("chunked_1M", "attend"): "chunk_attend_kernel<128, 8>",
+    ("chunked_1M", "combine"): "chunk_combine_kernel<128, 8>",
     ("backward_32K", "bucket"): "chunk_count/scan/scatter + bin_sort kernels",
     ("backward_32K", "attend"): "bwd_item_kernel<128, 8>",
     ("backward_32K", "combine"): "bwd_row/bwd_chunk/bwd_landmark kernels",
@@ -199,7 +206,7 @@ def algorithmic(cfg, U, elem=2):
                 q_attn_bytes=qa, out_bytes=qa, kv_bytes=U * 2 * 64 * d * elem,
                 bytes=lm_bytes + q_ret + 2 * qa + U * 2 * 64 * d * elem,
                 scan_flops=2 * d * cand, attend_flops=4 * cfg.group * 64 * d * sel,
-                bwd_flops=10 * cfg.group * 64 * d * sel)
+                bwd_flops=10 * cfg.group * 64 * d * sel, partial_bytes=sel * cfg.group * d * 2)
 
 
 # source file of each kernel family; a kernel's traffic figure goes stale when
@@ -261,6 +268,9 @@ def roofline(workload, stage, ms, alg):
     elif stage == "combine" and workload.startswith("backward"):
         units = ("hbm", alg["bwd_combine_bytes"], "per-pair dq partials (G*d*4 B) + per-item dV, dk "
                  "partials (2*64*d*4 B) read, fp32 gradients written")
+    elif stage == "combine" and not workload.startswith("backward"):
+        units = ("hbm", alg["partial_bytes"] + alg["out_bytes"],
+                 "G*d*2 B fp16 partial per selection x %d + out" % alg["selections"])
     elif stage == "attend" and workload.startswith("global"):
         units = ("mfma", alg["attend_flops"] + alg["scan_flops"],
                  "4*G*64*d FLOP per (row, eligible chunk) x %d + 2*d per retrieval score x %d"
@@ -616,7 +626,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workloads", default="prefill_128K,decode_16M,global_32K,backward_32K")
+    ap.add_argument("--workloads", default="prefill_128K,decode_16M,chunked_1M,global_32K,backward_32K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the 1 GiB calibration copy first (for counter passes)")
@@ -657,7 +667,7 @@ def main():
         if not names:
             print(json.dumps(crossover), flush=True)
             return
-    for name in ["decode_16M", "global_32K", "backward_32K", "prefill_128K"]:
+    for name in ["decode_16M", "chunked_1M", "global_32K", "backward_32K", "prefill_128K"]:
         if name in names:
             results[name] = bench_workload(name, args.steps, args.warmup, timer,
                                            not args.no_cpu_baseline)

@@ -14,6 +14,11 @@ namespace {
 
 constexpr int64_t kRowsPerWave = 16;
 constexpr int64_t kMaxSplits = 512;    // wide scan: 1024 chunks x 512 splits
+// the block scan pays off with many rows per (batch, kv head) over a long
+// history (the wide scan re-reads the landmarks once per 16 rows)
+constexpr int64_t kBlockScanMinRows = 512;
+constexpr int64_t kBigItemPairs = INT64_C(1) << 22;   // (row, slot) pairs from which items hold 128
+constexpr int64_t kBlockScanMinChunks = 128;
 // The workspace starts with arrival counters that every call leaves at zero.
 constexpr size_t kCounterBytes = 16384;
 constexpr int64_t kScanCounters = 2048;     // counters [0, 2048): wide-scan row blocks
@@ -33,6 +38,7 @@ struct Plan {
   bool global;           // K covers every eligible chunk (K > 64): fused dense kernel
   int32_t attn_splits, slots_per_split, attn_mode;
   int64_t n_bins, max_items, n_bands;   // chunk-major attend
+  int32_t pairs_per_item;
   size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
   size_t off_ccounts, off_coffsets, off_ccursor, off_citems, off_cnitems, off_cpairs, off_cwts,
       off_cparts, off_cseg;
@@ -96,16 +102,22 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool
     p->total = kCounterBytes;
     return HSA_OK;
   }
-  // Scan plan.  Up to 2048 row blocks of 16 rows: the wide kernel (1024 chunks
-  // per workgroup; with several splits a merge combines the per-split lists).
-  // More row blocks than that: bf16 with K <= 32 takes the block kernel (64
-  // rows per workgroup over all their chunks); otherwise one wave per 16 rows.
+  // Scan plan.  bf16 with K <= 32, at least kBlockScanMinRows rows per
+  // (batch, kv head) and kBlockScanMinChunks eligible chunks: the block kernel
+  // (64 rows per workgroup over all their chunks).  Otherwise up to 2048 row blocks of 16 rows: the wide kernel (1024
+  // chunks per workgroup; with several splits a merge combines the per-split
+  // lists); beyond that the block kernel where it applies, else one wave per
+  // 16 rows.
   const int64_t row_blocks = (s->q_len + kRowsPerWave - 1) / kRowsPerWave * s->batch * s->n_kv_heads;
   if (row_blocks > INT32_MAX) return HSA_ERR_BAD_SHAPE;
   const int64_t wchunks = 1024;
   const int64_t wsplits = std::max<int64_t>(1, (nmax + wchunks - 1) / wchunks);
-  p->wide = row_blocks <= kScanCounters && wsplits <= kMaxSplits;
-  p->block = !p->wide && p->bf16 && p->K <= scan_block_max_k();
+  // many rows per (batch, kv head) in bf16 with K <= 32: the block scan (each
+  // landmark tile read once per 64 rows); few rows: the wide scan
+  const bool block_ok = p->bf16 && p->K <= scan_block_max_k();
+  p->block = block_ok && s->q_len >= kBlockScanMinRows && nmax >= kBlockScanMinChunks;
+  p->wide = !p->block && row_blocks <= kScanCounters && wsplits <= kMaxSplits;
+  p->block = p->block || (!p->wide && block_ok);
   p->split_len = (int32_t)(p->wide ? wchunks : std::max<int64_t>(64, (nmax + 63) / 64 * 64));
   p->n_splits = (int32_t)(p->wide ? wsplits : 1);
 
@@ -116,7 +128,10 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool
   p->n_bands = (s->q_len + chunk_band_rows() - 1) / chunk_band_rows();
   p->n_bins = (int64_t)s->batch * s->n_kv_heads * p->n_bands * Nc;
   const int64_t n_pairs = p->rows * p->K;
-  p->max_items = (n_pairs + chunk_pairs_per_item() - 1) / chunk_pairs_per_item() + p->n_bins;
+  // large problems: 128-pair items (K and V staged half as often); smaller ones
+  // keep 64-pair items so the items still fill the GPU
+  p->pairs_per_item = n_pairs >= kBigItemPairs ? (int32_t)chunk_pairs_per_item() : 64;
+  p->max_items = (n_pairs + p->pairs_per_item - 1) / p->pairs_per_item + p->n_bins;
   if (p->rows < 1024 && p->bf16) {
     p->attn_mode = 3;
     p->attn_splits = (p->K + decode_slots_per_block() - 1) / decode_slots_per_block();
@@ -254,7 +269,7 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
     c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
     c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
     c.band_rows = chunk_band_rows(); c.n_bands = p.n_bands;
-    c.pairs_per_item = (int32_t)chunk_pairs_per_item();
+    c.pairs_per_item = p.pairs_per_item;
     c.attn_scale = p.attn_scale; c.qk_norm = p.qk_norm ? 1 : 0;
     return launch_attend_chunk(c, p.D, p.G, st, mk) == hipSuccess ? HSA_OK : HSA_ERR_DEVICE;
   }

@@ -170,7 +170,7 @@ int decode_slots_per_block();
 hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st, const Marks& mk);
 // Pair bucketing alone: weights, bin counts and offsets, work items, pair ids.
 hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st);
-int64_t chunk_pairs_per_item();   // forward work items
+int64_t chunk_pairs_per_item();   // forward work items of large problems (else 64)
 int64_t chunk_band_rows();        // forward bins
 int64_t bwd_band_rows();          // backward bins (each bin sortable in LDS)
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
