@@ -296,7 +296,9 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
     const float rq_mine = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
     float rk[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) rk[nt] = (a.qk_norm ? 1.0f / fmaxf(sqrtf(kss[nt]), 1e-6f) : 1.0f) * a.attn_scale;
+    // logits in base 2: log2(e) folded into the key factor
+    for (int nt = 0; nt < 4; ++nt)
+      rk[nt] = (a.qk_norm ? 1.0f / fmaxf(sqrtf(kss[nt]), 1e-6f) : 1.0f) * a.attn_scale * 1.4426950408889634f;
     // S = Q K^T: lane holds S[4*jg + i][16*nt + ma]
     floatx4 s[4];
 #pragma unroll
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
       float sum = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        x[nt] = expf(x[nt] - mx);
+        x[nt] = __builtin_amdgcn_exp2f(x[nt] - mx);
         sum += x[nt];
       }
       sum += dpp_f<0xB1>(sum);
