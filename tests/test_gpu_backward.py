@@ -210,3 +210,23 @@ def test_backward_duplicate_slots(hsa):
         idx[0, ::7, 0, 1] = idx[0, ::7, 0, 0]
 
     full_parity(hsa, cfg, edit)
+
+
+def test_backward_profiled_matches(hsa):
+    """hsa_backward_profiled gives the gradients of hsa_backward bit for bit and
+    records its bucket, attend and combine stages."""
+    import torch
+    cfg = small(q_len=512)
+    inp = W.generate(cfg)
+    idx, sc = selection(inp)
+    dout = W.cotangent(cfg)
+    dev = inputs_to_device(inp)
+    ti, ts, td = torch.from_numpy(idx).cuda(), torch.from_numpy(sc).cuda(), to_device(dout, "bf16")
+    a = hsa.backward(*dev, ti, ts, td)
+    evs = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in hsa.STAGES}
+    b = hsa.backward(*dev, ti, ts, td, stage_events=evs)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    for n in ("bucket", "attend", "combine"):
+        assert evs[n][0].elapsed_time(evs[n][1]) > 0, n

@@ -256,6 +256,25 @@ def test_deterministic(hsa):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("cfg_i,kw", [(3, dict(kv_len=1 << 18)), (1, dict(q_len=4096, kv_len=8192)),
+                                      (2, dict(q_len=2048, kv_len=2048))])
+def test_profiled_forward_matches_and_records_stages(hsa, cfg_i, kw):
+    """hsa_forward_profiled gives the outputs of hsa_forward bit for bit and
+    records an event pair around every stage its plan runs."""
+    import torch
+    cfg = W.shrink(W.CONFIGS[cfg_i], **kw)
+    inp = W.generate(cfg)
+    dev = inputs_to_device(inp)
+    a = hsa.forward(*dev, q_pos0=cfg.q_pos0, top_k=cfg.top_k, return_topk=True)
+    evs = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in hsa.STAGES}
+    b = hsa.forward(*dev, q_pos0=cfg.q_pos0, top_k=cfg.top_k, return_topk=True, stage_events=evs)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert evs["scan"][0].elapsed_time(evs["scan"][1]) > 0
+    assert evs["attend"][0].elapsed_time(evs["attend"][1]) > 0
+
+
 # ----------------------------------------------------------------------------
 # the two halves through their own entry points
 # ----------------------------------------------------------------------------
