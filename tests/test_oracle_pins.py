@@ -159,7 +159,7 @@ def test_causality_future_chunks_do_not_matter():
 
 @pytest.mark.parametrize("qk_norm", [True, False])
 def test_k1_equals_dense_sdpa_over_chosen_chunk(qk_norm):
-    """The benchmark spec invariant: K = 1 gives dense softmax attention over the chosen
+    """Invariant: K = 1 gives dense softmax attention over the chosen
     chunk.  Reference: torch SDPA.  Catches missing/extra normalisation, wrong
     scale, K/V transposed or read from the wrong chunk/head."""
     cfg = small_cfg(top_k=1, n_q_heads=4, n_kv_heads=2, batch=2, qk_norm=qk_norm)
@@ -183,7 +183,7 @@ def test_k1_equals_dense_sdpa_over_chosen_chunk(qk_norm):
 
 
 def test_uniform_scores_give_mean_of_chunk_attentions():
-    """The benchmark spec invariant: uniform retrieval scores and K >= #chunks give the mean
+    """Invariant: uniform retrieval scores and K >= #chunks give the mean
     of the per-chunk attentions (reference: torch SDPA per chunk)."""
     cfg = small_cfg(top_k=8, n_q_heads=2)
     inp = W.generate(cfg, seed=8)
@@ -201,7 +201,7 @@ def test_uniform_scores_give_mean_of_chunk_attentions():
 
 
 def test_weights_sum_to_one_and_follow_scores():
-    """The benchmark spec invariant: blend weights sum to 1; larger score => larger weight."""
+    """Invariant: blend weights sum to 1; larger score => larger weight."""
     cfg = W.shrink(W.CONFIGS[1], q_len=2048, kv_len=2048)
     inp = W.generate(cfg)
     rows = np.arange(64, 2048, 97)
