@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs a) {
       const int k = k0 + e < K ? k0 + e : K - 1;
       const int32_t c = a.idx[row * K + k];
       ok[e] = k0 + e < K && c >= 0 && (int64_t)c < a.Nc;
-      u[e] = *reinterpret_cast<const uint4*>(&a.partials[((row * K + k) * G + h) * D + 8 * j]);
+      u[e] = load_stream(reinterpret_cast<const uint4*>(&a.partials[((row * K + k) * G + h) * D + 8 * j]));
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

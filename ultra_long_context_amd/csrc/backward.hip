@@ -406,8 +406,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float* pv = a.item_part + (int64_t)min(it + u, i1 - 1) * 2 * kChunk * D + poff;
-        v4[u] = *reinterpret_cast<const float4*>(pv);
-        k4[u] = *reinterpret_cast<const float4*>(pv + kChunk * D);
+        v4[u] = load_stream(reinterpret_cast<const float4*>(pv));
+        k4[u] = load_stream(reinterpret_cast<const float4*>(pv + kChunk * D));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, uint32_t n_attn)
         const int k = min(k0 + e, K - 1);
         const int32_t ci = c.idx[row * K + k];
         ok[e] = k0 + e < K && ci >= 0 && (int64_t)ci < c.Nc;
-        v[e] = *reinterpret_cast<const uint2*>(a.dq_part + ((row * K + k) * G + hd) * D + x4);
+        v[e] = load_stream(reinterpret_cast<const uint2*>(a.dq_part + ((row * K + k) * G + hd) * D + x4));
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)

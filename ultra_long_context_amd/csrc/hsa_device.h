@@ -14,6 +14,23 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming loads for data read exactly once (partials of a reduction): the
+// lines are not kept in the caches for reuse.
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3]));
+}
 
 // ---------------------------------------------------------------------------
 // element conversion
