@@ -9,8 +9,11 @@ Workloads (synthetic, seeded; shapes of the paper's setting):
 A step is one hsa_forward call (landmark scan, top-K, per-chunk attention, blend)
 over the whole batch, inputs resident in HBM.  Each step is preceded, outside its
 HIP-event window, by a 1 GiB read that evicts L2 and the 256 MB Infinity Cache,
-so every step starts cold.  ms_per_step is the mean event-timed step; the wall
-time of the whole timed region (flushes included) is reported as wall_ms_per_step.
+so every step starts cold.  ms_per_step is the mean event-timed step (the
+call's kernel launches made directly; median, p10 and p90 beside it); the wall
+time of the whole timed region (flushes included) is wall_ms_per_step, the same
+step without the flush warm_ms_per_step, and the step replayed from a captured
+HIP graph (checked bit for bit against the direct call) graph_ms_per_step.
 
 roofline: a second pass of `steps` cold forwards has the library record HIP events
 around each kernel stage on the launch stream (hsa_forward_profiled); the stage
@@ -93,14 +96,17 @@ def to_dev(a, dtype):
 
 
 class Timer:
-    """Cold-cache timing of a captured HIP graph with HIP events.
+    """Cold-cache timing of one call (all its kernels) with HIP events.
 
     Each step enqueues a 1 GiB read of an unrelated buffer (evicting L2 and the
     256 MB Infinity Cache with clean lines; a write would leave dirty lines whose
-    write-back competes with the timed step), then event e0, the graph replay,
-    event e1.  The read keeps the GPU busy while the host enqueues e0 and the
-    replay, so the events bracket GPU work only.  Events live on torch's current
-    stream, which is the stream the library launches on."""
+    write-back competes with the timed step), then event e0, the call (its
+    kernel launches, or a captured graph's replay), event e1.  The read keeps
+    the GPU busy while the host enqueues e0 and the call, so the events bracket
+    GPU work only.  Events live on torch's current stream, which is the stream
+    the library launches on.  On ROCm a graph replay starts its first kernel
+    several microseconds later than the same launches made directly, which
+    shows on steps of tens of microseconds."""
 
     def __init__(self):
         import torch
@@ -137,20 +143,31 @@ class Timer:
         return g
 
     def time(self, graph, steps, flush=True):
+        """Graph replays: (mean, median, wall) ms."""
+        m = self.time_eager(graph.replay, steps, flush)
+        return m["mean"], m["median"], m["wall"]
+
+    def time_eager(self, fn, steps, flush=True):
+        """`steps` calls of fn() (each enqueues one step), each bracketed by
+        events, after the cache-evicting read when flush.  Returns mean,
+        median, p10, p90 of the event times and the host wall time per step,
+        all in ms."""
         torch = self.torch
         evs = self.events(steps)
+        self.cold()                        # the flush's first launch after a capture is slow on the host
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e0, e1 in evs:
             if flush:
                 self.cold()
             e0.record()
-            graph.replay()
+            fn()
             e1.record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
         ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-        return float(np.mean(ms)), float(np.median(ms)), wall * 1e3
+        return dict(mean=float(np.mean(ms)), median=float(np.median(ms)), p10=float(np.percentile(ms, 10)),
+                    p90=float(np.percentile(ms, 90)), wall=wall * 1e3)
 
 
     def stages(self, call, steps):
@@ -335,9 +352,12 @@ def bench_backward(name, cfg, steps, warmup, timer, cpu_baseline):
     if not all(torch.equal(a, b) for a, b in zip(grads, eager)):
         raise RuntimeError("graph replay differs from the eager backward")
     log("[bench] %s: warmup done, graph replay matches eager bit for bit" % name)
-    ms_mean, ms_med, wall_ms = timer.time(g_step, steps)
-    log("[bench] %s: %.4f ms/step (median %.4f, wall incl. flush %.3f)" % (name, ms_mean, ms_med, wall_ms))
-    warm_mean, _, _ = timer.time(g_step, steps, flush=False)
+    tm = timer.time_eager(step, steps)
+    ms_mean, ms_med, wall_ms = tm["mean"], tm["median"], tm["wall"]
+    graph_ms, _, _ = timer.time(g_step, steps)
+    log("[bench] %s: %.4f ms/step (median %.4f, p10 %.4f, p90 %.4f, wall incl. flush %.3f; graph replay %.4f)" % (
+        name, ms_mean, ms_med, tm["p10"], tm["p90"], wall_ms, graph_ms))
+    warm_mean = timer.time_eager(step, steps, flush=False)["mean"]
     stage_ms = timer.stages(lambda evs: hsa.backward(q_ret, lm, q_attn, k, v, idx, sc, dout, out=grads,
                                                      stage_events=evs), steps)
     log("[bench] %s: kernel stages (ms) %s" % (name, json.dumps(stage_ms)))
@@ -355,8 +375,8 @@ def bench_backward(name, cfg, steps, warmup, timer, cpu_baseline):
                         + idx.numel() * 8 + grads_bytes)
     qtok = cfg.batch * cfg.q_len
     res = dict(workload=name, config=cfg, value=qtok / (ms_mean / 1e3), ms_per_step=ms_mean,
-               ms_median=ms_med, wall_ms_per_step=wall_ms, warm_ms_per_step=warm_mean,
-               stage_ms=stage_ms, alg=alg, U=U)
+               ms_median=ms_med, ms_p10=tm["p10"], ms_p90=tm["p90"], wall_ms_per_step=wall_ms,
+               warm_ms_per_step=warm_mean, graph_ms_per_step=graph_ms, stage_ms=stage_ms, alg=alg, U=U)
     dom = max(stage_ms, key=stage_ms.get)
     res["roofline"] = roofline(name, dom, stage_ms[dom], alg)
     res["hbm_frac_whole_step"] = (alg["bwd_bytes"] / 8e12) / (ms_mean / 1e3)
@@ -401,7 +421,7 @@ def bench_crossover(steps, warmup, timer, lengths=CROSSOVER_LENGTHS):
     memory-efficient backend only) on the 32K training window's head layout
     (B=1, 8 q heads / 1 kv head, d=128, top-K 8) at growing L = Lq = Lkv.
     Inputs: seeded N(0,1) bf16 drawn on the GPU; landmarks = chunk means
-    (hsa_chunk_landmarks).  Each side is a captured graph timed cold."""
+    (hsa_chunk_landmarks).  Each side is timed cold as direct calls."""
     import torch
     import torch.nn.functional as F
     from torch.nn.attention import SDPBackend, sdpa_kernel
@@ -422,7 +442,7 @@ def bench_crossover(steps, warmup, timer, lengths=CROSSOVER_LENGTHS):
 
         for _ in range(warmup):
             hsa_step()
-        hsa_ms, _, _ = timer.time(timer.capture(hsa_step), steps)
+        hsa_ms = timer.time_eager(hsa_step, steps)["mean"]
         # dense comparator: [B, H, L, d] with the kv head repeated for the 8 q heads
         qd = q_attn.permute(0, 2, 1, 3).contiguous()
         kd = k.expand(1, 8, L, 128).contiguous()
@@ -437,7 +457,7 @@ def bench_crossover(steps, warmup, timer, lengths=CROSSOVER_LENGTHS):
                     for _ in range(warmup):
                         dense_step()
                     torch.cuda.synchronize()
-                    dense_ms, _, _ = timer.time(timer.capture(dense_step), steps)
+                    dense_ms = timer.time_eager(dense_step, steps)["mean"]
                 backend = be.name.lower()
                 break
             except RuntimeError as e:
@@ -489,9 +509,12 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
     if not torch.equal(out, eager):
         raise RuntimeError("graph replay differs from the eager forward")
     log("[bench] %s: warmup done, graph replay matches eager" % name)
-    ms_mean, ms_med, wall_ms = timer.time(g_step, steps)
-    log("[bench] %s: %.4f ms/step (median %.4f, wall incl. flush %.3f)" % (name, ms_mean, ms_med, wall_ms))
-    warm_mean, _, _ = timer.time(g_step, steps, flush=False)
+    tm = timer.time_eager(step, steps)
+    ms_mean, ms_med, wall_ms = tm["mean"], tm["median"], tm["wall"]
+    graph_ms, _, _ = timer.time(g_step, steps)
+    log("[bench] %s: %.4f ms/step (median %.4f, p10 %.4f, p90 %.4f, wall incl. flush %.3f; graph replay %.4f)" % (
+        name, ms_mean, ms_med, tm["p10"], tm["p90"], wall_ms, graph_ms))
+    warm_mean = timer.time_eager(step, steps, flush=False)["mean"]
 
     # per-kernel timing: the same forward, cold, with HIP events recorded by the
     # library around each kernel stage on the launch stream
@@ -511,8 +534,8 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
 
     qtok = cfg.batch * cfg.q_len
     res = dict(workload=name, config=cfg, value=qtok / (ms_mean / 1e3), ms_per_step=ms_mean,
-               ms_median=ms_med, wall_ms_per_step=wall_ms, warm_ms_per_step=warm_mean,
-               stage_ms=stage_ms, alg=alg, U=U)
+               ms_median=ms_med, ms_p10=tm["p10"], ms_p90=tm["p90"], wall_ms_per_step=wall_ms,
+               warm_ms_per_step=warm_mean, graph_ms_per_step=graph_ms, stage_ms=stage_ms, alg=alg, U=U)
     dom = max(stage_ms, key=stage_ms.get)
     res["roofline"] = roofline(name, dom, stage_ms[dom], alg)
     res["hbm_frac_whole_step"] = (alg["bytes"] / 8e12) / (ms_mean / 1e3)
@@ -521,7 +544,7 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
         # KV-cache maintenance beside the step: every chunk-mean landmark of the
         # history rebuilt from K (hsa_chunk_landmarks), an HBM stream
         lm_buf = torch.empty_like(lm)
-        lm_ms, _, _ = timer.time(timer.capture(lambda: hsa.chunk_landmarks(k, out=lm_buf)), steps)
+        lm_ms = timer.time_eager(lambda: hsa.chunk_landmarks(k, out=lm_buf), steps)["mean"]
         nbytes = k.numel() * k.element_size() + lm_buf.numel() * lm_buf.element_size()
         gbs = nbytes / (lm_ms / 1e3) / 1e9
         res["landmark_rebuild"] = dict(kernel=KERNELS[(name, "landmarks")], chunks=cfg.batch * cfg.n_kv_heads * cfg.n_chunks,
@@ -687,7 +710,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": cfg_dict(cfg),
         "roofline": m["roofline"],
+        "ms_median": m["ms_median"], "ms_p10": m["ms_p10"], "ms_p90": m["ms_p90"],
         "wall_ms_per_step": m["wall_ms_per_step"], "warm_ms_per_step": m["warm_ms_per_step"],
+        "graph_ms_per_step": m["graph_ms_per_step"],
         "hbm_frac_whole_step": m["hbm_frac_whole_step"],
         "step_roofline": m["step_roofline"],
         "stage_ms": m["stage_ms"],
@@ -697,8 +722,8 @@ def main():
     for name, r in results.items():
         if name == main_name:
             continue
-        sub = {k: r[k] for k in ("value", "ms_per_step", "ms_median", "wall_ms_per_step",
-                                 "warm_ms_per_step", "roofline", "hbm_frac_whole_step", "step_roofline",
+        sub = {k: r[k] for k in ("value", "ms_per_step", "ms_median", "ms_p10", "ms_p90", "wall_ms_per_step",
+                                 "warm_ms_per_step", "graph_ms_per_step", "roofline", "hbm_frac_whole_step", "step_roofline",
                                  "landmark_rebuild") if k in r}
         sub["unit"] = "query-tokens/s"
         sub["config"] = cfg_dict(r["config"])
