@@ -623,45 +623,54 @@ __device__ __forceinline__ int block_cut(uint64_t* row, int K, int jq, uint64_t&
   return m;
 }
 
-// One pass of a block-scan workgroup over its landmark tiles: tile t + 1 is
-// loaded into registers while tile t is scored from LDS.  fn(sub-tile scores,
-// sub-tile, first chunk, whole sub-tile eligible for every row of the wave).
+// Landmark tile (kTile chunks from c_first) into LDS with direct global->LDS
+// loads (global_load_lds_dwordx4): one wave operation moves 64 x 16 bytes to
+// 1 KiB of consecutive LDS, so rows are unpadded and their 16-byte units are
+// XOR-swizzled by row (unit u of row r sits in slot u ^ (r % RU)), which keeps
+// the MFMA operand reads of 16 consecutive rows on distinct banks.  Chunks at
+// or past c_stop load chunk 0 (scores masked by the caller).
+template <int D>
+__device__ __forceinline__ void tile_to_lds(const uint16_t* lm, int c_first, int c_stop, uint16_t* dst,
+                                            int w, int lane) {
+  constexpr int RU = D / 8;                       // 16-byte units per landmark
+  constexpr int OPS = kTile * RU / kWave / kBlkWaves;   // wave operations per wave
+#pragma unroll
+  for (int i = 0; i < OPS; ++i) {
+    const int op = w * OPS + i;
+    const int r = op * (kWave / RU) + lane / RU;  // tile row
+    const int u = (lane % RU) ^ (r % RU);         // global unit stored in this lane's slot
+    const int c = c_first + r;
+    const uint16_t* src = lm + (int64_t)(c < c_stop ? c : 0) * D + 8 * u;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(dst + op * (kWave * 8)),
+                                     16, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(0): this wave's direct-to-LDS loads have landed.
+__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One pass of a block-scan workgroup over its landmark tiles.  Two LDS tile
+// buffers (distinct arrays, so the compiler can tell the in-flight copy into
+// one from the reads of the other): tile t + 1 streams into the idle buffer
+// while tile t is scored.  fn(sub-tile scores, sub-tile, first chunk, whole
+// sub-tile eligible for every row of the wave).
 template <int D, bool kUnrollSub, class F>
 __device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int n_tiles, int w_stop,
-                                            int w_min, uint16_t (*lmt)[kTile * (D + 8)],
-                                            const QOperand<true, D>& q, int tid, int qrow, int j, F&& fn) {
-  constexpr int LROW = D + 8;
-  constexpr int RU = D / 8;              // 16-byte units per landmark
-  constexpr int NU = kTile * RU / 256;   // 16-byte tile loads per thread
+                                            int w_min, uint16_t* lmA, uint16_t* lmB,
+                                            const QOperand<true, D>& q, int w, int lane, int qrow, int j,
+                                            F&& fn) {
+  constexpr int RU = D / 8;
   constexpr int KSTEP = D / 32;
-  uint4 pre[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {         // chunks past c_stop: scores masked
-    const int qi = tid * NU + u, c0 = qi / RU;
-    pre[u] = *reinterpret_cast<const uint4*>(lm + (int64_t)(c0 < c_stop ? c0 : 0) * D + (qi % RU) * 8);
-  }
-  if (n_tiles > 0) {
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int qi = tid * NU + u;
-      *reinterpret_cast<uint4*>(&lmt[0][(qi / RU) * LROW + (qi % RU) * 8]) = pre[u];
-    }
-  }
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const bool more = t + 1 < n_tiles;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int qi = tid * NU + u, c0 = (t + 1) * kTile + qi / RU;
-      pre[u] = *reinterpret_cast<const uint4*>(lm + (int64_t)(c0 < c_stop ? c0 : 0) * D + (qi % RU) * 8);
-    }
-    const uint16_t* L = lmt[t & 1];
+  if (n_tiles <= 0) return;                       // uniform over the workgroup
+  auto score = [&](const uint16_t* L, int t) __attribute__((always_inline)) {
     auto sub_tile = [&](int sub) __attribute__((always_inline)) {
       const int cs = t * kTile + 16 * sub;
+      const int r = 16 * sub + qrow;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KSTEP; ++k) {
-        const uint4 x = *reinterpret_cast<const uint4*>(L + (16 * sub + qrow) * LROW + 32 * k + 8 * j);
+        const uint4 x = *reinterpret_cast<const uint4*>(L + r * D + 8 * ((4 * k + j) ^ (r % RU)));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), q.v[k], acc, 0, 0, 0);
       }
       fn(acc, sub, cs, cs + 16 <= w_min);
@@ -679,23 +688,31 @@ __device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int 
         sub_tile(sub);
       }
     }
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int qi = tid * NU + u;
-        *reinterpret_cast<uint4*>(&lmt[(t + 1) & 1][(qi / RU) * LROW + (qi % RU) * 8]) = pre[u];
-      }
-    }
+  };
+  tile_to_lds<D>(lm, 0, c_stop, lmA, w, lane);
+  wait_tile();
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_to_lds<D>(lm, (t + 1) * kTile, c_stop, lmB, w, lane);   // past the end: chunk 0, unused
+    score(lmA, t);
+    wait_tile();
+    __syncthreads();
+    if (t + 1 >= n_tiles) break;
+    tile_to_lds<D>(lm, (t + 2) * kTile, c_stop, lmA, w, lane);
+    score(lmB, t + 1);
+    wait_tile();
     __syncthreads();
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
-  __shared__ __align__(16) uint16_t lmt[2][kTile * (D + 8)];   // landmark tiles, 16-byte row pad
+  __shared__ __align__(16) uint16_t lmA[kTile * D];   // landmark tiles (swizzled rows)
+  __shared__ __align__(16) uint16_t lmB[kTile * D];
   __shared__ uint64_t buf[kBlkWaves][kRows * kBlkStride];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index as a scalar (LDS copy base)
   const int qrow = lane & 15, j = lane >> 4;     // MFMA layout
   const int rq = lane >> 2, jq = lane & 3;       // quad layout
   // consecutive workgroups: the same row block of successive (batch, kv head)
@@ -725,10 +742,10 @@ __global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
   const int K = a.K;
 
   auto sweep1 = [&](auto&& fn) __attribute__((always_inline)) {
-    block_sweep<D, true>(lm, c_stop, n_tiles, w_stop, w_min, lmt, q, tid, qrow, j, fn);
+    block_sweep<D, true>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
   };
   auto sweep2 = [&](auto&& fn) __attribute__((always_inline)) {
-    block_sweep<D, false>(lm, c_stop, n_tiles, w_stop, w_min, lmt, q, tid, qrow, j, fn);
+    block_sweep<D, false>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
   };
 
   // --- pass 1: group maxima, then a lower bound of each row's K-th key -------
