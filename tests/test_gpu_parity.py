@@ -351,6 +351,21 @@ def test_block_scan_ties_exact(hsa):
     parity(hsa, inp, rows=sample_rows(cfg, 150), exact=True, ret_scale=0.125)
 
 
+@pytest.mark.parametrize("mode,K", [("grid_small", 32), ("normal", 8)])
+def test_block_scan_small_tiles(hsa, mode, K):
+    """Block scan with at least 3072 workgroups: 32-chunk landmark tiles, three
+    workgroups per CU (the 128K prefill launch).  Ragged rows and history;
+    integer-valued scores full of ties compared exactly."""
+    cfg = small(batch=1, n_kv_heads=8, n_q_heads=8, q_len=24600, q_pos0=45, kv_len=24700, top_k=K,
+                head_dim=64)
+    inp = W.generate(cfg, mode=mode)
+    rows = np.union1d(sample_rows(cfg, 150, seed=K), np.arange(0, 130, 9))
+    if mode == "grid_small":
+        parity(hsa, inp, rows=rows, exact=True, ret_scale=0.125)
+    else:
+        parity(hsa, inp, rows=rows)
+
+
 # ----------------------------------------------------------------------------
 # full workload sizes, in the launch configuration bench.py times; the oracle
 # checks sampled rows (all 16 rows for the decode workload)

@@ -516,7 +516,7 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kBlkWaves = 4;
 constexpr int kBlkRows = kBlkWaves * kRows;     // query rows per workgroup
-constexpr int kTile = 64;                       // chunks per LDS tile
+constexpr int kTileMax = 64;                    // chunks per LDS tile: 64, or 32 with 3 workgroups per CU
 constexpr int kBlkCap = 64;                     // candidate slots per row
 constexpr int kBlkStride = kBlkCap + 1;         // padded: a wave's 16 rows start on different banks
 constexpr int kBlkMaxK = 32;                    // a cut leaves >= 32 free slots
@@ -623,17 +623,17 @@ __device__ __forceinline__ int block_cut(uint64_t* row, int K, int jq, uint64_t&
   return m;
 }
 
-// Landmark tile (kTile chunks from c_first) into LDS with direct global->LDS
+// Landmark tile (TILE chunks from c_first) into LDS with direct global->LDS
 // loads (global_load_lds_dwordx4): one wave operation moves 64 x 16 bytes to
 // 1 KiB of consecutive LDS, so rows are unpadded and their 16-byte units are
 // XOR-swizzled by row (unit u of row r sits in slot u ^ (r % RU)), which keeps
 // the MFMA operand reads of 16 consecutive rows on distinct banks.  Chunks at
 // or past c_stop load chunk 0 (scores masked by the caller).
-template <int D>
+template <int D, int TILE>
 __device__ __forceinline__ void tile_to_lds(const uint16_t* lm, int c_first, int c_stop, uint16_t* dst,
                                             int w, int lane) {
   constexpr int RU = D / 8;                       // 16-byte units per landmark
-  constexpr int OPS = kTile * RU / kWave / kBlkWaves;   // wave operations per wave
+  constexpr int OPS = TILE * RU / kWave / kBlkWaves;    // wave operations per wave
 #pragma unroll
   for (int i = 0; i < OPS; ++i) {
     const int op = w * OPS + i;
@@ -655,7 +655,7 @@ __device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // one from the reads of the other): tile t + 1 streams into the idle buffer
 // while tile t is scored.  fn(sub-tile scores, sub-tile, first chunk, whole
 // sub-tile eligible for every row of the wave).
-template <int D, bool kUnrollSub, class F>
+template <int D, int TILE, bool kUnrollSub, class F>
 __device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int n_tiles, int w_stop,
                                             int w_min, uint16_t* lmA, uint16_t* lmB,
                                             const QOperand<true, D>& q, int w, int lane, int qrow, int j,
@@ -663,9 +663,11 @@ __device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int 
   constexpr int RU = D / 8;
   constexpr int KSTEP = D / 32;
   if (n_tiles <= 0) return;                       // uniform over the workgroup
-  auto score = [&](const uint16_t* L, int t) __attribute__((always_inline)) {
+  // vbase: with 32-chunk tiles the sub-tiles of odd tiles are numbered 2, 3,
+  // so fn always sees the four 16-chunk sub-tiles of 64 chunks as 0..3
+  auto score = [&](const uint16_t* L, int t, int vbase) __attribute__((always_inline)) {
     auto sub_tile = [&](int sub) __attribute__((always_inline)) {
-      const int cs = t * kTile + 16 * sub;
+      const int cs = t * TILE + 16 * sub;
       const int r = 16 * sub + qrow;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -673,42 +675,42 @@ __device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int 
         const uint4 x = *reinterpret_cast<const uint4*>(L + r * D + 8 * ((4 * k + j) ^ (r % RU)));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), q.v[k], acc, 0, 0, 0);
       }
-      fn(acc, sub, cs, cs + 16 <= w_min);
+      fn(acc, vbase + sub, cs, cs + 16 <= w_min);
     };
     if constexpr (kUnrollSub) {          // fn indexes registers by sub-tile
 #pragma unroll
-      for (int sub = 0; sub < kTile / 16; ++sub) {
-        if (t * kTile + 16 * sub >= w_stop) break;
+      for (int sub = 0; sub < TILE / 16; ++sub) {
+        if (t * TILE + 16 * sub >= w_stop) break;
         sub_tile(sub);
       }
     } else {                             // fn is large: one copy of it
 #pragma unroll 1
-      for (int sub = 0; sub < kTile / 16; ++sub) {
-        if (t * kTile + 16 * sub >= w_stop) break;
+      for (int sub = 0; sub < TILE / 16; ++sub) {
+        if (t * TILE + 16 * sub >= w_stop) break;
         sub_tile(sub);
       }
     }
   };
-  tile_to_lds<D>(lm, 0, c_stop, lmA, w, lane);
+  tile_to_lds<D, TILE>(lm, 0, c_stop, lmA, w, lane);
   wait_tile();
   __syncthreads();
   for (int t = 0; t < n_tiles; t += 2) {
-    tile_to_lds<D>(lm, (t + 1) * kTile, c_stop, lmB, w, lane);   // past the end: chunk 0, unused
-    score(lmA, t);
+    tile_to_lds<D, TILE>(lm, (t + 1) * TILE, c_stop, lmB, w, lane);   // past the end: chunk 0, unused
+    score(lmA, t, 0);
     wait_tile();
     __syncthreads();
     if (t + 1 >= n_tiles) break;
-    tile_to_lds<D>(lm, (t + 2) * kTile, c_stop, lmA, w, lane);
-    score(lmB, t + 1);
+    tile_to_lds<D, TILE>(lm, (t + 2) * TILE, c_stop, lmA, w, lane);
+    score(lmB, t + 1, (kTileMax - TILE) / 16);   // 32-chunk tiles: sub-tiles 2, 3 of the pair
     wait_tile();
     __syncthreads();
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
-  __shared__ __align__(16) uint16_t lmA[kTile * D];   // landmark tiles (swizzled rows)
-  __shared__ __align__(16) uint16_t lmB[kTile * D];
+template <int D, int TILE>
+__global__ __launch_bounds__(256, TILE == 32 ? 3 : 2) void scan_block_kernel(ScanArgs a) {
+  __shared__ __align__(16) uint16_t lmA[TILE * D];   // landmark tiles (swizzled rows)
+  __shared__ __align__(16) uint16_t lmB[TILE * D];
   __shared__ uint64_t buf[kBlkWaves][kRows * kBlkStride];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -738,14 +740,14 @@ __global__ __launch_bounds__(256, 2) void scan_block_kernel(ScanArgs a) {
   q.load(reinterpret_cast<const uint16_t*>(a.q_ret) + ((b * a.Lq + (r < a.Lq ? r : 0)) * a.Hkv + g) * D,
          r < a.Lq, j);
   const uint16_t* lm = reinterpret_cast<const uint16_t*>(a.landmarks) + (int64_t)bg * a.Nc * D;
-  const int n_tiles = (c_stop + kTile - 1) / kTile;
+  const int n_tiles = (c_stop + TILE - 1) / TILE;
   const int K = a.K;
 
   auto sweep1 = [&](auto&& fn) __attribute__((always_inline)) {
-    block_sweep<D, true>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
+    block_sweep<D, TILE, true>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
   };
   auto sweep2 = [&](auto&& fn) __attribute__((always_inline)) {
-    block_sweep<D, false>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
+    block_sweep<D, TILE, false>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
   };
 
   // --- pass 1: group maxima, then a lower bound of each row's K-th key -------
@@ -863,8 +865,16 @@ hipError_t launch_scan_block(const ScanArgs& a, int64_t B, int D, hipStream_t st
   if (a.K > kBlkMaxK) return hipErrorInvalidValue;
   const int64_t rbk = (a.Lq + kBlkRows - 1) / kBlkRows;
   const dim3 grid((unsigned)(rbk * B * a.Hkv), 1, 1), block(kBlkWaves * 64, 1, 1);
-  if (D == 128) hipLaunchKernelGGL((scan_block_kernel<128>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((scan_block_kernel<64>), grid, block, 0, st, a);
+  // 32-chunk tiles fit three workgroups per CU (better latency hiding) when
+  // the grid fills them; with fewer workgroups 64-chunk tiles halve the steps
+  const bool small_tiles = grid.x >= 4 * 3 * 256;
+  if (D == 128) {
+    if (small_tiles) hipLaunchKernelGGL((scan_block_kernel<128, 32>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_block_kernel<128, 64>), grid, block, 0, st, a);
+  } else {
+    if (small_tiles) hipLaunchKernelGGL((scan_block_kernel<64, 32>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((scan_block_kernel<64, 64>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
