@@ -67,15 +67,14 @@ KERNELS = {
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
     ("decode_16M", "landmarks"): "chunk_landmark_kernel<true, 128>",
     ("global_32K", "attend"): "attend_global_kernel<128, 8>",
-    ("chunked_1M", "scan"): "scan_wide_kernel<true, 128>",
-    ("chunked_1M", "merge"): "merge_lists_kernel",
+    ("chunked_1M", "scan"): "scan_block_kernel<128, 64>",
     ("chunked_1M", "bucket"): "chunk_count/scan/scatter kernels",
     ("chunked_1M", "attend"): "chunk_attend_kernel<128, 8>",
     ("chunked_1M", "combine"): "chunk_combine_kernel<128, 8>",
     ("backward_32K", "bucket"): "chunk_count/scan/scatter + bin_sort kernels",
     ("backward_32K", "attend"): "bwd_item_kernel<128, 8>",
-    ("backward_32K", "combine"): "bwd_row/bwd_chunk/bwd_landmark kernels",
-    ("prefill_128K", "scan"): "scan_block_kernel<128>",
+    ("backward_32K", "combine"): "bwd_dq/bwd_chunk/bwd_landmark kernels",
+    ("prefill_128K", "scan"): "scan_block_kernel<128, 32>",
     ("prefill_128K", "bucket"): "chunk_count/scan/scatter kernels",
     ("prefill_128K", "attend"): "chunk_attend_kernel<128, 8>",
     ("prefill_128K", "combine"): "chunk_combine_kernel<128, 8>",
