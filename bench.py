@@ -382,6 +382,7 @@ def bench_backward(name, cfg, steps, warmup, timer, cpu_baseline):
     res["step_roofline"] = step_roofline(alg["bwd_bytes"], alg["bwd_flops"], ms_mean)
     if cpu_baseline:
         res["cpu_baseline"] = oracle_backward_baseline(cfg, inp, dout_np, idx.cpu().numpy(), sc.cpu().numpy())
+        res["cpu_baseline"]["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]
     del q_ret, lm, q_attn, k, v, dout, grads, eager, inp
     torch.cuda.empty_cache()
     return res
@@ -556,6 +557,7 @@ def bench_workload(name, steps, warmup, timer, cpu_baseline):
         del lm_buf
     if cpu_baseline:
         res["cpu_baseline"] = oracle_baseline(cfg, inp)
+        res["cpu_baseline"]["gpu_over_cpu"] = res["value"] / res["cpu_baseline"]["value"]
     del dev, q_ret, lm, q_attn, k, v, out, inp
     torch.cuda.empty_cache()
     return res
@@ -580,9 +582,21 @@ def oracle_baseline(cfg, inp, budget_s=20.0):
                    top_k=cfg.top_k, rows=rows)
     dt = time.perf_counter() - t
     log("[bench] oracle: %d rows in %.1fs on %d threads" % (len(rows), dt, threads))
-    return dict(value=len(rows) / dt, unit="query-tokens/s", cores=threads, kind="oracle",
-                sample="%d of %d query rows (every %d-th row, all heads), %.1f s" % (
-                    len(rows), total, stride, dt))
+    res = dict(value=len(rows) / dt, unit="query-tokens/s", cores=threads, kind="oracle",
+               sample="%d of %d query rows (every %d-th row, all heads), %.1f s" % (
+                   len(rows), total, stride, dt))
+    if total <= 64 and threads > 1:       # decode: the same rows on one thread as well
+        oracle.set_threads(1)
+        try:
+            t = time.perf_counter()
+            oracle.forward(inp.q_ret, inp.landmarks, inp.q_attn, inp.k, inp.v, q_pos0=cfg.q_pos0,
+                           top_k=cfg.top_k, rows=rows)
+            dt1 = time.perf_counter() - t
+        finally:
+            oracle.set_threads(threads)
+        log("[bench] oracle: %d rows in %.1fs on 1 thread" % (len(rows), dt1))
+        res["value_1_thread"] = len(rows) / dt1
+    return res
 
 
 def pmc_mean_kib(csv_path, counter, match):
