@@ -366,6 +366,34 @@ def test_block_scan_small_tiles(hsa, mode, K):
         parity(hsa, inp, rows=rows)
 
 
+def _random_shapes(n, seed):
+    """Seeded small shapes across the plan's branches: few rows (decode
+    attend) and many (chunk-major), bf16 and fp32, G 1-16, d 64/128, K 1-64,
+    ragged histories and first positions, qk_norm on and off."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2])) if G <= 8 else 1
+        d = int(rng.choice([64, 128]))
+        dtype = str(rng.choice(["bf16", "bf16", "f32"]))
+        q_len = int(rng.choice([1, 7, 16, 40, 300, 1100]))
+        kv_len = max(int(rng.integers(64, 9000)), q_len)
+        q_pos0 = int(rng.integers(0, (kv_len // 64 + 1) * 64 - q_len + 1))   # rows' chunks lie in the history
+        K = int(rng.choice([1, 3, 8, 16, 32, 64]))
+        out.append(dict(name="rand%d" % i, batch=int(rng.choice([1, 2])), q_len=q_len, q_pos0=q_pos0,
+                        kv_len=kv_len, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d, top_k=K, dtype=dtype,
+                        qk_norm=bool(rng.integers(0, 2)), n_needles=2, seed=100 + i))
+    return out
+
+
+@pytest.mark.parametrize("kw", _random_shapes(12, seed=2024), ids=lambda kw: kw["name"])
+def test_random_shapes(hsa, kw):
+    cfg = small(**kw)
+    assert (cfg.q_pos0 + cfg.q_len - 1) // 64 <= cfg.kv_len // 64
+    parity(hsa, W.generate(cfg), rows=sample_rows(cfg, 120, seed=cfg.seed))
+
+
 # ----------------------------------------------------------------------------
 # full workload sizes, in the launch configuration bench.py times; the oracle
 # checks sampled rows (all 16 rows for the decode workload)
