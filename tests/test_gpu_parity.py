@@ -406,6 +406,14 @@ def test_full_size_workloads_sampled(hsa, i, n_rows):
     parity(hsa, inp, rows=sample_rows(cfg, n_rows, seed=i))
 
 
+def test_decode_16M_largest_top_k_and_group(hsa):
+    """The 16M-token decode history at the largest top-K (64) with 16 query
+    heads per kv head: 256 split lists of 64 entries per row, all 16 rows
+    checked."""
+    cfg = W.config(3, top_k=64, n_q_heads=16)
+    parity(hsa, W.generate(cfg))
+
+
 def test_one_wave_scan_buffer_compaction(hsa):
     """One-wave scan path with K = 64 and heavy ties: the LDS buffer is cut back."""
     cfg = small(batch=2, n_kv_heads=2, n_q_heads=4, q_len=8256, kv_len=8256, top_k=64, head_dim=64)
