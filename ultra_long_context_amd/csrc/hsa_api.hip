@@ -21,9 +21,10 @@ constexpr int64_t kBigItemPairs = INT64_C(1) << 22;   // (row, slot) pairs from 
 constexpr int64_t kBlockScanMinChunks = 128;
 // The workspace starts with arrival counters that every call leaves at zero.
 constexpr size_t kCounterBytes = 16384;
-constexpr int64_t kScanCounters = 2048;     // counters [0, 2048): wide-scan row blocks
-constexpr int64_t kAttendCounters = 2048;   // counters [2048, 4096): attend rows
-static_assert((kScanCounters + kAttendCounters) * 4 <= (int64_t)kCounterBytes, "counter region");
+constexpr int64_t kWideMaxRowBlocks = 2048;   // wide scan: at most this many blocks of 16 rows
+constexpr int64_t kAttendCounterBase = 2048;  // counters [2048, 4096): attend rows ([0, 2048) unused)
+constexpr int64_t kAttendCounters = 2048;
+static_assert((kAttendCounterBase + kAttendCounters) * 4 <= (int64_t)kCounterBytes, "counter region");
 
 struct Plan {
   int64_t B, Lq, q_pos0, Lkv, Nc;
@@ -116,7 +117,7 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool
   // landmark tile read once per 64 rows); few rows: the wide scan
   const bool block_ok = p->bf16 && p->K <= scan_block_max_k();
   p->block = block_ok && s->q_len >= kBlockScanMinRows && nmax >= kBlockScanMinChunks;
-  p->wide = !p->block && row_blocks <= kScanCounters && wsplits <= kMaxSplits;
+  p->wide = !p->block && row_blocks <= kWideMaxRowBlocks && wsplits <= kMaxSplits;
   p->block = p->block || (!p->wide && block_ok);
   p->split_len = (int32_t)(p->wide ? wchunks : std::max<int64_t>(64, (nmax + 63) / 64 * 64));
   p->n_splits = (int32_t)(p->wide ? wsplits : 1);
@@ -230,7 +231,7 @@ hsa_status_t launch_decode(const Plan& p, const void* q_attn, const void* k, con
   a.q_attn = q_attn; a.k = k; a.v = v; a.lists = lists; a.idx_in = idx_in; a.score_in = score_in;
   a.idx_out = idx_out; a.score_out = score_out; a.out = out;
   a.partials = reinterpret_cast<float*>(w + p.off_partials);
-  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters) + kScanCounters;
+  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters) + kAttendCounterBase;
   a.Lq = p.Lq; a.Lkv = p.Lkv; a.Nc = p.Nc; a.Hq = p.Hq; a.Hkv = p.Hkv; a.K = p.K;
   a.n_splits = p.n_splits; a.n_blocks = p.attn_splits;
   a.ret_scale = p.ret_scale; a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0;
@@ -247,7 +248,7 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
   AttendArgs a;
   a.q_attn = q_attn; a.k = k; a.v = v; a.idx = idx; a.score = score; a.out = out;
   a.partials = reinterpret_cast<float*>(w + p.off_partials);
-  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters) + kScanCounters;
+  a.counters = reinterpret_cast<uint32_t*>(w + p.off_counters) + kAttendCounterBase;
   a.Lq = p.Lq; a.Lkv = p.Lkv; a.Nc = p.Nc; a.Hq = p.Hq; a.Hkv = p.Hkv; a.K = p.K;
   a.n_splits = p.attn_splits; a.slots_per_split = p.slots_per_split;
   a.attn_scale = p.attn_scale; a.qk_norm = p.qk_norm ? 1 : 0; a.mode = p.attn_mode;
