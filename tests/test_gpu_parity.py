@@ -394,6 +394,34 @@ def test_random_shapes(hsa, kw):
     parity(hsa, W.generate(cfg), rows=sample_rows(cfg, 120, seed=cfg.seed))
 
 
+def _random_long_shapes(n, seed):
+    """Seeded few-row shapes over histories of more than 1024 chunks, so the
+    wide scan splits the chunks and the per-split lists are merged: bf16
+    (decode attend, merge in its prologue) and fp32 (merge kernel, then the
+    per-row attend), G 1-16, d 64/128, K 1-64, rows short of their chunk end."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2])) if G <= 4 else 1
+        q_len = int(rng.choice([1, 5, 16, 33]))
+        kv_len = int(rng.integers(65600, 300000))
+        q_pos0 = max(0, kv_len - q_len - int(rng.integers(0, 5000)))
+        out.append(dict(name="long%d" % i, batch=int(rng.choice([1, 2])), q_len=q_len, q_pos0=q_pos0,
+                        kv_len=kv_len, n_q_heads=G * Hkv, n_kv_heads=Hkv,
+                        head_dim=int(rng.choice([64, 128])), top_k=int(rng.choice([1, 7, 32, 64])),
+                        dtype=str(rng.choice(["bf16", "f32"])), qk_norm=bool(rng.integers(0, 2)),
+                        n_needles=3, seed=200 + i))
+    return out
+
+
+@pytest.mark.parametrize("kw", _random_long_shapes(8, seed=77), ids=lambda kw: kw["name"])
+def test_random_long_histories(hsa, kw):
+    cfg = small(**kw)
+    assert cfg.kv_len // 64 > 1024 and (cfg.q_pos0 + cfg.q_len - 1) // 64 <= cfg.kv_len // 64
+    parity(hsa, W.generate(cfg))
+
+
 # ----------------------------------------------------------------------------
 # full workload sizes, in the launch configuration bench.py times; the oracle
 # checks sampled rows (all 16 rows for the decode workload)
