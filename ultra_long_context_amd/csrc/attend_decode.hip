@@ -4,7 +4,7 @@
 //
 // One workgroup of 4 waves serves 4 selected slots of one query row:
 //   selection  when the landmark scan left one sorted candidate list per chunk
-//              range, wave 0 merges them (only lists whose head reaches the
+//              range, the waves merge them (only lists whose head reaches the
 //              K-th largest head key can contribute) and the workgroup of slot
 //              block 0 writes the row's final topk_idx / topk_score;
 //   attend     each wave takes one slot: the chunk's keys are the B operand of
@@ -171,6 +171,115 @@ __device__ __forceinline__ int merge_row_lists(const uint64_t* L, int n_splits, 
   return merge_row_lists_nh<kMaxHeads>(L, n_splits, K, C, top, act, lane);
 }
 
+// The fast path of merge_row_lists with the workgroup's waves sharing the
+// work: wave w loads entry w of every list, wave 0 derives the bound from the
+// heads, the waves compact their entries at or above it side by side into C
+// and rank the candidates against a quarter of C each.  Whenever the one-round
+// result is not exact (more than 64 candidates, or a list whose last loaded
+// entry reaches the K-th selected key) wave 0 runs merge_row_lists instead.
+// Called by every wave of the workgroup; the result (top[0..m), m) is valid in
+// wave 0.
+struct MergeShared {
+  uint64_t lo;                        // bound from the heads
+  int cnt[kSlotsPerBlock];            // entries at or above it, per wave
+  int prank[kSlotsPerBlock][kWave];   // partial ranks of the candidates
+  uint64_t lastmax[kWave];            // per lane: largest last loaded entry
+};
+static_assert(kSlotsPerBlock == kFirst, "one wave per first entry of the lists");
+
+template <int NH>
+__device__ __forceinline__ int merge_row_lists_waves(const uint64_t* L, int n_splits, int K, uint64_t* C,
+                                                     uint64_t* top, int* act, MergeShared& sh, int w, int lane) {
+  const int nh = (n_splits + kWave - 1) / kWave;      // <= NH
+  const int ne = K < kFirst ? K : kFirst;
+  uint64_t f[NH];                                     // entry w of lists lane + 64 i
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const int sp = lane + kWave * i;
+    const uint64_t v = L[(int64_t)(w < ne ? w : 0) * n_splits + (sp < n_splits ? sp : 0)];
+    f[i] = (w < ne && i < nh && sp < n_splits) ? v : 0ull;
+  }
+  if (w == 0) {
+    // the K-th largest lane maximum of the heads: K lanes hold a key at or
+    // above it, so it bounds the row's K-th largest key from below (0 if fewer)
+    uint64_t hmax = f[0];
+#pragma unroll
+    for (int i = 1; i < NH; ++i) hmax = f[i] > hmax ? f[i] : hmax;
+    C[lane] = hmax;
+    const int hrank = lds_rank(C, kWave, hmax);
+    const uint64_t kmask_h = __ballot(hmax != 0ull && hrank == K - 1);
+    const uint64_t lo_heads = kmask_h != 0ull ? shfl_u64(hmax, (int)__builtin_ctzll(kmask_h)) : 0ull;
+    if (lane == 0) sh.lo = lo_heads;
+  }
+  if (w == kFirst - 1) {
+    uint64_t lm = f[0];
+#pragma unroll
+    for (int i = 1; i < NH; ++i) lm = f[i] > lm ? f[i] : lm;
+    sh.lastmax[lane] = lm;
+  }
+  __syncthreads();
+  const uint64_t lo = sh.lo;
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NH; ++i) n += wave_count(f[i] != 0ull && f[i] >= lo);
+  if (lane == 0) sh.cnt[w] = n;
+  __syncthreads();
+  int off = 0, total = 0;
+#pragma unroll
+  for (int v = 0; v < kSlotsPerBlock; ++v) {
+    off += v < w ? sh.cnt[v] : 0;
+    total += sh.cnt[v];
+  }
+  if (total <= kWave) {
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const bool keep = f[i] != 0ull && f[i] >= lo;
+      const uint64_t mask = __ballot(keep);
+      if (keep) C[off + __popcll(mask & lanemask_lt())] = f[i];
+      off += __popcll(mask);
+    }
+  }
+  __syncthreads();
+  if (total <= kWave) {                   // partial ranks against C[16 w, 16 w + 16)
+    const uint64_t mine = lane < total ? C[lane] : 0ull;
+    constexpr int Q = kWave / kSlotsPerBlock;
+    const int q0 = Q * w;
+    uint64_t x[Q];
+#pragma unroll
+    for (int u = 0; u < Q; ++u) x[u] = C[q0 + u < total ? q0 + u : 0];
+    int pr = 0;
+#pragma unroll
+    for (int u = 0; u < Q; ++u) pr += (q0 + u < total && x[u] > mine) ? 1 : 0;
+    sh.prank[w][lane] = pr;
+  }
+  __syncthreads();
+  if (w != 0) return 0;
+  if (total <= kWave) {
+    const uint64_t mine = lane < total ? C[lane] : 0ull;
+    int rank = 0;
+#pragma unroll
+    for (int v = 0; v < kSlotsPerBlock; ++v) rank += sh.prank[v][lane];
+    const int m = total < K ? total : K;
+    // K-th selected key (with fewer than K, any nonzero entry would still enter)
+    const uint64_t kmask = __ballot(lane < total && rank == K - 1);
+    const uint64_t kth = (m == K && kmask != 0ull) ? shfl_u64(mine, (int)__builtin_ctzll(kmask)) : 1ull;
+    if (ne == K || !__any(sh.lastmax[lane] >= kth)) {
+      if (lane < total && rank < K) top[rank] = mine;
+      return m;
+    }
+  }
+  return merge_row_lists_nh<NH>(L, n_splits, K, C, top, act, lane);
+}
+
+// Dispatch on the list-head slots per lane; called by every wave.
+__device__ __forceinline__ int merge_row_lists_wg(const uint64_t* L, int n_splits, int K, uint64_t* C,
+                                                  uint64_t* top, int* act, MergeShared& sh, int w, int lane) {
+  if (n_splits <= kWave) return merge_row_lists_waves<1>(L, n_splits, K, C, top, act, sh, w, lane);
+  if (n_splits <= 2 * kWave) return merge_row_lists_waves<2>(L, n_splits, K, C, top, act, sh, w, lane);
+  if (n_splits <= 4 * kWave) return merge_row_lists_waves<4>(L, n_splits, K, C, top, act, sh, w, lane);
+  return merge_row_lists_waves<kMaxHeads>(L, n_splits, K, C, top, act, sh, w, lane);
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   constexpr int KSTEP = D / 32;
@@ -186,6 +295,7 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   __shared__ int32_t sel_c[kMaxTopK];
   __shared__ float sel_w[kMaxTopK];
   __shared__ int last;
+  __shared__ MergeShared msh;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t row = blockIdx.x;                     // (b*Lq + r)*Hkv + g
@@ -196,10 +306,13 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   const int K = a.K;
 
   // --- the row's selection and blend weights -------------------------------
+  int m_merged = 0;
+  if (a.lists != nullptr)                 // uniform: every wave takes part
+    m_merged = merge_row_lists_wg(a.lists + row * a.n_splits * K, a.n_splits, K, cand, top, act, msh, w, lane);
   if (w == 0) {
     int m;
     if (a.lists != nullptr) {
-      m = merge_row_lists(a.lists + row * a.n_splits * K, a.n_splits, K, cand, top, act, lane);
+      m = m_merged;
     } else {
       const int32_t ci = lane < K ? a.idx_in[row * K + lane] : -1;
       const float si = lane < K ? a.score_in[row * K + lane] : 0.f;
