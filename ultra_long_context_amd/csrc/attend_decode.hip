@@ -5,8 +5,10 @@
 // One workgroup of 4 waves serves 4 selected slots of one query row:
 //   selection  when the landmark scan left one sorted candidate list per chunk
 //              range, the waves merge them (only lists whose head reaches the
-//              K-th largest head key can contribute) and the workgroup of slot
-//              block 0 writes the row's final topk_idx / topk_score;
+//              K-th largest head key can contribute); every wave ends with the
+//              ranked selection in its lanes and takes its own slot's chunk and
+//              blend weight from it, and the workgroup of slot block 0 writes
+//              the row's final topk_idx / topk_score;
 //   attend     each wave takes one slot: the chunk's keys are the B operand of
 //              v_mfma_f32_16x16x32_bf16 straight from HBM, the G attention
 //              queries the A operand (16 rows, G of them used), V is staged
@@ -177,19 +179,22 @@ __device__ __forceinline__ int merge_row_lists(const uint64_t* L, int n_splits, 
 // and rank the candidates against a quarter of C each.  Whenever the one-round
 // result is not exact (more than 64 candidates, or a list whose last loaded
 // entry reaches the K-th selected key) wave 0 runs merge_row_lists instead.
-// Called by every wave of the workgroup; the result (top[0..m), m) is valid in
-// wave 0.
+// Called by every wave of the workgroup; every wave ends with the selection
+// spread over its lanes: lane p holds a candidate e with rank r (the r-th
+// largest key; valid if p < n and r < K), n returned.
 struct MergeShared {
   uint64_t lo;                        // bound from the heads
   int cnt[kSlotsPerBlock];            // entries at or above it, per wave
   int prank[kSlotsPerBlock][kWave];   // partial ranks of the candidates
   uint64_t lastmax[kWave];            // per lane: largest last loaded entry
+  int m;                              // size of the one-wave merge's selection
 };
 static_assert(kSlotsPerBlock == kFirst, "one wave per first entry of the lists");
 
 template <int NH>
 __device__ __forceinline__ int merge_row_lists_waves(const uint64_t* L, int n_splits, int K, uint64_t* C,
-                                                     uint64_t* top, int* act, MergeShared& sh, int w, int lane) {
+                                                     uint64_t* top, int* act, MergeShared& sh, int w, int lane,
+                                                     uint64_t& e_out, int& rank_out) {
   const int nh = (n_splits + kWave - 1) / kWave;      // <= NH
   const int ne = K < kFirst ? K : kFirst;
   uint64_t f[NH];                                     // entry w of lists lane + 64 i
@@ -253,7 +258,8 @@ __device__ __forceinline__ int merge_row_lists_waves(const uint64_t* L, int n_sp
     sh.prank[w][lane] = pr;
   }
   __syncthreads();
-  if (w != 0) return 0;
+  // every wave: full ranks and the exactness test (same data, same outcome)
+  bool exact = false;
   if (total <= kWave) {
     const uint64_t mine = lane < total ? C[lane] : 0ull;
     int rank = 0;
@@ -263,21 +269,31 @@ __device__ __forceinline__ int merge_row_lists_waves(const uint64_t* L, int n_sp
     // K-th selected key (with fewer than K, any nonzero entry would still enter)
     const uint64_t kmask = __ballot(lane < total && rank == K - 1);
     const uint64_t kth = (m == K && kmask != 0ull) ? shfl_u64(mine, (int)__builtin_ctzll(kmask)) : 1ull;
-    if (ne == K || !__any(sh.lastmax[lane] >= kth)) {
-      if (lane < total && rank < K) top[rank] = mine;
-      return m;
-    }
+    exact = ne == K || !__any(sh.lastmax[lane] >= kth);
+    e_out = mine;
+    rank_out = rank;
   }
-  return merge_row_lists_nh<NH>(L, n_splits, K, C, top, act, lane);
+  if (exact) return total;
+  // not exact (uniform over the workgroup): the one-wave merge on wave 0
+  if (w == 0) {
+    const int m = merge_row_lists_nh<NH>(L, n_splits, K, C, top, act, lane);
+    if (lane == 0) sh.m = m;
+  }
+  __syncthreads();
+  const int m = sh.m;
+  e_out = lane < m ? top[lane] : 0ull;
+  rank_out = lane;
+  return m;
 }
 
 // Dispatch on the list-head slots per lane; called by every wave.
 __device__ __forceinline__ int merge_row_lists_wg(const uint64_t* L, int n_splits, int K, uint64_t* C,
-                                                  uint64_t* top, int* act, MergeShared& sh, int w, int lane) {
-  if (n_splits <= kWave) return merge_row_lists_waves<1>(L, n_splits, K, C, top, act, sh, w, lane);
-  if (n_splits <= 2 * kWave) return merge_row_lists_waves<2>(L, n_splits, K, C, top, act, sh, w, lane);
-  if (n_splits <= 4 * kWave) return merge_row_lists_waves<4>(L, n_splits, K, C, top, act, sh, w, lane);
-  return merge_row_lists_waves<kMaxHeads>(L, n_splits, K, C, top, act, sh, w, lane);
+                                                  uint64_t* top, int* act, MergeShared& sh, int w, int lane,
+                                                  uint64_t& e, int& rank) {
+  if (n_splits <= kWave) return merge_row_lists_waves<1>(L, n_splits, K, C, top, act, sh, w, lane, e, rank);
+  if (n_splits <= 2 * kWave) return merge_row_lists_waves<2>(L, n_splits, K, C, top, act, sh, w, lane, e, rank);
+  if (n_splits <= 4 * kWave) return merge_row_lists_waves<4>(L, n_splits, K, C, top, act, sh, w, lane, e, rank);
+  return merge_row_lists_waves<kMaxHeads>(L, n_splits, K, C, top, act, sh, w, lane, e, rank);
 }
 
 template <int D, int G>
@@ -292,8 +308,6 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   __shared__ uint64_t top[kMaxTopK];
   __shared__ int act[kWave];
   __shared__ float osum[kSlotsPerBlock][G * D];
-  __shared__ int32_t sel_c[kMaxTopK];
-  __shared__ float sel_w[kMaxTopK];
   __shared__ int last;
   __shared__ MergeShared msh;
 
@@ -306,53 +320,50 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
   const int K = a.K;
 
   // --- the row's selection and blend weights -------------------------------
-  int m_merged = 0;
-  if (a.lists != nullptr)                 // uniform: every wave takes part
-    m_merged = merge_row_lists_wg(a.lists + row * a.n_splits * K, a.n_splits, K, cand, top, act, msh, w, lane);
-  if (w == 0) {
-    int m;
-    if (a.lists != nullptr) {
-      m = m_merged;
-    } else {
-      const int32_t ci = lane < K ? a.idx_in[row * K + lane] : -1;
-      const float si = lane < K ? a.score_in[row * K + lane] : 0.f;
-      // given selection: keep it as is (slot order), packing only valid entries
-      m = -1;
-      if (lane < K) {
-        sel_c[lane] = (ci >= 0 && (int64_t)ci < a.Nc) ? ci : -1;
-        sel_w[lane] = si;
+  // every wave holds the whole selection, lane p: chunk, score and rank (the
+  // merged selection's order, or the slot order of a given one), and takes its
+  // own slot's chunk and weight from it
+  const int slot = blk * kSlotsPerBlock + w;
+  int32_t chunk = -1, rank = lane;
+  float s = -INFINITY;
+  bool valid;
+  if (a.lists != nullptr) {                // uniform: every wave takes part in the merge
+    uint64_t e = 0ull;
+    const int n = merge_row_lists_wg(a.lists + row * a.n_splits * K, a.n_splits, K, cand, top, act, msh, w, lane,
+                                     e, rank);
+    valid = lane < n && rank < K;
+    if (valid) {
+      chunk = (int32_t)cand_chunk(e);
+      s = key_score(cand_key(e)) * a.ret_scale;
+    }
+    if (blk == 0 && w == 0 && a.idx_out != nullptr) {
+      const int m = n < K ? n : K;
+      if (valid) {
+        a.idx_out[row * K + rank] = chunk;
+        a.score_out[row * K + rank] = s;
+      }
+      if (lane >= m && lane < K) {
+        a.idx_out[row * K + lane] = -1;
+        a.score_out[row * K + lane] = -INFINITY;
       }
     }
-    float s = -INFINITY;
-    int32_t c = -1;
-    if (m >= 0) {                         // merged: sorted top[0..m)
-      if (lane < m) {
-        c = (int32_t)cand_chunk(top[lane]);
-        s = key_score(cand_key(top[lane])) * a.ret_scale;
-      }
-      if (blk == 0 && lane < K && a.idx_out != nullptr) {
-        a.idx_out[row * K + lane] = lane < m ? c : -1;
-        a.score_out[row * K + lane] = lane < m ? s : -INFINITY;
-      }
-    } else if (lane < K) {
-      c = sel_c[lane];
-      s = sel_w[lane];
-    }
-    const bool valid = c >= 0;
-    const float mx = wave_max(valid ? s : -INFINITY);
-    const float ex = valid ? expf(s - mx) : 0.f;
-    const float den = wave_sum(ex);
-    if (lane < K) {
-      sel_c[lane] = valid ? c : -1;
-      sel_w[lane] = valid ? ex / den : 0.f;
+  } else {                                 // given selection: kept as is (slot order)
+    const int32_t ci = lane < K ? a.idx_in[row * K + lane] : -1;
+    valid = ci >= 0 && (int64_t)ci < a.Nc;
+    if (valid) {
+      chunk = ci;
+      s = a.score_in[row * K + lane];
     }
   }
-  __syncthreads();
+  const float mx = wave_max(valid ? s : -INFINITY);
+  const float ex = valid ? expf(s - mx) : 0.f;
+  const float den = wave_sum(ex);
+  const uint64_t hit = __ballot(valid && rank == slot);
+  const int src = hit != 0ull ? (int)__builtin_ctzll(hit) : 0;
+  const int c = hit != 0ull ? __shfl(chunk, src, kWave) : -1;
+  const float wk = hit != 0ull ? __shfl(ex, src, kWave) / den : 0.f;
 
   // --- one slot per wave ----------------------------------------------------
-  const int slot = blk * kSlotsPerBlock + w;
-  const int c = slot < K ? sel_c[slot] : -1;
-  const float wk = slot < K ? sel_w[slot] : 0.f;
   const int ma = lane & 15, jg = lane >> 4;
   floatx4 o[NT];
 #pragma unroll
@@ -362,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
     const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k) + base;
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v) + base;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_attn) + (br * a.Hq + (int64_t)g * G) * D;
-    // all loads first: keys as B operands, queries as A operands, V rows (lane = key)
+    // all loads first: keys as B operands, queries as A operands, V rows
     uint4 kb[4][KSTEP], qa[KSTEP], vx[D / 8];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -374,11 +385,15 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
       qa[t] = *reinterpret_cast<const uint4*>(qp + (ma < G ? ma : 0) * D + 32 * t + 8 * jg);
       if (ma >= G) qa[t] = make_uint4(0, 0, 0, 0);
     }
+    // V: consecutive lanes take consecutive 16-byte pieces of the chunk
 #pragma unroll
-    for (int dg = 0; dg < D / 8; ++dg) vx[dg] = *reinterpret_cast<const uint4*>(vp + lane * D + 8 * dg);
+    for (int dg = 0; dg < D / 8; ++dg) vx[dg] = *reinterpret_cast<const uint4*>(vp + (dg * kWave + lane) * 8);
     // V rows into LDS (read back transposed as the B operand of P V)
 #pragma unroll
-    for (int dg = 0; dg < D / 8; ++dg) *reinterpret_cast<uint4*>(&vs[w][lane * VROW + 8 * dg]) = vx[dg];
+    for (int dg = 0; dg < D / 8; ++dg) {
+      const int e = (dg * kWave + lane) * 8;
+      *reinterpret_cast<uint4*>(&vs[w][(e / D) * VROW + e % D]) = vx[dg];
+    }
     // norms: lane holds 32 dims of query row ma and of key 16*nt + ma
     float qss = 0.f, kss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
