@@ -54,6 +54,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
+N_SIMDS = 256 * 4                # 256 CUs x 4 SIMDs
+N_XCDS = 8                       # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 VALU_FP32_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 FLOP (FMA) x 2.4 GHz, non-packed
 
 WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "global_32K": 1, "backward_32K": 1, "chunked_1M": 4}
@@ -256,6 +258,34 @@ def traffic_file(workload, kernel):
     return os.path.join(PROFILES, "%s_%s_hbm_traffic.txt" % (kernel.split("<")[0], workload))
 
 
+def mfma_file(workload, kernel):
+    return os.path.join(PROFILES, "%s_%s_mfma.txt" % (kernel.split("<")[0], workload))
+
+
+def summary_fields(path, kernel):
+    """key: value lines of a committed counter summary, or None if there is none
+    or the kernel sources changed since it was taken."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k_, v_ = line.split(":", 1)
+                kv[k_.strip()] = v_.strip()
+    if kv.get("source_digest") != source_digest(kernel):
+        return None
+    return kv
+
+
+def measured_mfma_busy(workload, kernel):
+    """Fraction of SIMD cycles the MFMA unit was busy during the kernel, from the
+    committed counter summary (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x
+    SIMDs), or None."""
+    kv = summary_fields(mfma_file(workload, kernel), kernel)
+    return None if kv is None else float(kv["mfma_busy_percent"]) / 100.0
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed counter summary, or None if there
     is none or the kernel sources changed since it was taken."""
@@ -307,9 +337,13 @@ def roofline(workload, stage, ms, alg):
         achieved, peak, unit = amount / (ms / 1e3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = amount / (ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    return dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
-                traffic=measured_traffic(workload, kernel), kernel=kernel, stage=stage,
-                kernel_ms=ms, algorithmic_per_launch=amount, algorithmic_units=how)
+    res = dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
+               traffic=measured_traffic(workload, kernel), kernel=kernel, stage=stage,
+               kernel_ms=ms, algorithmic_per_launch=amount, algorithmic_units=how)
+    mb = measured_mfma_busy(workload, kernel)
+    if bound == "mfma" or mb is not None:
+        res["mfma_busy_counter"] = mb
+    return res
 
 
 def step_roofline(nbytes, flops, ms):
@@ -646,6 +680,60 @@ def pmc_summary(fetch_csv, write_csv, workload, kernel, command):
     return "\n".join(lines) + "\n"
 
 
+def pmc_dispatch_values(csv_path, counter, match):
+    """Per-dispatch values of `counter` for kernels whose name contains `match`,
+    with each dispatch's duration in microseconds."""
+    import csv
+    vals, dur = {}, {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter and match in row.get("Kernel_Name", ""):
+                d = row.get("Dispatch_Id") or row.get("Correlation_Id")
+                vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
+                dur[d] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+    return vals, dur
+
+
+def mfma_summary(csv_path, workload, kernel, command):
+    """Text summary of one counter pass (SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16) for `kernel`: the MFMA busy
+    fraction over all SIMDs and the bf16 MFMA work the hardware counted.
+    GRBM_GUI_ACTIVE is reported summed over the XCDs, so the busy cycles of
+    the SIMDs are set against GRBM_GUI_ACTIVE / N_XCDS cycles each (the same
+    figure as rocprofv3's derived MfmaUtil, recorded beside it when present)."""
+    match = kernel.split("<")[0]
+    busy, dur = pmc_dispatch_values(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES", match)
+    gui, _ = pmc_dispatch_values(csv_path, "GRBM_GUI_ACTIVE", match)
+    mops, _ = pmc_dispatch_values(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16", match)
+    ds = sorted(set(busy) & set(gui) & set(mops))
+    if not ds:
+        raise SystemExit("no dispatch of a kernel matching %r with all three counters in %s" % (match, csv_path))
+    b = float(np.mean([busy[d] for d in ds]))
+    g = float(np.mean([gui[d] for d in ds]))
+    flop = float(np.mean([mops[d] for d in ds])) * 512.0
+    us = float(np.mean([dur[d] for d in ds]))
+    util, _ = pmc_dispatch_values(csv_path, "MfmaUtil", match)   # rocprofv3's derived metric, if collected
+    lines = [
+        "# MFMA activity of %s, workload %s (rocprofv3 counter pass)" % (kernel, workload),
+        "# command: %s" % command,
+        "kernel: %s" % kernel,
+        "workload: %s" % workload,
+        "source_digest: %s" % source_digest(kernel),
+        "dispatches: %d" % len(ds),
+        "SQ_VALU_MFMA_BUSY_CYCLES_per_dispatch: %.0f" % b,
+        "GRBM_GUI_ACTIVE_per_dispatch: %.0f" % g,
+        "simds: %d" % N_SIMDS,
+        "xcds: %d" % N_XCDS,
+        "mfma_busy_percent: %.2f" % (100.0 * b / (g / N_XCDS * N_SIMDS)),
+        "mfma_bf16_flop_per_dispatch: %.0f" % flop,
+        "dispatch_us: %.1f" % us,
+        "mfma_bf16_tflops_counted: %.1f" % (flop / (us * 1e-6) / 1e12),
+    ]
+    if util:
+        lines.append("rocprof_MfmaUtil_percent: %.2f" % float(np.mean(list(util.values()))))
+    return "\n".join(lines) + "\n"
+
+
 def copy_calibration():
     """The plain copy kernel the counter passes are scaled by."""
     import torch
@@ -668,10 +756,16 @@ def main():
                     help="run the 1 GiB calibration copy first (for counter passes)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of --kernel-of from two counter passes")
+    ap.add_argument("--mfma-summary", metavar="CSV",
+                    help="print the MFMA activity summary of --kernel-of from one counter pass")
     ap.add_argument("--kernel-of", default="prefill_128K:attend",
-                    help="workload:stage whose kernel --pmc-summary reports")
+                    help="workload:stage whose kernel --pmc-summary / --mfma-summary reports")
     ap.add_argument("--command", default="", help="command recorded in the --pmc-summary header")
     args = ap.parse_args()
+    if args.mfma_summary:
+        wl, stage = args.kernel_of.split(":")
+        sys.stdout.write(mfma_summary(args.mfma_summary, wl, KERNELS[(wl, stage)], args.command))
+        return
     if args.pmc_summary:
         wl, stage = args.kernel_of.split(":")
         sys.stdout.write(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl,

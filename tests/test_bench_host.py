@@ -70,3 +70,28 @@ def test_counter_summary_scales_by_the_calibration_copy(tmp_path):
     assert float(vals["fetch_bytes_per_launch"]) == pytest.approx(2000.0 * 1024 * 2.0)
     assert float(vals["write_bytes_per_launch"]) == pytest.approx(500.0 * 1024)
     assert int(vals["fetch_dispatches"]) == 2
+
+
+def test_mfma_summary_busy_fraction(tmp_path):
+    """A kernel whose 1024 SIMDs are each MFMA-busy for a quarter of the
+    dispatch's cycles (GRBM_GUI_ACTIVE arrives summed over the 8 XCDs) reads 25 %;
+    the counted bf16 FLOPs are the MOPS counter times 512."""
+    path = tmp_path / "m.csv"
+    name = "void hsa::(anonymous namespace)::chunk_attend_kernel<128, 8>(hsa::ChunkArgs)"
+    cycles = 2_000_000                            # per XCD
+    with open(path, "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                     "Start_Timestamp", "End_Timestamp"])
+        for d in (1, 2):
+            for cn, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * cycles * bench.N_SIMDS),
+                          ("GRBM_GUI_ACTIVE", cycles * bench.N_XCDS),
+                          ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e9)):
+                wr.writerow([d, name, cn, v, 0, 1_000_000])     # 1 ms
+            wr.writerow([3, "void at::native::neg_kernel", "GRBM_GUI_ACTIVE", 5.0, 0, 10])
+    text = bench.mfma_summary(str(path), "prefill_128K", "chunk_attend_kernel<128, 8>", "cmd")
+    vals = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and not line.startswith("#"))
+    assert int(vals["dispatches"]) == 2
+    assert float(vals["mfma_busy_percent"]) == pytest.approx(25.0)
+    assert float(vals["mfma_bf16_flop_per_dispatch"]) == pytest.approx(512e9)
+    assert float(vals["mfma_bf16_tflops_counted"]) == pytest.approx(512e9 / 1e-3 / 1e12)
