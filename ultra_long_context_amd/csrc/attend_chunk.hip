@@ -310,7 +310,7 @@ __device__ __forceinline__ float sumsq8(uint4 x, float acc) {
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
-  constexpr int KROW = D + 8;          // bf16 elements per K row in LDS (16-byte pad)
+  constexpr int KROW = D + 16;         // bf16 elements per K row in LDS (32-byte pad: no bank conflicts)
   constexpr int VROW = D + 16;         // bf16 elements per V row in LDS (read back transposed)
   constexpr int PT = 16 / G;           // pairs per MFMA tile (16 head-rows)
   constexpr int KSTEP = D / 32;        // MFMA K-steps over the head dimension

@@ -31,7 +31,7 @@ constexpr float kLog2eG = 1.4426950408889634f;
 template <int D, int G>
 __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) {
   constexpr int R = 256 / G;                   // query rows per workgroup
-  constexpr int KROW = D + 8, VROW = D + 16, LROW = D + 8;
+  constexpr int KROW = D + 16, VROW = D + 16, LROW = D + 16;   // 288-byte rows: no LDS bank conflicts
   constexpr int KSTEP = D / 32, NT = D / 16;
   constexpr int TPR = 16 / G;                  // rows per 16-head-row tile (G = 8: 2, G = 16: 1)
   __shared__ __align__(16) uint16_t ks[2][kChunk * KROW];

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void bin_sort_kernel(BwdArgs a) {
 // --- per work item ------------------------------------------------------------
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
-  constexpr int KROW = D + 8;               // K, V rows (bf16)
+  constexpr int KROW = D + 16;              // K, V rows (bf16; 32-byte pad: no bank conflicts)
   constexpr int PROW = kChunk + 16;          // staged P, h rows [head-row][key]
   constexpr int QROW = D + 16;              // staged q, dO_w rows [head-row][dim]
   constexpr int PT = 16 / G;                // pairs per 16-head-row tile
