@@ -31,13 +31,16 @@ MFMA FLOPs / 2.5 PFLOP/s); frac = t_roof / ms_per_step.
 cpu_baseline: the fp64 oracle on a bounded, stratified sample of query rows of the
 same workload, timed on this host's cores (test infrastructure, not the product).
 
-Further workloads (--workloads): chunked_1M (8,192 new rows appended to a
-1,048,576-token history, 32 q / 4 kv heads, top-K 32; HBM-bound: roofline in
-bytes), global_32K (top-K covering all 512 chunks of the
-32K window: global HSA), backward_32K (hsa_backward on the 32K window for the
-forward's selection; roofline on the per-item MFMA kernel, 10*G*64*d FLOP per
-selection), crossover (HSA forward vs dense causal SDPA from 4K to 1M tokens,
-opt-in; also against dense attention at the bf16 MFMA peak).
+Further workloads (--workloads, all in the default run): prefill_32K (the 32K
+training window: B=1, 8 q heads / 1 kv head, d=128, top-K 8), chunked_1M
+(8,192 new rows appended to a 1,048,576-token history, 32 q / 4 kv heads,
+top-K 32; HBM-bound: roofline in bytes), global_32K (top-K covering all 512
+chunks of the 32K window: global HSA), backward_32K (hsa_backward on the 32K
+window for the forward's selection; roofline on the per-item MFMA kernel,
+10*G*64*d FLOP per selection), crossover (HSA forward vs dense causal SDPA
+from 4K to 256K tokens by default, --crossover-max up to 1M; also against
+dense attention at the bf16 MFMA peak).  Every cpu_baseline names the host's
+CPU model and the threads the oracle used.
 """
 from __future__ import annotations
 
@@ -58,7 +61,8 @@ N_SIMDS = 256 * 4                # 256 CUs x 4 SIMDs
 N_XCDS = 8                       # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 VALU_FP32_PEAK_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 FLOP (FMA) x 2.4 GHz, non-packed
 
-WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "global_32K": 1, "backward_32K": 1, "chunked_1M": 4}
+WORKLOADS = {"prefill_128K": 2, "decode_16M": 3, "prefill_32K": 1, "global_32K": 1, "backward_32K": 1,
+             "chunked_1M": 4}
 # global_32K: the 32K training-window prefill with a top-K covering all 512
 # chunks (global HSA of the warm-up stage); the dense fused kernel runs it
 OVERRIDES = {"global_32K": dict(top_k=512, name="global_hsa_32K_gqa8")}
@@ -76,6 +80,10 @@ KERNELS = {
     ("backward_32K", "bucket"): "chunk_count/scan/scatter + bin_sort kernels",
     ("backward_32K", "attend"): "bwd_item_kernel<128, 8>",
     ("backward_32K", "combine"): "bwd_dq/bwd_chunk/bwd_landmark kernels",
+    ("prefill_32K", "scan"): "scan_block_kernel<128, 64>",
+    ("prefill_32K", "bucket"): "chunk_count/scan/scatter kernels",
+    ("prefill_32K", "attend"): "chunk_attend_kernel<128, 8>",
+    ("prefill_32K", "combine"): "chunk_combine_kernel<128, 8>",
     ("prefill_128K", "scan"): "scan_block_kernel<128, 32>",
     ("prefill_128K", "bucket"): "chunk_count/scan/scatter kernels",
     ("prefill_128K", "attend"): "chunk_attend_kernel<128, 8>",
@@ -87,6 +95,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def to_dev(a, dtype):
@@ -443,11 +464,13 @@ def oracle_backward_baseline(cfg, inp, dout, idx, sc, budget_s=15.0):
     threads = min(oracle.max_threads(), cfg.batch * cfg.n_kv_heads)   # parallel over (batch, kv head)
     log("[bench] oracle backward: %d rows in %.1fs on %d threads" % (len(rows), dt, threads))
     return dict(value=cfg.batch * len(rows) / dt, unit="query-tokens/s", cores=threads, kind="oracle",
+                cpu_model=cpu_model(),
                 sample="%d of %d query rows (every %d-th row of each sequence, all heads), %.1f s" % (
                     cfg.batch * len(rows), total, stride, dt))
 
 
 CROSSOVER_LENGTHS = (4096, 8192, 16384, 32768, 65536, 131072, 262144, 524288, 1048576)
+CROSSOVER_DEFAULT_MAX = 262144   # dense SDPA past 256K takes seconds per call
 
 
 def bench_crossover(steps, warmup, timer, lengths=CROSSOVER_LENGTHS):
@@ -617,6 +640,7 @@ def oracle_baseline(cfg, inp, budget_s=20.0):
     dt = time.perf_counter() - t
     log("[bench] oracle: %d rows in %.1fs on %d threads" % (len(rows), dt, threads))
     res = dict(value=len(rows) / dt, unit="query-tokens/s", cores=threads, kind="oracle",
+               cpu_model=cpu_model(),
                sample="%d of %d query rows (every %d-th row, all heads), %.1f s" % (
                    len(rows), total, stride, dt))
     if total <= 64 and threads > 1:       # decode: the same rows on one thread as well
@@ -750,7 +774,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workloads", default="prefill_128K,decode_16M,chunked_1M,global_32K,backward_32K")
+    ap.add_argument("--workloads",
+                    default="prefill_128K,decode_16M,prefill_32K,chunked_1M,global_32K,backward_32K,crossover")
+    ap.add_argument("--crossover-max", type=int, default=CROSSOVER_DEFAULT_MAX,
+                    help="longest sequence of the crossover sweep (up to 1048576)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the 1 GiB calibration copy first (for counter passes)")
@@ -793,11 +820,12 @@ def main():
     crossover = None
     if "crossover" in names:
         names.remove("crossover")
-        crossover = bench_crossover(args.steps, args.warmup, timer)
+        crossover = bench_crossover(args.steps, args.warmup, timer,
+                                    lengths=tuple(L for L in CROSSOVER_LENGTHS if L <= args.crossover_max))
         if not names:
             print(json.dumps(crossover), flush=True)
             return
-    for name in ["decode_16M", "chunked_1M", "global_32K", "backward_32K", "prefill_128K"]:
+    for name in ["decode_16M", "prefill_32K", "chunked_1M", "global_32K", "backward_32K", "prefill_128K"]:
         if name in names:
             results[name] = bench_workload(name, args.steps, args.warmup, timer,
                                            not args.no_cpu_baseline)

@@ -42,6 +42,9 @@
  * allocating (hsa_workspace_init); every completed call leaves them zero.
  * `stream` is a hipStream_t (NULL: the default stream); calls only enqueue
  * work.  Concurrent calls on different streams need different workspaces.
+ * A call that returns HSA_ERR_DEVICE may have launched part of its kernels
+ * and left the counters non-zero: run hsa_workspace_init on the workspace
+ * again before its next use.
  *
  * Errors: all argument checks run on the host before any launch.  On any error
  * nothing is launched and no output is written.  HSA_ERR_DEVICE reports a

@@ -182,18 +182,40 @@ def new_workspace(nbytes: int, device):
     return ws
 
 
+def _cache_key(device):
+    """Workspaces are cached per (device, stream): calls on different streams
+    may overlap on the GPU, and the library requires each of them to have its
+    own workspace (arrival counters and partial buffers)."""
+    torch = _torch()
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    return index, torch.cuda.current_stream(device).cuda_stream
+
+
 def _workspace(shape, device, workspace=None):
     """The caller's workspace (which must have been initialised once), or a
-    cached one per device, grown as needed."""
+    cached one per (device, stream), grown as needed.  A replaced workspace
+    was only ever used on the same stream, so torch's stream-ordered allocator
+    hands its memory out again only after that stream's earlier work."""
     need = workspace_size(shape)
     if workspace is not None:
         return workspace, need
-    key = (device.index if device.index is not None else _torch().cuda.current_device())
+    key = _cache_key(device)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
         ws = new_workspace(need, device)
         _ws_cache[key] = ws
     return ws, need
+
+
+def _after_failure(status, ws, device, where):
+    """A call that failed on the device (HSA_ERR_DEVICE) may have left the
+    workspace's arrival counters non-zero; they are zeroed again
+    (hsa_workspace_init on the same stream) before the error is raised, so the
+    next call with this workspace starts clean.  Argument errors launch
+    nothing and leave the workspace as it was."""
+    if status == 5:
+        _load().hsa_workspace_init(_ptr(ws), ws.numel(), _stream(device))
+    raise HsaError(status, where)
 
 
 def _event_handle(ev) -> int:
@@ -253,11 +275,11 @@ def forward(q_ret, landmarks, q_attn, k, v, *, q_pos0: int, top_k: int, qk_norm:
     if stage_events is None:
         st = _load().hsa_forward(*args)
         if st:
-            raise HsaError(st, "hsa_forward")
+            _after_failure(st, ws, dev, "hsa_forward")
     else:
         st = _load().hsa_forward_profiled(*args, _stage_array(stage_events))
         if st:
-            raise HsaError(st, "hsa_forward_profiled")
+            _after_failure(st, ws, dev, "hsa_forward_profiled")
     return (out, idx, score) if return_topk else out
 
 
@@ -290,7 +312,7 @@ def retrieve_topk(q_ret, landmarks, *, q_pos0: int, top_k: int, kv_len: int | No
     st = _load().hsa_retrieve_topk(ctypes.byref(shape), _ptr(q_ret), _ptr(landmarks), _ptr(idx),
                                    _ptr(score), _ptr(ws), ws.numel(), _stream(dev))
     if st:
-        raise HsaError(st, "hsa_retrieve_topk")
+        _after_failure(st, ws, dev, "hsa_retrieve_topk")
     return idx, score
 
 
@@ -322,7 +344,7 @@ def chunk_attend_blend(q_attn, k, v, topk_idx, topk_score, *, qk_norm: bool = Tr
                                         _ptr(topk_idx), _ptr(topk_score), _ptr(out), _ptr(ws),
                                         ws.numel(), _stream(dev))
     if st:
-        raise HsaError(st, "hsa_chunk_attend_blend")
+        _after_failure(st, ws, dev, "hsa_chunk_attend_blend")
     return out
 
 
@@ -363,7 +385,7 @@ def backward(q_ret, landmarks, q_attn, k, v, topk_idx, topk_score, dout, *, qk_n
     Inputs as for forward / chunk_attend_blend (bf16), dout [B, Lq, Hq, d] bf16.
     Returns (dq_ret, dlandmarks, dq_attn, dk, dv), fp32, shaped like their
     inputs; `out` may supply them.  workspace: a uint8 GPU tensor of at least
-    backward_workspace_size() bytes (cached per device if None).  stage_events:
+    backward_workspace_size() bytes (cached per device and stream if None).  stage_events:
     as for forward (stages "bucket", "attend", "combine"; hsa_backward_profiled).
     """
     torch = _torch()
@@ -384,7 +406,7 @@ def backward(q_ret, landmarks, q_attn, k, v, topk_idx, topk_score, dout, *, qk_n
     dev = q_ret.device
     need = backward_workspace_size(shape)
     if workspace is None:
-        key = dev.index if dev.index is not None else torch.cuda.current_device()
+        key = _cache_key(dev)
         workspace = _bwd_ws_cache.get(key)
         if workspace is None or workspace.numel() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -14,7 +14,7 @@
 //   attend   per work item: K and V (row-major) in LDS, key norms once; per
 //            tile of 16 head-rows (16/G pairs x G heads): S = Q K^T on
 //            v_mfma_f32_16x16x32_bf16, in-chunk softmax across the tile's rows,
-//            P (times w_k, rounded to bf16) V on MFMA, fp16 partial per pair;
+//            P (times w_k, rounded to bf16) V on MFMA, bf16 partial per pair;
 //   combine  per row: the partials of its slots summed in slot order.
 // Results do not depend on the order of pairs inside a bin: every pair writes
 // only its own partial, and the combine order is fixed.
@@ -441,9 +441,11 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[st][e] = (__bf16)(s[2 * st + (e >> 2)][e & 3] * scale);
-    // O^T: lane holds dims 16*nt + 4*jg + i of head-row ma; fp16 partial, 8-byte stores
+    // O^T: lane holds dims 16*nt + 4*jg + i of head-row ma; bf16 partial, 8-byte
+    // stores.  bf16 keeps fp32's exponent range, so every finite partial
+    // (|w O| <= max |V| of the chunk) stays finite and normal.
     const bool live = pm < n_pairs;
-    __half* dst = a.partials + (live ? ((int64_t)pid_s[pm] * G + (ma % G)) * D : 0) + 4 * jg;
+    uint16_t* dst = a.partials + (live ? ((int64_t)pid_s[pm] * G + (ma % G)) * D : 0) + 4 * jg;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       floatx4 o = {0.f, 0.f, 0.f, 0.f};
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
         o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[st], o, 0, 0, 0);
       }
       if (live) {
-        const half2v h01 = {(_Float16)o[0], (_Float16)o[1]}, h23 = {(_Float16)o[2], (_Float16)o[3]};
+        const bf16x2 h01 = {(__bf16)o[0], (__bf16)o[1]}, h23 = {(__bf16)o[2], (__bf16)o[3]};
         *reinterpret_cast<uint2*>(dst + 16 * nt) =
             make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
       }
@@ -493,8 +495,8 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(ChunkArgs a) {
       const uint32_t wd[4] = {u[e].x, u[e].y, u[e].z, u[e].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += __half2float(__ushort_as_half((unsigned short)(wd[q] & 0xFFFFu)));
-        acc[2 * q + 1] += __half2float(__ushort_as_half((unsigned short)(wd[q] >> 16)));
+        acc[2 * q] += __uint_as_float(wd[q] << 16);
+        acc[2 * q + 1] += __uint_as_float(wd[q] & 0xFFFF0000u);
       }
     }
   }

@@ -1,7 +1,7 @@
 // attend_global.hip -- HSA with a top-K that covers every eligible chunk (the
 // "global HSA" of the warm-up stage in "Every Token Counts", agent-atlas
-// explainer, "Build Your Own" step 5: a large top-K covering the whole
-// sequence), bf16, G = 8 or 16 query heads per kv head.
+// explainer, "Build Your Own" step 5, where the top-K spans every eligible
+// chunk), bf16, G = 8 or 16 query heads per kv head.
 //
 // With every eligible chunk selected, Steps 2-4 reduce to: for each chunk c
 // before the query's own chunk, the in-chunk attention output O_c (Step 3)

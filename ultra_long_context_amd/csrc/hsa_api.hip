@@ -266,7 +266,7 @@ hsa_status_t launch_attend_blend(const Plan& p, const void* q_attn, const void* 
     c.item_start = nullptr;
     c.pairs = reinterpret_cast<uint32_t*>(w + p.off_cpairs);
     c.wts = reinterpret_cast<float*>(w + p.off_cwts);
-    c.partials = reinterpret_cast<__half*>(w + p.off_cparts);
+    c.partials = reinterpret_cast<uint16_t*>(w + p.off_cparts);
     c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
     c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
     c.band_rows = chunk_band_rows(); c.n_bands = p.n_bands;

@@ -136,12 +136,30 @@ namespace hsa {
 // ---------------------------------------------------------------------------
 // hand-off between workgroups of one kernel
 //
-// The per-XCD L2 caches are not coherent with each other.  Data that another
-// workgroup reads after an arrival-counter hand-off is written and read with
-// device-scope atomic accesses (sc1: write-through / re-fetch past the L2), and
-// each thread waits for its stores to complete before the barrier that
-// precedes the counter increment.  This gives the ordering of a release /
-// acquire pair without the full L2 write-back a device-scope fence costs.
+// Pattern: every thread of a producer workgroup stores its part with publish,
+// calls wait_stores, and the workgroup meets at a barrier; one thread then
+// calls arrive on the row's counter; the workgroup that sees the last count
+// meets at a barrier again and reads every part with fetch, then resets the
+// counter for the next call.
+//
+// Why the parts are complete when the last workgroup reads them:
+//  * In the HIP (scoped C++) memory model, the parts are relaxed device-scope
+//    atomics; the barrier makes each thread's store happen before the arriving
+//    thread's release (arrive is an acq_rel device-scope read-modify-write);
+//    the counter's modification order makes that release synchronise with the
+//    last workgroup's acquire (the same arrive), and its barrier makes the
+//    acquire happen before every fetch.  So every store happens before every
+//    fetch, and the fetches see the stored values.
+//  * On gfx950 this compiles to: publish = global_store ... sc1, which writes
+//    through the XCD's L2 to the device coherence point; wait_stores =
+//    s_waitcnt vmcnt(0), so each store has completed there before the barrier
+//    (a workgroup-scope barrier alone does not wait for global stores);
+//    arrive = buffer_wbl2 sc1 (L2 write-back; nothing of the hand-off is dirty
+//    in the L2, since the parts were written through) + atomic + buffer_inv
+//    sc1 (drops stale L2 lines); fetch = global_load ... sc1, which is served
+//    from the coherence point, not from a possibly stale line of this XCD's
+//    L2.  The L2s of different XCDs are not coherent with each other, which is
+//    why neither side may use plain cached accesses for the parts.
 // ---------------------------------------------------------------------------
 template <class T>
 __device__ __forceinline__ void publish(T* p, T v) {
@@ -154,7 +172,7 @@ __device__ __forceinline__ T fetch(const T* p) {
 // s_waitcnt vmcnt(0): every global store of this thread has completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ uint32_t arrive(uint32_t* ctr) {
-  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void reset_counter(uint32_t* ctr) {
   __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

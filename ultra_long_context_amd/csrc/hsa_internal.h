@@ -102,7 +102,7 @@ struct ChunkArgs {
   uint32_t* item_start;   // [n_bins] first work item of each bin, or nullptr
   uint32_t* pairs;        // [rows * K]    pair ids (row * K + slot), grouped by bin
   float* wts;             // [rows * K]    blend weights
-  __half* partials;       // [rows * K, G, D] weighted per-chunk outputs
+  uint16_t* partials;     // [rows * K, G, D] weighted per-chunk outputs (bf16)
   int64_t rows, Lq, Lkv, Nc, n_bins, max_items;
   int64_t band_rows, n_bands;   // bins split the query rows of a (batch, kv head) into bands
   int32_t pairs_per_item;       // work item size, at most 128 pairs
