@@ -35,7 +35,8 @@
  *
  * Ownership: every pointer is a caller-owned device pointer on the current HIP
  * device, 16-byte aligned; outputs must not alias inputs.  The library keeps
- * no state and allocates nothing: scratch memory is the caller's workspace
+ * no state and allocates nothing (hsa_forward_noalloc's static scratch array
+ * aside): scratch memory is the caller's workspace
  * (at least hsa_workspace_size() bytes, 256-byte aligned), which may be reused
  * by calls on the same stream, for any shape.  Its first 16 KiB hold arrival
  * counters that must be zero when a call starts: zero them once after
@@ -68,7 +69,8 @@ typedef enum {
   HSA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (d, G, K, dtype, flags) */
   HSA_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < hsa_workspace_size() */
   HSA_ERR_DEVICE = 5,              /* a HIP launch or runtime call failed */
-  HSA_ERR_MISALIGNED = 6           /* a pointer breaks the alignment rule */
+  HSA_ERR_MISALIGNED = 6,          /* a pointer breaks the alignment rule */
+  HSA_ERR_SCRATCH_TOO_SMALL = 7    /* hsa_forward_noalloc: shape needs more than the static scratch */
 } hsa_status_t;
 
 typedef enum { HSA_DTYPE_F32 = 0, HSA_DTYPE_BF16 = 1 } hsa_dtype_t;
@@ -129,6 +131,23 @@ hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret, const void
                          const void* q_attn, const void* k, const void* v, void* out,
                          int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* hsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments and results are those of hsa_forward; the
+ * workspace is a static device array inside the library, HSA_STATIC_SCRATCH_BYTES
+ * (16 MiB) per GPU, held until the process ends.  Shapes whose
+ * hsa_workspace_size() exceeds it are rejected with HSA_ERR_SCRATCH_TOO_SMALL
+ * before any launch (decode-sized calls fit: 16 query rows over a 16M-token
+ * history with top_k 32 need about 1.6 MiB; many-row prefills do not).  The
+ * call allocates nothing: on its first call on a device it takes the array's
+ * address and enqueues the zeroing of its counters on `stream`.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (e.g. on
+ * two streams) race; serialise them. */
+#define HSA_STATIC_SCRATCH_BYTES (16u << 20)
+hsa_status_t hsa_forward_noalloc(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
+                                 const void* q_attn, const void* k, const void* v, void* out,
+                                 int32_t* topk_idx, float* topk_score, void* stream);
 
 /* Backward of Steps 2-4 for a given selection: the gradients of
  * sum(out * dout) with respect to q_ret, landmarks, q_attn, k and v, where out

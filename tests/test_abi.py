@@ -38,8 +38,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(7):
+    for code in range(8):
         assert lib.hsa_status_string(code)
+        assert lib.hsa_status_string(code) != b"unknown status"
     assert lib.hsa_status_string(99) == b"unknown status"
     assert lib.hsa_version() == 100
 
@@ -222,3 +223,21 @@ def test_backward_checks_arguments():
     assert call(ws_ptr=ctypes.c_void_p(ws.ptr.value + 64)) == 6
     assert call(ws_bytes=need - 256) == 4
     assert lib.hsa_backward(None, *[b.ptr for b in bufs], ws.ptr, need, None) == 1
+
+
+def test_noalloc_rejects_shapes_beyond_the_static_scratch(lib):
+    """hsa_forward_noalloc checks the shape's workspace against its static
+    scratch on the host, before touching the device: a 32K-row prefill needs far
+    more than 16 MiB; invalid shapes fail as in hsa_forward."""
+    big = base(q_len=32768, kv_len=32768, q_pos0=0)
+    st, need = ws_size(big)
+    assert st == 0 and need > h.STATIC_SCRATCH_BYTES
+    p = ctypes.c_void_p(16)
+    assert lib.hsa_forward_noalloc(ctypes.byref(big), p, p, p, p, p, p, None, None, None) == 7
+    bad = base(head_dim=96)
+    assert lib.hsa_forward_noalloc(ctypes.byref(bad), p, p, p, p, p, p, None, None, None) == 3
+    assert lib.hsa_forward_noalloc(None, p, p, p, p, p, p, None, None, None) == 1
+    # decode-sized shapes fit the scratch
+    dec = base(batch=1, q_len=16, kv_len=1 << 24, q_pos0=1 << 24, top_k=32)
+    st, need = ws_size(dec)
+    assert st == 0 and need <= h.STATIC_SCRATCH_BYTES

@@ -17,7 +17,7 @@ import math
 import os
 import threading
 
-__all__ = ["HsaError", "HsaShape", "forward", "retrieve_topk", "chunk_attend_blend", "chunk_landmarks",
+__all__ = ["HsaError", "HsaShape", "forward", "forward_noalloc", "retrieve_topk", "chunk_attend_blend", "chunk_landmarks",
            "backward", "backward_workspace_size", "workspace_size", "new_workspace", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,7 @@ CHUNK = 64
 MAX_TOP_K = 64
 
 EXPORTED_SYMBOLS = ("hsa_workspace_size", "hsa_workspace_init", "hsa_retrieve_topk",
-                    "hsa_chunk_attend_blend", "hsa_forward", "hsa_forward_profiled",
+                    "hsa_chunk_attend_blend", "hsa_forward", "hsa_forward_profiled", "hsa_forward_noalloc",
                     "hsa_chunk_landmarks", "hsa_backward_workspace_size", "hsa_backward",
                     "hsa_backward_profiled",
                     "hsa_status_string", "hsa_version")
@@ -40,7 +40,9 @@ EXPORTED_SYMBOLS = ("hsa_workspace_size", "hsa_workspace_init", "hsa_retrieve_to
 STAGES = ("scan", "merge", "bucket", "attend", "combine")
 
 _STATUS = {0: "HSA_OK", 1: "HSA_ERR_NULL_POINTER", 2: "HSA_ERR_BAD_SHAPE", 3: "HSA_ERR_UNSUPPORTED",
-           4: "HSA_ERR_WORKSPACE_TOO_SMALL", 5: "HSA_ERR_DEVICE", 6: "HSA_ERR_MISALIGNED"}
+           4: "HSA_ERR_WORKSPACE_TOO_SMALL", 5: "HSA_ERR_DEVICE", 6: "HSA_ERR_MISALIGNED",
+           7: "HSA_ERR_SCRATCH_TOO_SMALL"}
+STATIC_SCRATCH_BYTES = 16 << 20   # HSA_STATIC_SCRATCH_BYTES (hsa_forward_noalloc)
 
 
 class HsaError(RuntimeError):
@@ -94,6 +96,8 @@ def _load():
             lib.hsa_forward_profiled.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                  ctypes.POINTER(vp)]
             lib.hsa_forward_profiled.restype = st
+            lib.hsa_forward_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.hsa_forward_noalloc.restype = st
             lib.hsa_chunk_landmarks.argtypes = [shp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
             lib.hsa_chunk_landmarks.restype = st
             lib.hsa_backward_workspace_size.argtypes = [shp, ctypes.POINTER(sz)]
@@ -281,6 +285,42 @@ def forward(q_ret, landmarks, q_attn, k, v, *, q_pos0: int, top_k: int, qk_norm:
         if st:
             _after_failure(st, ws, dev, "hsa_forward_profiled")
     return (out, idx, score) if return_topk else out
+
+
+def forward_noalloc(q_ret, landmarks, q_attn, k, v, out, *, q_pos0: int, top_k: int,
+                    qk_norm: bool = True, ret_scale: float | None = None,
+                    attn_scale: float | None = None, topk=None):
+    """hsa_forward_noalloc: the forward with the library's static scratch as its
+    workspace (no workspace argument; shapes needing more than
+    STATIC_SCRATCH_BYTES raise HSA_ERR_SCRATCH_TOO_SMALL).  `out` (and `topk`,
+    an optional (topk_idx, topk_score) pair) are caller-provided, so this
+    wrapper allocates nothing either.  Calls that overlap on one GPU race."""
+    torch = _torch()
+    for t, n in ((q_ret, "q_ret"), (landmarks, "landmarks"), (q_attn, "q_attn"), (k, "k"), (v, "v")):
+        _check(t, n, 4, q_ret.dtype)
+    _check(out, "out", 4, q_attn.dtype)
+    B, Lq, Hkv, d = q_ret.shape
+    Hq, Lkv = q_attn.shape[2], k.shape[2]
+    if (tuple(landmarks.shape) != (B, Hkv, Lkv // CHUNK, d) or tuple(q_attn.shape) != (B, Lq, Hq, d)
+            or tuple(k.shape) != (B, Hkv, Lkv, d) or tuple(v.shape) != tuple(k.shape)
+            or out.shape != q_attn.shape):
+        raise ValueError("inconsistent HSA input shapes")
+    idx = score = None
+    if topk is not None:
+        idx, score = topk
+        _check(idx, "topk_idx", 4, torch.int32)
+        _check(score, "topk_score", 4, torch.float32)
+        if tuple(idx.shape) != (B, Lq, Hkv, top_k) or score.shape != idx.shape:
+            raise ValueError("topk must be (topk_idx, topk_score) of shape [B, Lq, Hkv, K]")
+    shape = make_shape(batch=B, q_len=Lq, kv_len=Lkv, q_pos0=q_pos0, n_q_heads=Hq, n_kv_heads=Hkv,
+                       head_dim=d, top_k=top_k, dtype=_dtype_code(q_ret), qk_norm=qk_norm,
+                       ret_scale=ret_scale, attn_scale=attn_scale)
+    st = _load().hsa_forward_noalloc(ctypes.byref(shape), _ptr(q_ret), _ptr(landmarks), _ptr(q_attn),
+                                     _ptr(k), _ptr(v), _ptr(out), _ptr(idx), _ptr(score),
+                                     _stream(q_ret.device))
+    if st:
+        raise HsaError(st, "hsa_forward_noalloc")
+    return out
 
 
 def retrieve_topk(q_ret, landmarks, *, q_pos0: int, top_k: int, kv_len: int | None = None,

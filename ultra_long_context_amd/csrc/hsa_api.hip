@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "hsa.h"
 #include "hsa_internal.h"
@@ -560,6 +561,70 @@ HSA_EXPORT hsa_status_t hsa_backward_profiled(const hsa_shape_t* shape, const vo
                             dlandmarks, dq_attn, dk, dv, ws, ws_bytes, stream, mk);
 }
 
+// ---------------------------------------------------------------------------
+// hsa_forward_noalloc: hsa_forward with the library's own static scratch as
+// the workspace, for callers that cannot allocate device memory.
+//
+// `scratch` is one file-scope device array; every GPU the library runs on holds
+// its own copy until the process ends.  In host code its name is only a
+// stand-in for the symbol, so its device address is taken once per device with
+// hipGetSymbolAddress (that device current) and only that pointer is ever
+// passed to kernels.  The arrival counters at its start are zeroed once, by a
+// fill kernel, when the pointer is first taken on a device; every completed
+// call leaves them zero, and a call that fails on the device zeroes them again
+// (enqueued on its stream).  All calls on one GPU share the array: calls that
+// overlap on one GPU race.
+// ---------------------------------------------------------------------------
+namespace hsa {
+namespace {
+
+constexpr size_t kStaticScratchBytes = size_t(HSA_STATIC_SCRATCH_BYTES);
+constexpr int kMaxScratchDevices = 64;
+static_assert(kStaticScratchBytes >= kCounterBytes, "static scratch holds the counter region");
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch; on first use on a device
+// also enqueues the zeroing of its counter region on `st`.
+hsa_status_t static_scratch(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return HSA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return HSA_ERR_DEVICE;
+    if (launch_fill_u32(static_cast<uint32_t*>(p), (int64_t)(kCounterBytes / 4), 0u, st) != hipSuccess)
+      return HSA_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSA_OK;
+}
+
+}  // namespace
+}  // namespace hsa
+
+HSA_EXPORT hsa_status_t hsa_forward_noalloc(const hsa_shape_t* shape, const void* q_ret,
+                                            const void* landmarks, const void* q_attn, const void* k,
+                                            const void* v, void* out, int32_t* topk_idx,
+                                            float* topk_score, void* stream) {
+  hsa::Plan p;
+  hsa_status_t st = hsa::make_plan(shape, &p, true, true);
+  if (st != HSA_OK) return st;
+  if (p.total > hsa::kStaticScratchBytes) return HSA_ERR_SCRATCH_TOO_SMALL;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((st = hsa::static_scratch(s, &ws)) != HSA_OK) return st;
+  st = hsa::forward_impl(shape, q_ret, landmarks, q_attn, k, v, out, topk_idx, topk_score, ws,
+                         hsa::kStaticScratchBytes, stream, hsa::Marks{});
+  if (st == HSA_ERR_DEVICE)   // a partly launched call may have left counters non-zero
+    hsa::launch_fill_u32(static_cast<uint32_t*>(ws), (int64_t)(hsa::kCounterBytes / 4), 0u, s);
+  return st;
+}
+
 HSA_EXPORT const char* hsa_status_string(hsa_status_t status) {
   switch (status) {
     case HSA_OK: return "success";
@@ -569,6 +634,8 @@ HSA_EXPORT const char* hsa_status_string(hsa_status_t status) {
     case HSA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than hsa_workspace_size()";
     case HSA_ERR_DEVICE: return "HIP launch or runtime error";
     case HSA_ERR_MISALIGNED: return "pointer not 16-byte aligned (workspace: 256-byte)";
+    case HSA_ERR_SCRATCH_TOO_SMALL:
+      return "shape needs more workspace than the library's static scratch (HSA_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
