@@ -281,36 +281,152 @@ __global__ __launch_bounds__(64) void scan_topk_kernel(ScanArgs a) {
 // ---------------------------------------------------------------------------
 // Wide scan: few query rows over a long history (decode, appended rows).
 //
-// A workgroup of 16 waves scores one block of 16 rows against 1024 chunks in a
-// single pass: every wave issues all loads of its 64 landmarks at once, runs the
-// MFMA tiles and parks the 64x16 score keys in LDS.  Wave w then owns row w of
-// the block: its 64 lanes hold the row's 1024 keys (16 each), the K-th largest
-// lane maximum bounds the row's K-th key from below, and the few keys at or
-// above it are cut to the exact top K.  With one split the workgroup writes the
-// final selection; otherwise it writes one sorted list per row and split, which
-// a merge (merge_lists_kernel, or the decode attend's prologue) combines.  The
-// lists of a row are stored entry-major ([entry][split]), so the first entries
-// of every split are contiguous.
+// A workgroup of 16 waves scores one block of 16 rows against 1024 chunks.
+// Every wave issues the loads of its 64 landmarks up front; the chunks are then
+// taken in four quarters (sub-tile q of every wave, 256 chunks), so the
+// selection of one quarter runs while the next quarters' landmarks are still
+// in flight.  Per quarter: the waves run their MFMA tiles and park the 16x256
+// score keys in LDS (double-buffered); wave w then owns row w and folds the
+// quarter's keys into the row's candidates: a key enters only if it reaches
+// the K-th largest of the lanes' running maxima (K distinct chunks reach that
+// bound, so it never excludes a top-K key); the bound rises with every quarter
+// and the exact top K of the few survivors is taken once, after the last.
+// With one split the workgroup writes the final selection; otherwise it writes
+// one sorted list per row and split, which a merge (merge_lists_kernel, or the
+// decode attend's prologue) combines.  The lists of a row are stored
+// entry-major ([entry][split]), so the first entries of every split are
+// contiguous.
 // ---------------------------------------------------------------------------
 constexpr int kWideWaves = 16;
 constexpr int kWideChunksPerWave = 64;
 constexpr int kWideChunks = kWideWaves * kWideChunksPerWave;
-constexpr int kWideRowWords = kWideChunks + 4;     // padded LDS row (u32 keys)
-constexpr int kWideCandCap = 512;                  // u64 candidates that fit a row's LDS
+constexpr int kWideQuarter = kWideChunks / 4;      // chunks per quarter
+constexpr int kWideKeyWords = kWideQuarter + 4;    // padded LDS row of a quarter's u32 keys
+constexpr int kWideTmpCap = kMaxTopK + kWideQuarter;   // running list + one quarter's candidates
 
-// K-th largest of the wave's register-held u32 keys v[0..N) (multiplicity
-// counted); 0 if fewer than K are nonzero.
-template <int N>
-__device__ __forceinline__ uint32_t wave_kth_u32(const uint32_t (&v)[N], int K) {
-  uint32_t t = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = t | (1u << bit);
-    int c = 0;
+// Ranks of a and b among arr[0..n) in LDS (unique nonzero keys, n
+// wave-uniform): the number of entries above each.  Every lane reads the same
+// addresses (broadcast), eight entries in flight per step.
+__device__ __forceinline__ void lds_rank2(const uint64_t* arr, int n, uint64_t a, uint64_t b, int& ra, int& rb) {
+  ra = 0;
+  rb = 0;
+  for (int i0 = 0; i0 < n; i0 += 8) {
+    uint64_t x[8];
 #pragma unroll
-    for (int i = 0; i < N; ++i) c += wave_count(v[i] >= cand);
-    if (c >= K) t = cand;
+    for (int u = 0; u < 8; ++u) x[u] = arr[i0 + u < n ? i0 + u : n - 1];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = i0 + u < n;
+      ra += (in && x[u] > a) ? 1 : 0;
+      rb += (in && x[u] > b) ? 1 : 0;
+    }
   }
-  return t;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    v = u < v ? u : v;
+  }
+  return v;
+}
+
+// Running candidate set of one row over the quarters of a split (whole wave).
+// Admission: key >= tau, where tau is the upper 16 bits of the K-th largest
+// running lane maximum (K lanes, i.e. K distinct chunks, reach it, so it
+// bounds the row's K-th largest key from below and only rises), and packed
+// candidate > thr (0, or the exact K-th candidate after a cut).  T holds the
+// admitted candidates, n of them; entries that fall below a raised bound are
+// dropped when the buffer runs low, and if that is not enough the buffer is
+// cut to its exact top K.
+struct RowCands {
+  uint32_t lmx = 0;      // this lane's running maximum key
+  uint32_t tau = 0;
+  uint64_t thr = 0;
+  int n = 0;
+};
+
+// Keeps the entries of T[0..n) that can still be in the top K; returns their count.
+__device__ __forceinline__ int filter_cands(uint64_t* T, int n, uint32_t tau, uint64_t thr, int lane) {
+  int off = 0;
+  for (int p0 = 0; p0 < n; p0 += kWave) {
+    const int p = p0 + lane;
+    const uint64_t e = p < n ? T[p] : 0ull;
+    const bool keep = p < n && cand_key(e) >= tau && e >= thr;
+    const uint64_t mask = __ballot(keep);
+    // every lane has read its entry before any lane writes (same wave, in order)
+    if (keep) T[off + __popcll(mask & lanemask_lt())] = e;
+    off += __popcll(mask);
+  }
+  return off;
+}
+
+template <class ChunkOf>
+__device__ __forceinline__ void collect_quarter(const uint32_t (&v)[4], ChunkOf chunk_of, RowCands& rc, uint64_t* T,
+                                                int K, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rc.lmx = max(rc.lmx, v[i]);
+  const uint32_t m16 = rc.lmx >> 16;
+  uint32_t t16 = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t cand = t16 | (1u << bit);
+    if (wave_count(m16 >= cand) >= K) t16 = cand;
+  }
+  rc.tau = max(rc.tau, t16 << 16);
+  uint64_t e[4];
+  bool keep[4];
+  int nn = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    e[i] = pack_cand(v[i], (uint32_t)chunk_of(lane + kWave * i));
+    keep[i] = v[i] != 0u && v[i] >= rc.tau && e[i] > rc.thr;
+    nn += wave_count(keep[i]);
+  }
+  if (nn == 0) return;
+  if (rc.n + nn > kWideTmpCap) {
+    rc.n = filter_cands(T, rc.n, rc.tau, rc.thr, lane);
+    if (rc.n + nn > kWideTmpCap) {
+      // exact cut to the top K; later candidates must beat its K-th entry
+      rc.n = wave_keep_top<kWideTmpCap / kWave>(T, rc.n, K, lane);
+      uint64_t mn = ~0ull;
+      for (int p = lane; p < rc.n; p += kWave) mn = T[p] < mn ? T[p] : mn;
+      rc.thr = wave_min_u64(mn);
+      nn = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        keep[i] = keep[i] && e[i] > rc.thr;
+        nn += wave_count(keep[i]);
+      }
+    }
+  }
+  int off = rc.n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint64_t mask = __ballot(keep[i]);
+    if (keep[i]) T[off + __popcll(mask & lanemask_lt())] = e[i];
+    off += __popcll(mask);
+  }
+  rc.n = off;
+}
+
+// Exact top K of the row's candidates, sorted best first into L; returns m.
+__device__ __forceinline__ int finish_cands(RowCands& rc, uint64_t* T, uint64_t* L, int K, int lane) {
+  const int n = filter_cands(T, rc.n, rc.tau, rc.thr, lane);
+  if (n <= 2 * kWave) {
+    const uint64_t a = lane < n ? T[lane] : 0ull;
+    const uint64_t b = lane + kWave < n ? T[lane + kWave] : 0ull;
+    int ra = 0, rb = 0;
+    if (n <= kWave) ra = lds_rank(T, n, a);
+    else lds_rank2(T, n, a, b, ra, rb);
+    if (lane < n && ra < K) L[ra] = a;
+    if (lane + kWave < n && rb < K) L[rb] = b;
+    return n < K ? n : K;
+  }
+  const int mm = wave_keep_top<kWideTmpCap / kWave>(T, n, K, lane);
+  wave_rank_sort(T, mm, L, lane);
+  return mm;
 }
 
 // Writes a row's final selection (sorted top[0..m), padding after it).
@@ -332,8 +448,12 @@ template <bool BF16, int D>
 __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
   using T = typename Elem<BF16>::T;
   constexpr int LOADS = BF16 ? D / 32 : D / 16;
-  __shared__ __align__(16) uint32_t S[kWideWaves][kWideRowWords];
-  __shared__ uint64_t top[kWideWaves][kMaxTopK];
+  // sub-tiles whose landmark loads are in flight ahead of their use (bf16: all
+  // four, the wave's whole 16 KiB; fp32: as many as the registers allow)
+  constexpr int PF = BF16 ? 4 : (D == 128 ? 1 : 2);
+  __shared__ __align__(16) uint32_t S[2][kWideWaves][kWideKeyWords];
+  __shared__ uint64_t lst[kWideWaves][kMaxTopK];
+  __shared__ uint64_t tmp[kWideWaves][kWideTmpCap];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qrow = lane & 15, j = lane >> 4;
   const int s = blockIdx.y;
@@ -343,150 +463,87 @@ __global__ __launch_bounds__(1024) void scan_wide_kernel(ScanArgs a) {
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int c_begin = s * kWideChunks;
   const int c_end = min(c_begin + kWideChunks, a.n_max);
+  const int K = a.K;
 
-  // --- scores of this wave's 64 chunks for the block's 16 rows -------------
-  {
-    const int64_t r = rb * kRows + qrow;
-    const bool row_ok = r < a.Lq;
-    int lim = 0;
-    if (row_ok) {
-      const int64_t n = (a.q_pos0 + r) / kChunk;
-      lim = min((int)(n < a.Nc ? n : a.Nc), c_end);
-    }
-    QOperand<BF16, D> q;
-    q.load(reinterpret_cast<const T*>(a.q_ret) + ((b * a.Lq + (row_ok ? r : 0)) * a.Hkv + g) * D,
-           row_ok, j);
-    // with no eligible chunk at all (then c_begin == c_end == 0) the loads read
-    // the first query row instead: an address that is always valid
-    const T* lm = c_begin < c_end ? reinterpret_cast<const T*>(a.landmarks) + (int64_t)bg * a.Nc * D
-                                  : reinterpret_cast<const T*>(a.q_ret);
-    const int cw = c_begin + w * kWideChunksPerWave;
-    // landmark loads of GRP sub-tiles are all issued before their MFMAs
-    // (GRP = 4 for bf16: the wave's whole 16 KiB in flight at once)
-    constexpr int GRP = BF16 ? 4 : (D == 128 ? 1 : 2);
-#pragma unroll
-    for (int s0 = 0; s0 < 4; s0 += GRP) {
-      uint4 x[GRP][LOADS];
-#pragma unroll
-      for (int u = 0; u < GRP; ++u) {
-        // chunks past c_end load chunk c_begin instead (their keys are masked):
-        // unconditional loads are all in flight at once
-        const int cc0 = cw + (s0 + u) * 16 + qrow;
-        const int cc = cc0 < c_end ? cc0 : c_begin;
-        const T* p = lm + (int64_t)cc * D + (BF16 ? 8 : 4) * j;
-#pragma unroll
-        for (int t = 0; t < LOADS; ++t) x[u][t] = *reinterpret_cast<const uint4*>(p + (BF16 ? 32 : 16) * t);
-      }
-#pragma unroll
-      for (int u = 0; u < GRP; ++u) {
-        const int sub = s0 + u;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < LOADS; ++t) {
-          if constexpr (BF16) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[u][t]),
-                                                          q.v[t], acc, 0, 0, 0);
-          } else {
-            const float4 f = __builtin_bit_cast(float4, x[u][t]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.x, q.v[t].x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.y, q.v[t].y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.z, q.v[t].z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.w, q.v[t].w, acc, 0, 0, 0);
-          }
-        }
-        uint4 kv;
-        const int c0 = cw + sub * 16 + 4 * j;
-        kv.x = c0 + 0 < lim ? score_key(acc[0]) : 0u;
-        kv.y = c0 + 1 < lim ? score_key(acc[1]) : 0u;
-        kv.z = c0 + 2 < lim ? score_key(acc[2]) : 0u;
-        kv.w = c0 + 3 < lim ? score_key(acc[3]) : 0u;
-        *reinterpret_cast<uint4*>(&S[qrow][w * kWideChunksPerWave + sub * 16 + 4 * j]) = kv;
-      }
-    }
+  const int64_t r = rb * kRows + qrow;
+  const bool row_ok = r < a.Lq;
+  int lim = 0;
+  if (row_ok) {
+    const int64_t n = (a.q_pos0 + r) / kChunk;
+    lim = min((int)(n < a.Nc ? n : a.Nc), c_end);
   }
-  __syncthreads();
+  // with no eligible chunk at all (then c_begin == c_end == 0) the loads read
+  // the first query row instead: an address that is always valid
+  const T* lm = c_begin < c_end ? reinterpret_cast<const T*>(a.landmarks) + (int64_t)bg * a.Nc * D
+                                : reinterpret_cast<const T*>(a.q_ret);
+  const int cw = c_begin + w * kWideChunksPerWave;
+  uint4 x[4][LOADS];
+  auto issue = [&](int sub) {
+    // chunks past c_end load chunk c_begin instead (their keys are masked):
+    // unconditional loads are all in flight at once
+    const int cc0 = cw + sub * 16 + qrow;
+    const int cc = cc0 < c_end ? cc0 : c_begin;
+    const T* p = lm + (int64_t)cc * D + (BF16 ? 8 : 4) * j;
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t) x[sub][t] = *reinterpret_cast<const uint4*>(p + (BF16 ? 32 : 16) * t);
+  };
+  // the retrieval queries first (loads complete in order, and the first
+  // quarter needs them), unconditionally: rows past Lq have lim = 0, so all
+  // their keys are masked and their query values never matter
+  QOperand<BF16, D> q;
+  q.load(reinterpret_cast<const T*>(a.q_ret) + ((b * a.Lq + (row_ok ? r : 0)) * a.Hkv + g) * D, true, j);
+#pragma unroll
+  for (int sub = 0; sub < PF; ++sub) issue(sub);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // --- wave w: exact top K of row w over the workgroup's 1024 chunks --------
+  // candidates of row w (wave w)
   const int64_t rw = rb * kRows + w;
   const bool rw_ok = rw < a.Lq;
-  const int K = a.K;
-  uint64_t* C = reinterpret_cast<uint64_t*>(&S[w][0]);
-  uint32_t v[16];
-  uint32_t mx = 0;
+  RowCands rc;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = S[w][lane + kWave * i];
-    mx = max(mx, v[i]);
-  }
-  uint32_t tau = 0;                 // K lane maxima reach tau (upper 16 key bits)
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    if (__popcll(__ballot((mx >> 16) >= cand)) >= K) tau = cand;
-  }
-  tau <<= 16;
-  int total = 0;
+  for (int qt = 0; qt < 4; ++qt) {
+    if (qt + PF < 4) issue(qt + PF);
+    // --- scores of quarter qt: sub-tile qt of every wave --------------------
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) total += wave_count(v[i] != 0u && v[i] >= tau);
-  uint32_t need_at = 0xFFFFFFFFu;   // exact path: ties at the threshold admitted in chunk order
-  int need = 0;
-  if (total > kWideCandCap) {
-    tau = wave_kth_u32<16>(v, K);
-    int above = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) above += wave_count(v[i] > tau);
-    need = K - above;
-    need_at = tau;
-  }
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    bool keep = v[i] != 0u && (need_at == 0xFFFFFFFFu ? v[i] >= tau : v[i] > tau);
-    if (need_at != 0xFFFFFFFFu) {
-      const bool tie = v[i] != 0u && v[i] == need_at;
-      const uint64_t tm = __ballot(tie);
-      const int before = (int)__popcll(tm & lanemask_lt());
-      keep = keep || (tie && before < need);
-      const int nt = (int)__popcll(tm);
-      need -= need < nt ? need : nt;
+    for (int t = 0; t < LOADS; ++t) {
+      if constexpr (BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[qt][t]), q.v[t], acc, 0, 0, 0);
+      } else {
+        const float4 f = __builtin_bit_cast(float4, x[qt][t]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.x, q.v[t].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.y, q.v[t].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.z, q.v[t].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.w, q.v[t].w, acc, 0, 0, 0);
+      }
     }
-    const uint64_t mask = __ballot(keep);
-    if (keep) C[n + __popcll(mask & lanemask_lt())] = pack_cand(v[i], (uint32_t)(c_begin + lane + kWave * i));
-    n += __popcll(mask);
+    uint4 kv;
+    const int c0 = cw + qt * 16 + 4 * j;
+    kv.x = c0 + 0 < lim ? score_key(acc[0]) : 0u;
+    kv.y = c0 + 1 < lim ? score_key(acc[1]) : 0u;
+    kv.z = c0 + 2 < lim ? score_key(acc[2]) : 0u;
+    kv.w = c0 + 3 < lim ? score_key(acc[3]) : 0u;
+    // quarter entry w*16 + 4j + i <-> chunk c_begin + w*64 + qt*16 + 4j + i
+    *reinterpret_cast<uint4*>(&S[qt & 1][qrow][w * 16 + 4 * j]) = kv;
+    // one barrier per quarter: the other buffer was last read before it
+    __syncthreads();
+    // --- wave w adds the quarter's candidates of row w -----------------------
+    uint32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = S[qt & 1][w][lane + kWave * i];
+    collect_quarter(v, [&](int xq) { return c_begin + (xq >> 4) * kWideChunksPerWave + qt * 16 + (xq & 15); },
+                    rc, tmp[w], K, lane);
   }
+  const int m = finish_cands(rc, tmp[w], lst[w], K, lane);
+
+  if (!rw_ok) return;
   const int64_t row_flat = (b * a.Lq + rw) * a.Hkv + g;
-  if (n <= kWave) {                 // one candidate per lane: rank them in registers
-    const uint64_t e = lane < n ? C[lane] : 0ull;
-    const int rank = lds_rank(C, n, e);
-    const int m = n < K ? n : K;
-    if (!rw_ok) return;
-    if (a.n_splits == 1) {
-      int32_t* idx = a.out_idx + row_flat * K;
-      float* score = a.out_score + row_flat * K;
-      if (lane < n && rank < K) {
-        idx[rank] = (int32_t)cand_chunk(e);
-        score[rank] = key_score(cand_key(e)) * a.ret_scale;
-      }
-      if (lane >= m && lane < K) {
-        idx[lane] = -1;
-        score[lane] = -INFINITY;
-      }
-    } else {
-      // entry-major lists: entry j of split s at [row][j][s]
-      uint64_t* list = a.lists + row_flat * a.n_splits * K + s;
-      if (lane < n && rank < K) list[(int64_t)rank * a.n_splits] = e;
-      if (lane >= m && lane < K) list[(int64_t)lane * a.n_splits] = 0ull;
-    }
-    return;
-  }
-  const int m = wave_keep_top<kWideCandCap / kWave>(C, n, K, lane);
-  wave_rank_sort(C, m, top[w], lane);
   if (a.n_splits == 1) {
-    if (rw_ok) write_selection(top[w], m, K, lane, a.out_idx + row_flat * K, a.out_score + row_flat * K,
-                               a.ret_scale);
+    write_selection(lst[w], m, K, lane, a.out_idx + row_flat * K, a.out_score + row_flat * K, a.ret_scale);
     return;
   }
-  if (rw_ok && lane < K)
-    a.lists[row_flat * a.n_splits * K + (int64_t)lane * a.n_splits + s] = lane < m ? top[w][lane] : 0ull;
+  // entry-major lists: entry j of split s at [row][j][s]
+  if (lane < K) a.lists[row_flat * a.n_splits * K + (int64_t)lane * a.n_splits + s] = lane < m ? lst[w][lane] : 0ull;
 }
 
 // ---------------------------------------------------------------------------
