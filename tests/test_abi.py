@@ -61,7 +61,8 @@ def ws_size(shape):
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 2), (dict(q_len=0), 2), (dict(kv_len=-1), 2), (dict(q_pos0=-5), 2),
     (dict(n_q_heads=7, n_kv_heads=2), 2), (dict(n_q_heads=3, n_kv_heads=1), 3), (dict(n_q_heads=64), 3),
-    (dict(head_dim=96), 3), (dict(top_k=0), 2), (dict(top_k=65, n_q_heads=4), 3),
+    (dict(head_dim=96), 3), (dict(top_k=0), 2), (dict(top_k=65, n_q_heads=4), 0),
+    (dict(top_k=65, n_q_heads=1), 0),
     (dict(top_k=65, dtype=h.DTYPE_F32), 3), (dict(top_k=65, kv_len=1 << 20, q_pos0=1 << 19), 3),
     (dict(dtype=7), 3),
 ])
@@ -174,7 +175,7 @@ def test_chunk_landmarks_checks_arguments():
 
 def test_global_top_k_planning():
     """top_k above 64 is global HSA: only when it covers every row's eligible
-    chunks (bf16, G = 8 or 16), only through hsa_forward, without selection
+    chunks (bf16, any supported G), only through hsa_forward, without selection
     outputs; it needs only the counter region of the workspace."""
     st, n = ws_size(base(top_k=65))
     assert st == 0 and n == 16384

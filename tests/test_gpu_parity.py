@@ -591,7 +591,8 @@ def global_parity(hsa, inp, K, rows=None):
     return out
 
 
-@pytest.mark.parametrize("G,d", [(8, 128), (16, 128), (8, 64), (16, 64)])
+@pytest.mark.parametrize("G,d", [(8, 128), (16, 128), (8, 64), (16, 64), (1, 128), (2, 128), (4, 128),
+                                 (1, 64), (2, 64), (4, 64)])
 def test_global_hsa_prefill(hsa, G, d):
     """Every eligible chunk selected (K > 64): dense in-chunk attention blended
     by the softmax of all retrieval scores; early rows have no chunk (zero)."""
@@ -604,6 +605,15 @@ def test_global_hsa_appended_rows_and_batch(hsa):
     cfg = small(batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, q_len=700, q_pos0=2083, kv_len=2816,
                 top_k=8, seed=43)
     global_parity(hsa, W.generate(cfg), K=65, rows=sample_rows(cfg, 300, seed=3))
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (4, 2)])
+def test_global_hsa_small_groups_appended_rows(hsa, G, Hkv):
+    """G = 1, 2, 4 (256, 128, 64 rows per workgroup): appended rows over a longer
+    history, several kv heads, two sequences."""
+    cfg = small(batch=2, n_kv_heads=Hkv, n_q_heads=G * Hkv, head_dim=128, q_len=600, q_pos0=2500,
+                kv_len=3100, top_k=8, seed=60 + G)
+    global_parity(hsa, W.generate(cfg), K=100, rows=sample_rows(cfg, 240, seed=G))
 
 
 def test_global_hsa_uniform_scores_equal_chunk_mean(hsa):

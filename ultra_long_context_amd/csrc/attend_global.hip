@@ -1,7 +1,7 @@
 // attend_global.hip -- HSA with a top-K that covers every eligible chunk (the
 // "global HSA" of the warm-up stage in "Every Token Counts", agent-atlas
 // explainer, "Build Your Own" step 5, where the top-K spans every eligible
-// chunk), bf16, G = 8 or 16 query heads per kv head.
+// chunk), bf16, G = 1, 2, 4, 8 or 16 query heads per kv head.
 //
 // With every eligible chunk selected, Steps 2-4 reduce to: for each chunk c
 // before the query's own chunk, the in-chunk attention output O_c (Step 3)
@@ -9,14 +9,16 @@
 // the blend runs as an online softmax over the chunks:
 //   m' = max(m, s_c),  l' = l 2^(m-m') + 2^(s_c-m'),  acc' = acc 2^(m-m') + 2^(s_c-m') O_c,
 // out = acc / l (scores in base 2).  A workgroup of 16 waves owns 256/G
-// consecutive query rows of one (batch, kv head) (16 head-rows per wave) and
+// consecutive query rows of one (batch, kv head) (16 head-rows per wave: 16/G
+// rows of G heads) and
 // streams their eligible chunks: each chunk's K and V (row-major) are staged in
 // LDS once for all 256 head-rows, double-buffered so the next chunk's loads are
 // in flight during the current one; S^T = K Q^T and O^T += V^T P^T run on
 // v_mfma_f32_16x16x32_bf16, V^T read with LDS transpose loads, with P (times
 // the chunk's blend factor, over the in-chunk sum, rounded to bf16) fed from
 // registers.  Retrieval scores of the block's rows come 64 chunks at a
-// time from the same MFMA, landmarks as the A operand.
+// time (32 when G <= 2, the block then holding 128 or 256 rows) from the same
+// MFMA, landmarks as the A operand, 16 rows x 16 chunks per wave task.
 #include "hsa_device.h"
 #include "hsa_internal.h"
 
@@ -25,18 +27,19 @@ namespace {
 
 constexpr int kGWaves = 16;
 constexpr int kGThreads = kGWaves * 64;
-constexpr int kGTile = 64;                     // landmarks (chunks) per score tile
 constexpr float kLog2eG = 1.4426950408889634f;
 
 template <int D, int G>
 __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) {
   constexpr int R = 256 / G;                   // query rows per workgroup
+  // landmarks (chunks) per score tile: the scores of R rows x kGTile chunks sit in LDS
+  constexpr int kGTile = G <= 2 ? 32 : 64;
+  constexpr int kScoreTasks = (R / 16) * (kGTile / 16);   // 16 rows x 16 chunks each
   constexpr int KROW = D + 16, VROW = D + 16, LROW = D + 16;   // 288-byte rows: no LDS bank conflicts
   constexpr int KSTEP = D / 32, NT = D / 16;
   constexpr int TPR = 16 / G;                  // rows per 16-head-row tile (G = 8: 2, G = 16: 1)
   __shared__ __align__(16) uint16_t ks[2][kChunk * KROW];
   __shared__ __align__(16) uint16_t vs[2][kChunk * VROW];   // V rows, read back transposed
-  __shared__ float rk[2][kChunk];
   __shared__ __align__(16) uint16_t lt[kGTile * LROW];
   __shared__ float sc[R][kGTile + 1];          // base-2 retrieval scores, -inf past the row's chunks
 
@@ -81,7 +84,19 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
   }
   qss += __shfl_xor(qss, 16, kWave);
   qss += __shfl_xor(qss, 32, kWave);
-  const float rq = (a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f) * a.attn_scale * kLog2eG;
+  // the query factor (normalisation, attention scale, log2 e) is folded into
+  // the query operand once: S comes out of the MFMA as base-2 logits
+  {
+    const float rq = (a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f) * a.attn_scale * kLog2eG;
+#pragma unroll
+    for (int t = 0; t < KSTEP; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qa[t][e] = (__bf16)((float)qa[t][e] * rq);
+  }
+  // With query-key normalisation every logit is at most attn_scale * log2 e in
+  // magnitude, so exp2 cannot overflow without subtracting the maximum (the
+  // softmax is shift-invariant); otherwise the in-chunk maximum is subtracted.
+  const bool bounded = a.qk_norm && a.attn_scale * kLog2eG <= 64.0f;
 
   // K / V staging: each thread one 16-byte piece of K and one of V (8 dims of
   // one key), both row-major; the P.V operand is read from V with LDS
@@ -98,22 +113,26 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
   auto store_kv = [&](int bi) {
     if (tid < NKP) {
       const int key = tid * 8 / D, d0 = (tid * 8) % D;
-      *reinterpret_cast<uint4*>(&ks[bi][key * KROW + d0]) = kx;
-      // key norm: the D/8 consecutive lanes holding this key add their squares
-      float ss = 0.f;
-      {
+      bf16x8 kb = __builtin_bit_cast(bf16x8, kx);
+      if (a.qk_norm) {
+        // key norm: the D/8 consecutive lanes holding this key add their
+        // squares; the normalised key is staged (rounded to bf16)
+        float ss = 0.f;
         const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bf16x2 v2 = __builtin_bit_cast(bf16x2, kw[q]);
           ss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss, false);
         }
+        ss += dpp_f<0xB1>(ss);             // xor 1
+        ss += dpp_f<0x4E>(ss);             // xor 2
+        ss += dpp_f<0x141>(ss);            // half-row mirror: 8 lanes
+        if constexpr (D == 128) ss += dpp_f<0x140>(ss);   // row mirror: 16 lanes
+        const float rk = 1.0f / fmaxf(sqrtf(ss), 1e-6f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kb[e] = (__bf16)((float)kb[e] * rk);
       }
-      ss += dpp_f<0xB1>(ss);               // xor 1
-      ss += dpp_f<0x4E>(ss);               // xor 2
-      ss += dpp_f<0x141>(ss);              // half-row mirror: 8 lanes
-      if constexpr (D == 128) ss += dpp_f<0x140>(ss);   // row mirror: 16 lanes
-      if (d0 == 0) rk[bi][key] = a.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
+      *reinterpret_cast<uint4*>(&ks[bi][key * KROW + d0]) = __builtin_bit_cast(uint4, kb);
       *reinterpret_cast<uint4*>(&vs[bi][key * VROW + d0]) = vx;
     }
   };
@@ -140,8 +159,8 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
         }
       }
       __syncthreads();
-      if (w < (R / 16) * 4) {                  // wave: 16 rows x 16 chunks
-        const int rt = w >> 2, ct = w & 3;
+      for (int task = w; task < kScoreTasks; task += kGWaves) {   // 16 rows x 16 chunks
+        const int rt = task / (kGTile / 16), ct = task % (kGTile / 16);
         const int64_t qr = r0 + 16 * rt + ma;
         const bool ok = qr < a.Lq;
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_ret) +
@@ -178,19 +197,16 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    float mx = -INFINITY;
+    float mx = 0.f;
+    if (!bounded) {
+      mx = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const float4 r4 = *reinterpret_cast<const float4*>(&rk[cb][16 * nt + 4 * jg]);
-      const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s4[nt][i] = s4[nt][i] * rq * rr[i];
-        mx = fmaxf(mx, s4[nt][i]);
-      }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s4[nt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     float sum = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -264,7 +280,9 @@ hipError_t launch_attend_global(const GlobalArgs& a, int64_t B, int D, int G, hi
     hipLaunchKernelGGL((attend_global_kernel<DD, GG>), grid, block, 0, st, a);   \
     return hipGetLastError();                                                    \
   }
-  HSA_GLOBAL_CASE(128, 8) HSA_GLOBAL_CASE(128, 16) HSA_GLOBAL_CASE(64, 8) HSA_GLOBAL_CASE(64, 16)
+  HSA_GLOBAL_CASE(128, 1) HSA_GLOBAL_CASE(128, 2) HSA_GLOBAL_CASE(128, 4) HSA_GLOBAL_CASE(128, 8)
+  HSA_GLOBAL_CASE(128, 16) HSA_GLOBAL_CASE(64, 1) HSA_GLOBAL_CASE(64, 2) HSA_GLOBAL_CASE(64, 4)
+  HSA_GLOBAL_CASE(64, 8) HSA_GLOBAL_CASE(64, 16)
 #undef HSA_GLOBAL_CASE
   return hipErrorInvalidValue;
 }

@@ -95,7 +95,7 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool
   p->n_max = (int32_t)nmax;
   p->global = false;
   if (big_k) {   // every eligible chunk selected: no top-K, no selection arrays
-    if (!p->bf16 || (G != 8 && G != 16) || s->top_k < nmax) return HSA_ERR_UNSUPPORTED;
+    if (!p->bf16 || s->top_k < nmax) return HSA_ERR_UNSUPPORTED;
     p->global = true;
     p->wide = p->block = false;
     p->n_splits = 1;
