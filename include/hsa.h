@@ -158,7 +158,9 @@ hsa_status_t hsa_forward_noalloc(const hsa_shape_t* shape, const void* q_ret, co
  * (Technically)"), and q_attn, k, v through each chunk's softmax attention
  * (Step 3), including the query-key L2 normalisation when the flag is set
  * (gradient of x / max(|x|, 1e-6)).
- * bf16 inputs only (HSA_ERR_UNSUPPORTED otherwise), top_k <= 64.
+ * bf16 inputs only (HSA_ERR_UNSUPPORTED otherwise).  top_k may exceed 64:
+ * the warm-up stage's global HSA (top-K spanning every eligible chunk) is
+ * differentiated by passing the selection of every eligible chunk.
  *   topk_idx, topk_score [B, Lq, Hkv, top_k] as for hsa_chunk_attend_blend
  *                (slots outside [0, Nc) are unused).
  *   dout         [B, Lq, Hq, d] bf16.

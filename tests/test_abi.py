@@ -199,7 +199,8 @@ def test_backward_checks_arguments():
     st, need = bsize(base())
     assert st == 0 and need > 0 and need % 256 == 0
     assert bsize(base(dtype=h.DTYPE_F32))[0] == 3                     # bf16 only
-    assert bsize(base(top_k=65))[0] == 3                              # no global-HSA backward
+    assert bsize(base(top_k=65))[0] == 0                              # any number of slots
+    assert bsize(base(top_k=4096))[0] == 0
     assert bsize(base(head_dim=96))[0] == 3
     assert lib.hsa_backward_workspace_size(ctypes.byref(base()), None) == 1
     # larger problems need more workspace (per-pair and per-item buffers)

@@ -230,3 +230,24 @@ def test_backward_profiled_matches(hsa):
         assert torch.equal(x, y)
     for n in ("bucket", "attend", "combine"):
         assert evs[n][0].elapsed_time(evs[n][1]) > 0, n
+
+
+# ----------------------------------------------------------------------------
+# the warm-up stage's global HSA: a selection of every eligible chunk (K > 64)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,Hkv,d,qk_norm,q_len,kv_len,q_pos0", [
+    (8, 1, 128, True, 768, 6144, 5376),       # 84..95 eligible chunks per row, K = 96
+    (4, 2, 64, True, 4608, 4608, 0),          # prefill: 0..71 eligible chunks, K = 72
+    (16, 1, 128, False, 300, 8448, 8148),     # K = 132, no query-key normalisation
+])
+def test_backward_every_eligible_chunk(hsa, G, Hkv, d, qk_norm, q_len, kv_len, q_pos0):
+    """hsa_backward for a selection listing every eligible chunk (the oracle's
+    forward with top_k >= the number of eligible chunks): more than 64 slots
+    per row, the case global HSA trains with."""
+    n_max = min((q_pos0 + q_len - 1) // 64, kv_len // 64)
+    K = n_max + 1
+    cfg = small(q_len=q_len, kv_len=kv_len, q_pos0=q_pos0, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d,
+                qk_norm=qk_norm, top_k=K, seed=70 + G)
+    assert K > 64
+    full_parity(hsa, cfg)

@@ -64,6 +64,48 @@ __global__ __launch_bounds__(256) void chunk_count_kernel(ChunkArgs a) {
   if (valid) atomicAdd(&a.counts[bin_of(row, c, a)], 1u);
 }
 
+// --- more than 64 slots per row (a selection of every eligible chunk) ---------
+// Blend weights with one wave per row (slots strided over the lanes; the
+// maximum and the sum are reduced in a fixed order), and the bin histogram and
+// scatter with one thread per (row, slot) pair.
+__global__ __launch_bounds__(256) void chunk_wts_wide_kernel(ChunkArgs a) {
+  const int K = a.K, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int32_t* idx = a.idx + row * K;
+  const float* sc = a.score + row * K;
+  float mx = -INFINITY;
+  for (int k = lane; k < K; k += kWave) {
+    const int32_t c = idx[k];
+    if (c >= 0 && (int64_t)c < a.Nc) mx = fmaxf(mx, sc[k]);
+  }
+  mx = wave_max(mx);
+  float den = 0.f;
+  for (int k = lane; k < K; k += kWave) {
+    const int32_t c = idx[k];
+    if (c >= 0 && (int64_t)c < a.Nc) den += expf(sc[k] - mx);
+  }
+  den = wave_sum(den);
+  for (int k = lane; k < K; k += kWave) {
+    const int32_t c = idx[k];
+    a.wts[row * K + k] = (c >= 0 && (int64_t)c < a.Nc) ? expf(sc[k] - mx) / den : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256) void chunk_count_pairs_kernel(ChunkArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.rows * a.K) return;
+  const int32_t c = a.idx[t];
+  if (c >= 0 && (int64_t)c < a.Nc) atomicAdd(&a.counts[bin_of(t / a.K, c, a)], 1u);
+}
+
+__global__ __launch_bounds__(256) void chunk_scatter_pairs_kernel(ChunkArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.rows * a.K) return;
+  const int32_t c = a.idx[t];
+  if (c >= 0 && (int64_t)c < a.Nc) a.pairs[atomicAdd(&a.cursor[bin_of(t / a.K, c, a)], 1u)] = (uint32_t)t;
+}
+
 // --- bucketing through a workgroup histogram in LDS --------------------------
 // A workgroup takes kBucketRows query rows of one (batch, kv head), counts its
 // pairs per chunk in LDS and adds each nonzero count to the global bin once, so
@@ -532,12 +574,20 @@ int64_t chunk_band_rows() { return kBandRows; }
 hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st) {
   hipError_t e;
   if ((e = launch_fill_u32(a.counts, a.n_bins, 0u, st)) != hipSuccess) return e;
-  const bool lds = a.Nc <= kHistMax;
-  const int64_t seg = a.K <= 1 ? 1 : (int64_t)1 << (32 - __builtin_clz((unsigned)a.K - 1));
+  const bool wide = a.K > kWave;                 // more slots than lanes in a wave
+  const bool lds = !wide && a.Nc <= kHistMax;
+  const unsigned pair_blocks = (unsigned)((a.rows * a.K + 255) / 256);
+  if (wide) {
+    hipLaunchKernelGGL(chunk_wts_wide_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // rows per 256-thread block of the one-lane-per-slot kernels (K <= 64 there)
+  const int64_t seg = wide ? 64 : (a.K <= 1 ? 1 : (int64_t)1 << (32 - __builtin_clz((unsigned)a.K - 1)));
   const unsigned row_blocks = (unsigned)((a.rows + 256 / seg - 1) / (256 / seg));
   const unsigned range_blocks = (unsigned)((a.Lq + kBucketRows - 1) / kBucketRows * (a.rows / a.Lq));
   const size_t hist_bytes = (size_t)a.Nc * 4;
-  if (lds) hipLaunchKernelGGL(chunk_count_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
+  if (wide) hipLaunchKernelGGL(chunk_count_pairs_kernel, dim3(pair_blocks), dim3(256), 0, st, a);
+  else if (lds) hipLaunchKernelGGL(chunk_count_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
   else hipLaunchKernelGGL(chunk_count_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned n_seg = (unsigned)(a.n_bins / (a.Nc > 0 ? a.Nc : 1));
@@ -549,7 +599,8 @@ hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st) {
   } else if ((e = launch_fill_u32(a.n_items, 1, 0u, st)) != hipSuccess) {   // no bins: no work items
     return e;
   }
-  if (lds) hipLaunchKernelGGL(chunk_scatter_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
+  if (wide) hipLaunchKernelGGL(chunk_scatter_pairs_kernel, dim3(pair_blocks), dim3(256), 0, st, a);
+  else if (lds) hipLaunchKernelGGL(chunk_scatter_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
   else hipLaunchKernelGGL(chunk_scatter_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -25,12 +25,17 @@
 namespace hsa {
 namespace {
 
-constexpr int kGWaves = 16;
-constexpr int kGThreads = kGWaves * 64;
 constexpr float kLog2eG = 1.4426950408889634f;
 
-template <int D, int G>
-__global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) {
+// TW: 16-head-row tiles per wave.  The workgroup always holds 256 head-rows
+// (16 / TW waves); with TW = 2 every K and V^T operand read from LDS feeds two
+// MFMAs, halving the LDS operand traffic per chunk.  Measured on the 32K
+// window (G = 8): TW = 2 2.90 ms against TW = 1 2.72 ms (the loop is bound by
+// instruction issue, not by LDS operand reads), so the launches use TW = 1.
+template <int D, int G, int TW>
+__global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs a) {
+  constexpr int NW = 16 / TW;                  // waves per workgroup
+  constexpr int NTHR = 64 * NW;
   constexpr int R = 256 / G;                   // query rows per workgroup
   // landmarks (chunks) per score tile: the scores of R rows x kGTile chunks sit in LDS
   constexpr int kGTile = G <= 2 ? 32 : 64;
@@ -38,6 +43,8 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
   constexpr int KROW = D + 16, VROW = D + 16, LROW = D + 16;   // 288-byte rows: no LDS bank conflicts
   constexpr int KSTEP = D / 32, NT = D / 16;
   constexpr int TPR = 16 / G;                  // rows per 16-head-row tile (G = 8: 2, G = 16: 1)
+  constexpr int NKP = kChunk * D / 8;          // 16-byte pieces of K (and of V) per chunk
+  constexpr int PPT = (NKP + NTHR - 1) / NTHR; // pieces staged per thread
   __shared__ __align__(16) uint16_t ks[2][kChunk * KROW];
   __shared__ __align__(16) uint16_t vs[2][kChunk * VROW];   // V rows, read back transposed
   __shared__ __align__(16) uint16_t lt[kGTile * LROW];
@@ -58,22 +65,25 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
   };
   const int c_stop = n_of(min(r0 + R - 1, a.Lq - 1));
 
-  // this wave's 16 head-rows: rows r0 + TPR*w + ma/G, heads g*G + ma%G
-  const int rloc = TPR * w + ma / G;
-  const int64_t row = r0 + rloc;
-  const bool row_ok = row < a.Lq;
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + bg * a.Lkv * D;
-  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + bg * a.Lkv * D;
-  bf16x8 qa[KSTEP];
-  float qss = 0.f;
-  {
+  // tile u of this wave: 16 head-rows, rows r0 + TPR*(TW*w + u) + ma/G, heads g*G + ma%G;
+  // the query factor (normalisation, attention scale, log2 e) is folded into
+  // the query operand once: S comes out of the MFMA as base-2 logits
+  int rloc[TW];
+  bool row_ok[TW];
+  bf16x8 qa[TW][KSTEP];
+#pragma unroll
+  for (int u = 0; u < TW; ++u) {
+    rloc[u] = TPR * (TW * w + u) + ma / G;
+    const int64_t row = r0 + rloc[u];
+    row_ok[u] = row < a.Lq;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q_attn) +
-                         (((int64_t)b * a.Lq + (row_ok ? row : 0)) * a.Hq + (int64_t)g * G + ma % G) * D + 8 * jg;
+                         (((int64_t)b * a.Lq + (row_ok[u] ? row : 0)) * a.Hq + (int64_t)g * G + ma % G) * D + 8 * jg;
+    float qss = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) {
       uint4 x = *reinterpret_cast<const uint4*>(qp + 32 * t);
-      if (!row_ok) x = make_uint4(0, 0, 0, 0);
-      qa[t] = __builtin_bit_cast(bf16x8, x);
+      if (!row_ok[u]) x = make_uint4(0, 0, 0, 0);
+      qa[u][t] = __builtin_bit_cast(bf16x8, x);
       const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -81,65 +91,76 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
         qss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, qss, false);
       }
     }
-  }
-  qss += __shfl_xor(qss, 16, kWave);
-  qss += __shfl_xor(qss, 32, kWave);
-  // the query factor (normalisation, attention scale, log2 e) is folded into
-  // the query operand once: S comes out of the MFMA as base-2 logits
-  {
+    qss += __shfl_xor(qss, 16, kWave);
+    qss += __shfl_xor(qss, 32, kWave);
     const float rq = (a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f) * a.attn_scale * kLog2eG;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qa[t][e] = (__bf16)((float)qa[t][e] * rq);
+      for (int e = 0; e < 8; ++e) qa[u][t][e] = (__bf16)((float)qa[u][t][e] * rq);
   }
   // With query-key normalisation every logit is at most attn_scale * log2 e in
   // magnitude, so exp2 cannot overflow without subtracting the maximum (the
   // softmax is shift-invariant); otherwise the in-chunk maximum is subtracted.
   const bool bounded = a.qk_norm && a.attn_scale * kLog2eG <= 64.0f;
 
-  // K / V staging: each thread one 16-byte piece of K and one of V (8 dims of
-  // one key), both row-major; the P.V operand is read from V with LDS
-  // transpose loads in the key order of the S^T accumulators, so P^T feeds
-  // P.V from registers
-  constexpr int NKP = kChunk * D / 8;          // 16-byte pieces per chunk
-  uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + bg * a.Lkv * D;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + bg * a.Lkv * D;
+  // K / V staging: thread tid takes pieces tid + NTHR*i (8 dims of one key),
+  // both row-major; the P.V operand is read from V with LDS transpose loads in
+  // the key order of the S^T accumulators, so P^T feeds P.V from registers
+  uint4 kx[PPT], vx[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) kx[i] = vx[i] = make_uint4(0, 0, 0, 0);
   auto load_kv = [&](int c) {
-    if (tid < NKP) {
-      kx = *reinterpret_cast<const uint4*>(kbase + (int64_t)c * kChunk * D + tid * 8);
-      vx = *reinterpret_cast<const uint4*>(vbase + (int64_t)c * kChunk * D + tid * 8);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = tid + NTHR * i;
+      if (pc < NKP) {
+        kx[i] = *reinterpret_cast<const uint4*>(kbase + (int64_t)c * kChunk * D + pc * 8);
+        vx[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)c * kChunk * D + pc * 8);
+      }
     }
   };
   auto store_kv = [&](int bi) {
-    if (tid < NKP) {
-      const int key = tid * 8 / D, d0 = (tid * 8) % D;
-      bf16x8 kb = __builtin_bit_cast(bf16x8, kx);
-      if (a.qk_norm) {
-        // key norm: the D/8 consecutive lanes holding this key add their
-        // squares; the normalised key is staged (rounded to bf16)
-        float ss = 0.f;
-        const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const bf16x2 v2 = __builtin_bit_cast(bf16x2, kw[q]);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss, false);
+    for (int i = 0; i < PPT; ++i) {
+      const int pc = tid + NTHR * i;
+      if (pc < NKP) {
+        const int key = pc * 8 / D, d0 = (pc * 8) % D;
+        bf16x8 kb = __builtin_bit_cast(bf16x8, kx[i]);
+        if (a.qk_norm) {
+          // key norm: the D/8 consecutive lanes holding this key add their
+          // squares; the normalised key is staged (rounded to bf16)
+          float ss = 0.f;
+          const uint32_t kw[4] = {kx[i].x, kx[i].y, kx[i].z, kx[i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x2 v2 = __builtin_bit_cast(bf16x2, kw[q]);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss, false);
+          }
+          ss += dpp_f<0xB1>(ss);           // xor 1
+          ss += dpp_f<0x4E>(ss);           // xor 2
+          ss += dpp_f<0x141>(ss);          // half-row mirror: 8 lanes
+          if constexpr (D == 128) ss += dpp_f<0x140>(ss);   // row mirror: 16 lanes
+          const float rk = 1.0f / fmaxf(sqrtf(ss), 1e-6f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kb[e] = (__bf16)((float)kb[e] * rk);
         }
-        ss += dpp_f<0xB1>(ss);             // xor 1
-        ss += dpp_f<0x4E>(ss);             // xor 2
-        ss += dpp_f<0x141>(ss);            // half-row mirror: 8 lanes
-        if constexpr (D == 128) ss += dpp_f<0x140>(ss);   // row mirror: 16 lanes
-        const float rk = 1.0f / fmaxf(sqrtf(ss), 1e-6f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kb[e] = (__bf16)((float)kb[e] * rk);
+        *reinterpret_cast<uint4*>(&ks[bi][key * KROW + d0]) = __builtin_bit_cast(uint4, kb);
+        *reinterpret_cast<uint4*>(&vs[bi][key * VROW + d0]) = vx[i];
       }
-      *reinterpret_cast<uint4*>(&ks[bi][key * KROW + d0]) = __builtin_bit_cast(uint4, kb);
-      *reinterpret_cast<uint4*>(&vs[bi][key * VROW + d0]) = vx;
     }
   };
-  floatx4 acc[NT];
+  floatx4 acc[TW][NT];
+  float m[TW], l[TW];                          // online blend state of each tile's row
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;                // online blend state of this lane's row
+  for (int u = 0; u < TW; ++u) {
+    m[u] = -INFINITY;
+    l[u] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[u][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   if (c_stop > 0) {
     load_kv(0);
@@ -149,17 +170,15 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
   const uint16_t* lmb = reinterpret_cast<const uint16_t*>(a.landmarks) + bg * a.Nc * D;
   for (int c = 0; c < c_stop; ++c) {
     const int cb = c & 1;
-    if (c % kGTile == 0) {                     // retrieval scores of the next 64 chunks
-      {
-        const int qi = tid, cl = qi / (D / 8), u = qi % (D / 8);
-        if (qi < kGTile * D / 8) {
-          const int cc = c + cl < c_stop ? c + cl : c;
-          *reinterpret_cast<uint4*>(&lt[cl * LROW + u * 8]) =
-              *reinterpret_cast<const uint4*>(lmb + (int64_t)cc * D + u * 8);
-        }
+    if (c % kGTile == 0) {                     // retrieval scores of the next kGTile chunks
+      for (int qi = tid; qi < kGTile * D / 8; qi += NTHR) {
+        const int cl = qi / (D / 8), u = qi % (D / 8);
+        const int cc = c + cl < c_stop ? c + cl : c;
+        *reinterpret_cast<uint4*>(&lt[cl * LROW + u * 8]) =
+            *reinterpret_cast<const uint4*>(lmb + (int64_t)cc * D + u * 8);
       }
       __syncthreads();
-      for (int task = w; task < kScoreTasks; task += kGWaves) {   // 16 rows x 16 chunks
+      for (int task = w; task < kScoreTasks; task += NW) {   // 16 rows x 16 chunks
         const int rt = task / (kGTile / 16), ct = task % (kGTile / 16);
         const int64_t qr = r0 + 16 * rt + ma;
         const bool ok = qr < a.Lq;
@@ -186,67 +205,80 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
     }
     if (c + 1 < c_stop) load_kv(c + 1);       // next chunk in flight during this one
     // --- S^T = K Q^T: lane holds keys 16*nt + 4*jg + i of head-row ma ---------
-    floatx4 s4[4];
+    floatx4 s4[TW][4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      s4[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < TW; ++u) s4[u][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < KSTEP; ++t) {
         const uint4 kb = *reinterpret_cast<const uint4*>(&ks[cb][(16 * nt + ma) * KROW + 32 * t + 8 * jg]);
-        s4[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb), qa[t], s4[nt], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < TW; ++u)
+          s4[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb), qa[u][t], s4[u][nt],
+                                                              0, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    float mx = 0.f;
-    if (!bounded) {
-      mx = -INFINITY;
+    bf16x8 pb[TW][2];
+    float al[TW];
+#pragma unroll
+    for (int u = 0; u < TW; ++u) {
+      float mx = 0.f;
+      if (!bounded) {
+        mx = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s4[u][nt][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      }
+      float sum = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s4[nt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    }
-    float sum = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s4[nt][i] = __builtin_amdgcn_exp2f(s4[nt][i] - mx);
-        sum += s4[nt][i];
+        for (int i = 0; i < 4; ++i) {
+          s4[u][nt][i] = __builtin_amdgcn_exp2f(s4[u][nt][i] - mx);
+          sum += s4[u][nt][i];
+        }
+      sum += __shfl_xor(sum, 16, kWave);
+      sum += __shfl_xor(sum, 32, kWave);
+      // --- online blend over chunks (Step 4) ---------------------------------
+      const float sr = sc[rloc[u]][c % kGTile];
+      float f = 0.f;                           // this chunk's factor on O_c
+      al[u] = 1.0f;                            // rescale of the running sum
+      if (sr != -INFINITY) {
+        const float mn = fmaxf(m[u], sr);
+        al[u] = __builtin_amdgcn_exp2f(m[u] - mn);   // m = -inf first: 0
+        f = __builtin_amdgcn_exp2f(sr - mn);
+        l[u] = l[u] * al[u] + f;
+        m[u] = mn;
       }
-    sum += __shfl_xor(sum, 16, kWave);
-    sum += __shfl_xor(sum, 32, kWave);
-    // --- online blend over chunks (Step 4) -----------------------------------
-    const float sr = sc[rloc][c % kGTile];
-    float f = 0.f;                             // this chunk's factor on O_c
-    float al = 1.0f;                           // rescale of the running sum
-    if (sr != -INFINITY) {
-      const float mn = fmaxf(m, sr);
-      al = __builtin_amdgcn_exp2f(m - mn);     // m = -inf first: 0
-      f = __builtin_amdgcn_exp2f(sr - mn);
-      l = l * al + f;
-      m = mn;
+      const float scale = f * __builtin_amdgcn_rcpf(sum);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[u][st][e] = (__bf16)(s4[u][2 * st + (e >> 2)][e & 3] * scale);
     }
-    if (__any(al != 1.0f)) {                   // the running maximum rose for some row
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int u = 0; u < TW; ++u) {
+      if (__any(al[u] != 1.0f)) {              // the running maximum rose for some row
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nt][i] *= al;
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[u][nt][i] *= al[u];
+      }
     }
-    const float scale = f * __builtin_amdgcn_rcpf(sum);
-    bf16x8 pb[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[st][e] = (__bf16)(s4[2 * st + (e >> 2)][e & 3] * scale);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         // A = V^T: dims 16nt.., keys 32st + 4jg + 0..3 and 32st + 16 + 4jg + 0..3
         const bf16x8 va = lds_operand_tr2(vs[cb], VROW, 32 * st + 4 * jg, 32 * st + 16 + 4 * jg, 16 * nt, ma);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[st], acc[nt], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < TW; ++u)
+          acc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[u][st], acc[u][nt], 0, 0, 0);
       }
       if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the V^T operands in flight
     }
@@ -254,15 +286,21 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
     __syncthreads();
   }
   // --- out = acc / l; lane holds dims 16*nt + 4*jg + i of head-row ma --------
-  if (!row_ok) return;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;  // no eligible chunk: 0
-  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
-                 (((int64_t)b * a.Lq + row) * a.Hq + (int64_t)g * G + ma % G) * D + 4 * jg;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const uint32_t lo = (uint32_t)f32_to_bf16(acc[nt][0] * inv) | ((uint32_t)f32_to_bf16(acc[nt][1] * inv) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(acc[nt][2] * inv) | ((uint32_t)f32_to_bf16(acc[nt][3] * inv) << 16);
-    *reinterpret_cast<uint2*>(op + 16 * nt) = make_uint2(lo, hi);
+  for (int u = 0; u < TW; ++u) {
+    if (!row_ok[u]) continue;
+    const int64_t row = r0 + rloc[u];
+    const float inv = l[u] > 0.f ? 1.0f / l[u] : 0.f;   // no eligible chunk: 0
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) +
+                   (((int64_t)b * a.Lq + row) * a.Hq + (int64_t)g * G + ma % G) * D + 4 * jg;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t lo =
+          (uint32_t)f32_to_bf16(acc[u][nt][0] * inv) | ((uint32_t)f32_to_bf16(acc[u][nt][1] * inv) << 16);
+      const uint32_t hi =
+          (uint32_t)f32_to_bf16(acc[u][nt][2] * inv) | ((uint32_t)f32_to_bf16(acc[u][nt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + 16 * nt) = make_uint2(lo, hi);
+    }
   }
 }
 
@@ -270,15 +308,18 @@ __global__ __launch_bounds__(kGThreads) void attend_global_kernel(GlobalArgs a) 
 
 int global_rows_per_block(int G) { return 256 / G; }
 
+// Tiles per wave (measured: see the kernel's comment).
+template <int D> constexpr int global_tw() { return 1; }
+
 hipError_t launch_attend_global(const GlobalArgs& a, int64_t B, int D, int G, hipStream_t st) {
   const int64_t R = 256 / G;
   const int64_t blocks = (a.Lq + R - 1) / R * B * a.Hkv;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(kGThreads);
-#define HSA_GLOBAL_CASE(DD, GG)                                                  \
-  if (D == DD && G == GG) {                                                      \
-    hipLaunchKernelGGL((attend_global_kernel<DD, GG>), grid, block, 0, st, a);   \
-    return hipGetLastError();                                                    \
+#define HSA_GLOBAL_CASE(DD, GG)                                                                  \
+  if (D == DD && G == GG) {                                                                      \
+    constexpr int TW = global_tw<DD>();                                                          \
+    hipLaunchKernelGGL((attend_global_kernel<DD, GG, TW>), dim3((unsigned)blocks), dim3(64 * 16 / TW), 0, st, a); \
+    return hipGetLastError();                                                                    \
   }
   HSA_GLOBAL_CASE(128, 1) HSA_GLOBAL_CASE(128, 2) HSA_GLOBAL_CASE(128, 4) HSA_GLOBAL_CASE(128, 8)
   HSA_GLOBAL_CASE(128, 16) HSA_GLOBAL_CASE(64, 1) HSA_GLOBAL_CASE(64, 2) HSA_GLOBAL_CASE(64, 4)

@@ -475,6 +475,26 @@ __global__ __launch_bounds__(256) void bwd_slot_kernel(BwdArgs a) {
   if (active) a.draw[row * K + k] = valid ? a.ret_scale * (wdw - wk * sum) : 0.f;
 }
 
+// More than 64 slots per row: one wave per row, the sum over slots reduced in
+// a fixed order (lane-strided partial sums, then the wave reduction).
+__global__ __launch_bounds__(256) void bwd_slot_wide_kernel(BwdArgs a) {
+  const ChunkArgs& c = a.c;
+  const int K = c.K, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= c.rows) return;
+  float sum = 0.f;
+  for (int k = lane; k < K; k += kWave) {
+    const int32_t ci = c.idx[row * K + k];
+    if (ci >= 0 && (int64_t)ci < c.Nc) sum += a.wdw[row * K + k];
+  }
+  sum = wave_sum(sum);
+  for (int k = lane; k < K; k += kWave) {
+    const int32_t ci = c.idx[row * K + k];
+    const bool valid = ci >= 0 && (int64_t)ci < c.Nc;
+    a.draw[row * K + k] = valid ? a.ret_scale * (a.wdw[row * K + k] - c.wts[row * K + k] * sum) : 0.f;
+  }
+}
+
 // --- per row: dq_attn and dq_ret -----------------------------------------------
 // D / 4 threads per output row, each owning 4 dims.  Blocks [0, n_attn) take
 // the head-rows (row, head) of dq_attn: the pairs' dqhat summed in slot order,
@@ -629,7 +649,10 @@ hipError_t launch_bwd_dg(const BwdArgs& a, hipStream_t st, const Marks& mk) {
   }
   if ((e = mk.rec(kStageAttend, 1, st)) != hipSuccess) return e;
   if ((e = mk.rec(kStageCombine, 0, st)) != hipSuccess) return e;
-  {
+  if (a.c.K > kWave) {
+    hipLaunchKernelGGL(bwd_slot_wide_kernel, dim3((unsigned)((a.c.rows + 3) / 4)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
     const int64_t S = a.c.K <= 1 ? 1 : (int64_t)1 << (32 - __builtin_clz((unsigned)a.c.K - 1));
     hipLaunchKernelGGL(bwd_slot_kernel, dim3((unsigned)((a.c.rows + 256 / S - 1) / (256 / S))), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

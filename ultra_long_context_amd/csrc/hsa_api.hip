@@ -53,8 +53,10 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit) { return a >= 0 && b >= 0 && (b
 // check_positions: reject rows whose eligible chunks would reach past the
 // history (not needed when the caller supplies the selection).  allow_global:
 // a top_k above 64 that covers every row's eligible chunks is planned as
-// global HSA (hsa_forward only).
-hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool allow_global = false) {
+// global HSA (hsa_forward only).  big_selection: a given selection may have
+// any number of slots (the backward, which takes the selection as an input).
+hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool allow_global = false,
+                       bool big_selection = false) {
   if (!s) return HSA_ERR_NULL_POINTER;
   if (s->batch < 1 || s->q_len < 1 || s->kv_len < 0 || s->q_pos0 < 0 || s->n_q_heads < 1 ||
       s->n_kv_heads < 1 || s->top_k < 1)
@@ -63,7 +65,7 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool
   const int32_t G = s->n_q_heads / s->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return HSA_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return HSA_ERR_UNSUPPORTED;
-  const bool big_k = s->top_k > HSA_MAX_TOP_K;
+  const bool big_k = s->top_k > HSA_MAX_TOP_K && !big_selection;
   if (big_k && !allow_global) return HSA_ERR_UNSUPPORTED;
   if (s->dtype != HSA_DTYPE_F32 && s->dtype != HSA_DTYPE_BF16) return HSA_ERR_UNSUPPORTED;
   if (s->flags & ~HSA_FLAG_QK_L2NORM) return HSA_ERR_UNSUPPORTED;
@@ -434,7 +436,7 @@ struct BwdPlan {
 };
 
 hsa_status_t make_bwd_plan(const hsa_shape_t* s, BwdPlan* b) {
-  hsa_status_t st = make_plan(s, &b->p, false);
+  hsa_status_t st = make_plan(s, &b->p, false, false, true);
   if (st != HSA_OK) return st;
   Plan& p = b->p;
   // backward bins and work items: smaller bands (every bin sortable in LDS)
