@@ -72,7 +72,7 @@ KERNELS = {
     ("decode_16M", "scan"): "scan_wide_kernel<true, 128>",
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
     ("decode_16M", "landmarks"): "chunk_landmark_kernel<true, 128>",
-    ("global_32K", "attend"): "attend_global_kernel<128, 8>",
+    ("global_32K", "attend"): "attend_global_kernel<128, 8, 1>",
     ("chunked_1M", "scan"): "scan_block_kernel<128, 64>",
     ("chunked_1M", "bucket"): "chunk_count/scan/scatter kernels",
     ("chunked_1M", "attend"): "chunk_attend_kernel<128, 8>",
@@ -758,6 +758,58 @@ def mfma_summary(csv_path, workload, kernel, command):
     return "\n".join(lines) + "\n"
 
 
+def trace_summary(csv_path, workloads, command, gap_s=0.15):
+    """Per-workload kernel statistics from a rocprofv3 --kernel-trace CSV of a
+    bench.py run: dispatches are grouped into workloads at host gaps longer
+    than gap_s (input generation separates the workloads, which run in the
+    order `workloads`)."""
+    import csv
+    import re
+    rows = []
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+                         int(r.get("Grid_Size_X", 0) or 0) // max(1, int(r.get("Workgroup_Size_X", 1) or 1))
+                         * int(r.get("Grid_Size_Y", 1) or 1)))
+    rows.sort()
+    groups, cur, last_end = [], [], None
+    for st, en, name, wgs in rows:
+        if last_end is not None and st - last_end > gap_s * 1e9:
+            groups.append(cur)
+            cur = []
+        cur.append((st, en, name, wgs))
+        last_end = en if last_end is None else max(last_end, en)
+    if cur:
+        groups.append(cur)
+    # the first groups may hold setup work (allocation, calibration): label the
+    # last len(workloads) groups with the workload names
+    labels = ["setup %d" % i for i in range(max(0, len(groups) - len(workloads)))] + list(workloads)[-len(groups):]
+
+    def short(name):
+        if "reduce" in name and "sum" in name.lower():
+            return "torch sum (1 GiB cache-flush read)"
+        m = re.search(r"(\w+_kernel)(<[^>]*>)?", name)
+        return (m.group(1) + (m.group(2) or "")) if m else name[:48]
+
+    lines = ["# rocprofv3 kernel statistics per workload of bench.py (times in microseconds;",
+             "# cold timed calls, graph replays, eager warmup, stage-timed and selection calls)",
+             "# command: %s" % command,
+             "# dispatches grouped into workloads at host gaps > %.2f s (input generation)" % gap_s]
+    for label, grp in zip(labels, groups):
+        stats = {}
+        for st, en, name, wgs in grp:
+            k = (short(name), wgs)
+            stats.setdefault(k, []).append((en - st) / 1e3)
+        total = sum(sum(v) for v in stats.values())
+        lines.append("")
+        lines.append("## %s" % label)
+        lines.append("%-48s %8s %6s %11s %11s %11s %6s" % ("kernel", "wgs", "calls", "avg_us", "min_us", "max_us", "pct"))
+        for (name, wgs), v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+            lines.append("%-48s %8d %6d %11.1f %11.1f %11.1f %6.1f" % (
+                name[:48], wgs, len(v), float(np.mean(v)), min(v), max(v), 100.0 * sum(v) / total))
+    return "\n".join(lines) + "\n"
+
+
 def copy_calibration():
     """The plain copy kernel the counter passes are scaled by."""
     import torch
@@ -788,7 +840,15 @@ def main():
     ap.add_argument("--kernel-of", default="prefill_128K:attend",
                     help="workload:stage whose kernel --pmc-summary / --mfma-summary reports")
     ap.add_argument("--command", default="", help="command recorded in the --pmc-summary header")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-workload kernel statistics of a rocprofv3 --kernel-trace CSV of a run "
+                         "over --workloads")
     args = ap.parse_args()
+    if args.trace_summary:
+        order = ["decode_16M", "prefill_32K", "chunked_1M", "global_32K", "backward_32K", "prefill_128K"]
+        wl = [w for w in order if w in args.workloads.split(",")]
+        sys.stdout.write(trace_summary(args.trace_summary, wl, args.command))
+        return
     if args.mfma_summary:
         wl, stage = args.kernel_of.split(":")
         sys.stdout.write(mfma_summary(args.mfma_summary, wl, KERNELS[(wl, stage)], args.command))
