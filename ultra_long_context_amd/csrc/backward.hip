@@ -30,6 +30,9 @@ namespace {
 
 constexpr int kBP = 64;                     // pairs per work item (as the forward)
 constexpr float kLog2eB = 1.4426950408889634f;
+// 1 / max(sqrt(ss), 1e-6) for a sum of squares ss >= 0, by the hardware
+// reciprocal square root (within about 1 ulp)
+__device__ __forceinline__ float inv_norm(float ss) { return __builtin_amdgcn_rsqf(fmaxf(ss, 1e-12f)); }
 
 // --- sort each bin's pair ids ascending (bitonic in LDS) --------------------
 constexpr int kSortCap = 8192;
@@ -110,21 +113,27 @@ __global__ __launch_bounds__(256) void bin_sort_kernel(BwdArgs a) {
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
   constexpr int KROW = D + 16;              // K, V rows (bf16; 32-byte pad: no bank conflicts)
-  constexpr int PROW = kChunk + 16;          // staged P, h rows [head-row][key]
-  constexpr int QROW = D + 16;              // staged q, dO_w rows [head-row][dim]
   constexpr int PT = 16 / G;                // pairs per 16-head-row tile
   constexpr int KSTEP = D / 32, NT = D / 16;
   constexpr int HR = 32;                    // head-rows staged per phase B round (2 tiles)
-  // under 80 KiB of LDS: two workgroups per CU
+  // about 67 KiB of LDS: two workgroups per CU.  ks holds the normalised keys
+  // khat (k itself without query-key normalisation).
   __shared__ __align__(16) uint16_t ks[kChunk * KROW];
   __shared__ __align__(16) uint16_t vs[kChunk * KROW];
-  __shared__ float rk[kChunk];
   // phase B operands of 32 head-rows (2 tiles), row-major (read back
-  // transposed): P and h [hr][key], dO_w and q [hr][dim]
-  __shared__ __align__(16) uint16_t ps[HR * PROW];
-  __shared__ __align__(16) uint16_t hs[HR * PROW];
-  __shared__ __align__(16) uint16_t ds_[HR * QROW];
-  __shared__ __align__(16) uint16_t qs[HR * QROW];
+  // transposed): P and h [hr][key], dO and q [hr][dim], stored as four 8-row
+  // blocks whose stride is 8 padded rows plus 128 bytes.  A transpose load's
+  // lane groups jg = 0, 1 (and 2, 3) are served in the same cycle (64 banks of
+  // 4 bytes, 32 lanes of 8 bytes) and read blocks jg; with a plain row stride
+  // 8 rows span a multiple of 256 bytes for both row widths and the two groups
+  // fell on the same banks (37 % of the kernel's LDS-active cycles were bank
+  // conflicts, nearly all in these loads).
+  constexpr int PROW = kChunk + 16, QROW = D + 16;
+  constexpr int PBLK = 8 * PROW + 64, QBLK = 8 * QROW + 64;
+  __shared__ __align__(16) uint16_t ps[4 * PBLK];
+  __shared__ __align__(16) uint16_t hs[4 * PBLK];
+  __shared__ __align__(16) uint16_t ds_[4 * QBLK];
+  __shared__ __align__(16) uint16_t qs[4 * QBLK];
   __shared__ uint32_t pid_s[kBP];
   __shared__ float w_s[kBP];
   __shared__ int64_t qoff_s[kBP];
@@ -163,13 +172,14 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  {
+  if (c.qk_norm) {  // khat = k / max(|k|, 1e-6), each key's D dims over 4 threads
     const int key = tid >> 2, qd = tid & 3;
+    uint4 u[D / 32];
     float ss = 0.f;
 #pragma unroll
-    for (int x = 0; x < D / 4; x += 8) {
-      const uint4 u = *reinterpret_cast<const uint4*>(&ks[key * KROW + qd * (D / 4) + x]);
-      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+    for (int x = 0; x < D / 32; ++x) {
+      u[x] = *reinterpret_cast<const uint4*>(&ks[key * KROW + qd * (D / 4) + 8 * x]);
+      const uint32_t wd[4] = {u[x].x, u[x].y, u[x].z, u[x].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bf16x2 v2 = __builtin_bit_cast(bf16x2, wd[q]);
@@ -178,9 +188,20 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
     }
     ss += __shfl_xor(ss, 1, kWave);
     ss += __shfl_xor(ss, 2, kWave);
-    if (qd == 0) rk[key] = c.qk_norm ? 1.0f / fmaxf(sqrtf(ss), 1e-6f) : 1.0f;
+    const float r = inv_norm(ss);
+#pragma unroll
+    for (int x = 0; x < D / 32; ++x) {
+      uint32_t wd[4] = {u[x].x, u[x].y, u[x].z, u[x].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 o2 = {(__bf16)(__uint_as_float(wd[q] << 16) * r),
+                           (__bf16)(__uint_as_float(wd[q] & 0xFFFF0000u) * r)};
+        wd[q] = __builtin_bit_cast(uint32_t, o2);
+      }
+      *reinterpret_cast<uint4*>(&ks[key * KROW + qd * (D / 4) + 8 * x]) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   floatx4 dv[NT], dk[NT];
 #pragma unroll
@@ -190,11 +211,13 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
   }
   const float as = c.attn_scale;
   const int n_tiles = (n_pairs + PT - 1) / PT;
-  // q and dout rows of this wave's tile (16 head-rows), loaded one tile ahead
+  // q and dout rows of this wave's tile (16 head-rows), loaded one tile ahead.
+  // Head-rows past the item's pairs read the first pair's rows (finite data
+  // of this item) and carry weight 0, which zeroes everything they add.
   uint4 xr[KSTEP], yr[KSTEP];
   auto tile_off = [&](int tile) -> int64_t {
     const int pm = tile * PT + ma / G;
-    return tile < n_tiles && pm < n_pairs ? qoff_s[pm] + (int64_t)(ma % G) * D : 0;
+    return (tile < n_tiles && pm < n_pairs ? qoff_s[pm] : qoff_s[0]) + (int64_t)(ma % G) * D;
   };
   {
     const int64_t off = tile_off(w);
@@ -210,28 +233,25 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
     const int pm = tile * PT + ma / G, hd = ma % G;
     const bool live = tile < n_tiles && pm < n_pairs;
     const float wp = live ? w_s[pm] : 0.f;
+    // The pair's blend weight w scales its output gradient dO = w dout, and
+    // dP, dz and dV are linear in dO: the products below use dout itself and
+    // w enters once, in dz's factor and in the staged P (w P for dV).
     bf16x8 qa[KSTEP], da[KSTEP];
-    uint4 qst[KSTEP], dst[KSTEP];             // this tile's q and dO_w rows for phase B
+    uint4 qst[KSTEP], dst[KSTEP];             // this tile's q and dout rows for phase B
     float qss = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) {
-      uint4 x = xr[t], y = yr[t];
-      if (!live) x = y = make_uint4(0, 0, 0, 0);
+      const uint4 x = xr[t], y = yr[t];
       qa[t] = __builtin_bit_cast(bf16x8, x);
-      const uint32_t qw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
-      uint32_t dw4[4];
+      da[t] = __builtin_bit_cast(bf16x8, y);
+      const uint32_t qw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bf16x2 v2 = __builtin_bit_cast(bf16x2, qw[q]);
         qss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, qss, false);
-        const bf16x2 o2 = {(__bf16)(__uint_as_float(yw[q] << 16) * wp),
-                           (__bf16)(__uint_as_float(yw[q] & 0xFFFF0000u) * wp)};
-        dw4[q] = __builtin_bit_cast(uint32_t, o2);
       }
-      const uint4 dw = make_uint4(dw4[0], dw4[1], dw4[2], dw4[3]);
-      da[t] = __builtin_bit_cast(bf16x8, dw);
       qst[t] = x;
-      dst[t] = dw;
+      dst[t] = y;
     }
     if (t0 + 4 < n_tiles) {   // next tile's rows, in flight during this one
       const int64_t off = tile_off(t0 + 4 + w);
@@ -243,8 +263,8 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
     }
     qss += __shfl_xor(qss, 16, kWave);
     qss += __shfl_xor(qss, 32, kWave);
-    const float rq = c.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
-    // S^T = K Q^T and dP^T = V dO_w^T: lane holds keys 16*nt + 4*jg + i of head-row ma
+    const float rq = c.qk_norm ? inv_norm(qss) : 1.0f;
+    // S^T = khat Q^T and dP'^T = V dout^T: lane holds keys 16*nt + 4*jg + i of head-row ma
     floatx4 sv[4], dp[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -259,69 +279,61 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    float rkl[4][4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const float4 r4 = *reinterpret_cast<const float4*>(&rk[16 * nt + 4 * jg]);
-      rkl[nt][0] = r4.x; rkl[nt][1] = r4.y; rkl[nt][2] = r4.z; rkl[nt][3] = r4.w;
-    }
+    // softmax over the chunk's keys in base 2: the logit factor cs > 0, so the
+    // largest raw product gives the largest logit
+    const float cs = rq * as * kLog2eB;
     float mx = -INFINITY;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[nt][i] = sv[nt][i] * (rq * as * kLog2eB) * rkl[nt][i];
-        mx = fmaxf(mx, sv[nt][i]);
-      }
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[nt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    float sum = 0.f;
+    const float mxs = mx * cs;
+    float sum = 0.f, edp = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[nt][i] = __builtin_amdgcn_exp2f(sv[nt][i] - mx);
+        sv[nt][i] = __builtin_amdgcn_exp2f(fmaf(sv[nt][i], cs, -mxs));   // e, unnormalised
         sum += sv[nt][i];
+        edp = fmaf(sv[nt][i], dp[nt][i], edp);
       }
     sum += __shfl_xor(sum, 16, kWave);
     sum += __shfl_xor(sum, 32, kWave);
+    edp += __shfl_xor(edp, 16, kWave);
+    edp += __shfl_xor(edp, 32, kWave);
     const float inv = __builtin_amdgcn_rcpf(sum);
-    float pdp = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[nt][i] *= inv;                                   // P
-        pdp += sv[nt][i] * dp[nt][i];
-      }
-    pdp += __shfl_xor(pdp, 16, kWave);
-    pdp += __shfl_xor(pdp, 32, kWave);                      // sum_j P dP = w dout . O
+    const float pdp = edp * inv;                            // sum_j P dP' = dout . O
     {  // w dw of the pair: its G head-rows are lanes ma with equal ma / G
       float wdw = pdp;
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) wdw += __shfl_xor(wdw, o, kWave);
-      if (live && jg == 0 && hd == 0) a.wdw[pid_s[pm]] = wdw;
+      if (live && jg == 0 && hd == 0) a.wdw[pid_s[pm]] = wp * wdw;
     }
-    // g = attn dz |k|^-1 (for dqhat), h = attn dz |q|^-1 (for dkhat), dz = P (dP - pdp)
+    // dz = w P (dP' - pdp) attn (the score gradient), g = dz (for dqhat, khat
+    // staged), h = dz |q|^-1 (for dkhat); the staged P is w P (for dV)
+    const float pw = inv * wp, ez = pw * as;
     bf16x8 gb[2];
-    uint2 pst[4], hst[4];                     // this tile's P and h rows for phase B
+    uint2 pst[4], hst[4];                     // this tile's w P and h rows for phase B
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      float hv[4];
+      float hv[4], pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float dz = sv[nt][i] * (dp[nt][i] - pdp) * as;
+        const float dz = sv[nt][i] * ez * (dp[nt][i] - pdp);
         hv[i] = dz * rq;
-        gb[nt >> 1][4 * (nt & 1) + i] = (__bf16)(dz * rkl[nt][i]);
+        pv[i] = sv[nt][i] * pw;
+        gb[nt >> 1][4 * (nt & 1) + i] = (__bf16)dz;
       }
-      // P and h of head-row ma, keys 16nt + 4jg .. +3
-      const bf16x2 p01 = {(__bf16)sv[nt][0], (__bf16)sv[nt][1]}, p23 = {(__bf16)sv[nt][2], (__bf16)sv[nt][3]};
+      // w P and h of head-row ma, keys 16nt + 4jg .. +3
+      const bf16x2 p01 = {(__bf16)pv[0], (__bf16)pv[1]}, p23 = {(__bf16)pv[2], (__bf16)pv[3]};
       const bf16x2 h01 = {(__bf16)hv[0], (__bf16)hv[1]}, h23 = {(__bf16)hv[2], (__bf16)hv[3]};
       pst[nt] = make_uint2(__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23));
       hst[nt] = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
     }
-    // dqhat^T = K^T g^T: lane holds dims 16*nt + 4*jg + i of head-row ma.  The
-    // A operand K^T comes from the row-major keys by transpose loads, in the
+    // dqhat^T = khat^T g^T: lane holds dims 16*nt + 4*jg + i of head-row ma.  The
+    // A operand khat^T comes from the row-major keys by transpose loads, in the
     // key order of g (keys 32st + 4jg + 0..3 and 32st + 16 + 4jg + 0..3)
     uint16_t* dq = a.dq_part + (live ? ((int64_t)pid_s[pm] * G + hd) * D : 0) + 4 * jg;
 #pragma unroll
@@ -345,26 +357,27 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if ((w >> 1) == half) {
-        const int r = 16 * (w & 1) + ma;
+        const int r = 16 * (w & 1) + ma, qr = (r >> 3) * QBLK + (r & 7) * QROW,
+                  pr = (r >> 3) * PBLK + (r & 7) * PROW;
 #pragma unroll
         for (int t = 0; t < KSTEP; ++t) {
-          *reinterpret_cast<uint4*>(&qs[r * QROW + 32 * t + 8 * jg]) = qst[t];
-          *reinterpret_cast<uint4*>(&ds_[r * QROW + 32 * t + 8 * jg]) = dst[t];
+          *reinterpret_cast<uint4*>(&qs[qr + 32 * t + 8 * jg]) = qst[t];
+          *reinterpret_cast<uint4*>(&ds_[qr + 32 * t + 8 * jg]) = dst[t];
         }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          *reinterpret_cast<uint2*>(&ps[r * PROW + 16 * nt + 4 * jg]) = pst[nt];
-          *reinterpret_cast<uint2*>(&hs[r * PROW + 16 * nt + 4 * jg]) = hst[nt];
+          *reinterpret_cast<uint2*>(&ps[pr + 16 * nt + 4 * jg]) = pst[nt];
+          *reinterpret_cast<uint2*>(&hs[pr + 16 * nt + 4 * jg]) = hst[nt];
         }
       }
       __syncthreads();
-      const int r0 = 8 * jg;
-      const bf16x8 pa = lds_operand_tr(ps, PROW, r0, 16 * w, ma);
-      const bf16x8 ha = lds_operand_tr(hs, PROW, r0, 16 * w, ma);
+      // lane group jg reads head-rows 8 jg .. 8 jg + 7: block jg
+      const bf16x8 pa = lds_operand_tr(ps + jg * PBLK, PROW, 0, 16 * w, ma);
+      const bf16x8 ha = lds_operand_tr(hs + jg * PBLK, PROW, 0, 16 * w, ma);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8 db = lds_operand_tr(ds_, QROW, r0, 16 * nt, ma);
-        const bf16x8 qb = lds_operand_tr(qs, QROW, r0, 16 * nt, ma);
+        const bf16x8 db = lds_operand_tr(ds_ + jg * QBLK, QROW, 0, 16 * nt, ma);
+        const bf16x8 qb = lds_operand_tr(qs + jg * QBLK, QROW, 0, 16 * nt, ma);
         dv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, db, dv[nt], 0, 0, 0);
         dk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha, qb, dk[nt], 0, 0, 0);
         if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);
