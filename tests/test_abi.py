@@ -176,8 +176,15 @@ def test_chunk_landmarks_checks_arguments():
 def test_global_top_k_planning():
     """top_k above 64 is global HSA: only when it covers every row's eligible
     chunks (bf16, any supported G), only through hsa_forward, without selection
-    outputs; it needs only the counter region of the workspace."""
-    st, n = ws_size(base(top_k=65))
+    outputs; its workspace is the counter region plus, with query-key
+    normalisation, the normalised keys of the complete chunks (bf16)."""
+    shp = base(top_k=65)
+    st, n = ws_size(shp)
+    keys = shp.batch * shp.n_kv_heads * (shp.kv_len // 64) * 64 * shp.head_dim * 2
+    assert shp.flags & h.HSA_FLAG_QK_L2NORM
+    assert st == 0 and n == 16384 + keys
+    shp.flags = 0
+    st, n = ws_size(shp)
     assert st == 0 and n == 16384
     st, _ = ws_size(base(top_k=4096, n_q_heads=16))
     assert st == 0

@@ -11,8 +11,9 @@
 // out = acc / l (scores in base 2).  A workgroup of 16 waves owns 256/G
 // consecutive query rows of one (batch, kv head) (16 head-rows per wave: 16/G
 // rows of G heads) and
-// streams their eligible chunks: each chunk's K and V (row-major) are staged in
-// LDS once for all 256 head-rows, double-buffered so the next chunk's loads are
+// streams their eligible chunks: each chunk's K (normalised once per call by
+// key_norm_kernel when query-key normalisation is on) and V (row-major) are
+// staged in LDS once for all 256 head-rows, double-buffered so the next chunk's loads are
 // in flight during the current one; S^T = K Q^T and O^T += V^T P^T run on
 // v_mfma_f32_16x16x32_bf16, V^T read with LDS transpose loads, with P (times
 // the chunk's blend factor, over the in-chunk sum, rounded to bf16) fed from
@@ -26,6 +27,41 @@ namespace hsa {
 namespace {
 
 constexpr float kLog2eG = 1.4426950408889634f;
+
+// Normalised keys khat = k / max(|k|, 1e-6) (bf16) of the complete chunks,
+// written once per call for every workgroup of the global kernel to stage
+// (each would otherwise normalise every chunk again).  Thread t takes 16-byte
+// piece t (8 dims of one key; a key's D/8 pieces sit in consecutive lanes of
+// one DPP row): the same lane layout and reduction order as a staging pass,
+// so the rounded keys do not depend on which kernel normalised them.
+template <int D>
+__global__ __launch_bounds__(256) void key_norm_kernel(GlobalArgs a, int64_t n_pieces) {
+  constexpr int PPK = D / 8;                                 // pieces per key
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tc = t < n_pieces ? t : 0;
+  const int64_t per_bg = a.Nc * kChunk * PPK;                // pieces per (batch, kv head)
+  const int64_t bg = tc / per_bg, pc = tc % per_bg;
+  const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.k) +
+                                                  bg * a.Lkv * D + pc * 8);
+  float ss = 0.f;
+  const uint32_t kw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x2 v2 = __builtin_bit_cast(bf16x2, kw[q]);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss, false);
+  }
+  ss += dpp_f<0xB1>(ss);           // xor 1
+  ss += dpp_f<0x4E>(ss);           // xor 2
+  ss += dpp_f<0x141>(ss);          // half-row mirror: 8 lanes
+  if constexpr (D == 128) ss += dpp_f<0x140>(ss);   // row mirror: 16 lanes
+  const float rk = 1.0f / fmaxf(sqrtf(ss), 1e-6f);
+  bf16x8 kb = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kb[e] = (__bf16)((float)kb[e] * rk);
+  if (t < n_pieces)
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.k_hat) + bg * per_bg * 8 + pc * 8) =
+        __builtin_bit_cast(uint4, kb);
+}
 
 // TW: 16-head-row tiles per wave.  The workgroup always holds 256 head-rows
 // (16 / TW waves); with TW = 2 every K and V^T operand read from LDS feeds two
@@ -104,7 +140,9 @@ __global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs 
   // softmax is shift-invariant); otherwise the in-chunk maximum is subtracted.
   const bool bounded = a.qk_norm && a.attn_scale * kLog2eG <= 64.0f;
 
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + bg * a.Lkv * D;
+  // keys as staged: the normalised copy (with query-key normalisation) or K itself
+  const uint16_t* kbase = a.qk_norm ? reinterpret_cast<const uint16_t*>(a.k_hat) + bg * a.Nc * kChunk * D
+                                    : reinterpret_cast<const uint16_t*>(a.k) + bg * a.Lkv * D;
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + bg * a.Lkv * D;
   // K / V staging: thread tid takes pieces tid + NTHR*i (8 dims of one key),
   // both row-major; the P.V operand is read from V with LDS transpose loads in
@@ -128,26 +166,7 @@ __global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs 
       const int pc = tid + NTHR * i;
       if (pc < NKP) {
         const int key = pc * 8 / D, d0 = (pc * 8) % D;
-        bf16x8 kb = __builtin_bit_cast(bf16x8, kx[i]);
-        if (a.qk_norm) {
-          // key norm: the D/8 consecutive lanes holding this key add their
-          // squares; the normalised key is staged (rounded to bf16)
-          float ss = 0.f;
-          const uint32_t kw[4] = {kx[i].x, kx[i].y, kx[i].z, kx[i].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bf16x2 v2 = __builtin_bit_cast(bf16x2, kw[q]);
-            ss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, ss, false);
-          }
-          ss += dpp_f<0xB1>(ss);           // xor 1
-          ss += dpp_f<0x4E>(ss);           // xor 2
-          ss += dpp_f<0x141>(ss);          // half-row mirror: 8 lanes
-          if constexpr (D == 128) ss += dpp_f<0x140>(ss);   // row mirror: 16 lanes
-          const float rk = 1.0f / fmaxf(sqrtf(ss), 1e-6f);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kb[e] = (__bf16)((float)kb[e] * rk);
-        }
-        *reinterpret_cast<uint4*>(&ks[bi][key * KROW + d0]) = __builtin_bit_cast(uint4, kb);
+        *reinterpret_cast<uint4*>(&ks[bi][key * KROW + d0]) = kx[i];
         *reinterpret_cast<uint4*>(&vs[bi][key * VROW + d0]) = vx[i];
       }
     }
@@ -315,6 +334,16 @@ hipError_t launch_attend_global(const GlobalArgs& a, int64_t B, int D, int G, hi
   const int64_t R = 256 / G;
   const int64_t blocks = (a.Lq + R - 1) / R * B * a.Hkv;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (a.qk_norm && a.Nc > 0) {
+    if (a.k_hat == nullptr) return hipErrorInvalidValue;
+    const int64_t n_pieces = B * a.Hkv * a.Nc * kChunk * (D / 8);
+    const int64_t nb = (n_pieces + 255) / 256;
+    if (nb > INT32_MAX) return hipErrorInvalidValue;
+    if (D == 128) hipLaunchKernelGGL(key_norm_kernel<128>, dim3((unsigned)nb), dim3(256), 0, st, a, n_pieces);
+    else hipLaunchKernelGGL(key_norm_kernel<64>, dim3((unsigned)nb), dim3(256), 0, st, a, n_pieces);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 #define HSA_GLOBAL_CASE(DD, GG)                                                                  \
   if (D == DD && G == GG) {                                                                      \
     constexpr int TW = global_tw<DD>();                                                          \

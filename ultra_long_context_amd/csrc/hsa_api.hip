@@ -44,6 +44,7 @@ struct Plan {
   size_t off_idx, off_score, off_lists, off_partials, off_counters, total;
   size_t off_ccounts, off_coffsets, off_ccursor, off_citems, off_cnitems, off_cpairs, off_cwts,
       off_cparts, off_cseg;
+  size_t off_khat = 0;   // global HSA with qk_norm: normalised keys
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -104,6 +105,11 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool
     p->attn_mode = 4;
     p->off_counters = 0;
     p->total = kCounterBytes;
+    p->off_khat = 0;
+    if (p->qk_norm && Nc > 0) {   // normalised keys of the complete chunks, staged once per call
+      p->off_khat = align_up(p->total, 256);
+      p->total = p->off_khat + (size_t)(s->batch * s->n_kv_heads) * (size_t)Nc * HSA_CHUNK_TOKENS * p->D * 2;
+    }
     return HSA_OK;
   }
   // Scan plan.  bf16 with K <= 32, at least kBlockScanMinRows rows per
@@ -357,6 +363,7 @@ hsa_status_t forward_impl(const hsa_shape_t* shape, const void* q_ret, const voi
   if (p.global) {
     GlobalArgs g;
     g.q_ret = q_ret; g.landmarks = lm; g.q_attn = q_attn; g.k = kk; g.v = vv; g.out = out;
+    g.k_hat = p.off_khat ? static_cast<char*>(ws) + p.off_khat : nullptr;
     g.Lq = p.Lq; g.q_pos0 = p.q_pos0; g.Lkv = p.Lkv; g.Nc = p.Nc; g.Hq = p.Hq; g.Hkv = p.Hkv;
     g.ret_scale = p.ret_scale; g.attn_scale = p.attn_scale; g.qk_norm = p.qk_norm ? 1 : 0;
     const hipStream_t gs = static_cast<hipStream_t>(stream);

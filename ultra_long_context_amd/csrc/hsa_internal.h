@@ -150,6 +150,7 @@ struct GlobalArgs {
   const void* q_attn;     // [B, Lq, Hq, D]
   const void* k;          // [B, Hkv, Lkv, D]
   const void* v;
+  void* k_hat;            // [B, Hkv, Nc * 64, D] normalised keys (bf16, workspace), with qk_norm
   void* out;              // [B, Lq, Hq, D]
   int64_t Lq, q_pos0, Lkv, Nc;
   int32_t Hq, Hkv;
@@ -157,6 +158,7 @@ struct GlobalArgs {
   int32_t qk_norm;
 };
 
+// Normalised keys of the complete chunks into a.k_hat, then the global kernel.
 hipError_t launch_attend_global(const GlobalArgs& a, int64_t B, int D, int G, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
 hipError_t launch_scan_wide(const ScanArgs& a, int64_t B, bool bf16, int D, hipStream_t st);
