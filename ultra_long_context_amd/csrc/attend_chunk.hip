@@ -408,6 +408,12 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     }
   }
   __syncthreads();
+  const int n_tiles = (n_pairs + PT - 1) / PT;
+  const int ma = lane & 15, jg = lane >> 4;        // head-row of the tile, lane group
+  // this wave's first two tiles of queries in flight during the key norms
+  bf16x8 qa[KSTEP], qn[KSTEP], qn2[KSTEP];
+  if (w < n_tiles) load_q_tile<D, G>(a, qoff_s, n_pairs, w, ma, jg, qa);
+  if (w + 4 < n_tiles) load_q_tile<D, G>(a, qoff_s, n_pairs, w + 4, ma, jg, qn);
   {  // key inverse norms: 4 threads per key
     const int key = tid >> 2, qd = tid & 3;
     float ss = 0.f;
@@ -421,8 +427,6 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
   }
   __syncthreads();
 
-  const int n_tiles = (n_pairs + PT - 1) / PT;
-  const int ma = lane & 15, jg = lane >> 4;        // head-row of the tile, lane group
   // S^T accumulators: lane holds keys 16*nt + 4*jg + i of head-row ma
   float rkl[4][4];
 #pragma unroll
@@ -430,11 +434,9 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rkl[nt][i] = rk[16 * nt + 4 * jg + i];
 
-  bf16x8 qa[KSTEP], qn[KSTEP];
-  if (w < n_tiles) load_q_tile<D, G>(a, qoff_s, n_pairs, w, ma, jg, qa);
   for (int tile = w; tile < n_tiles; tile += 4) {
-    // prefetch the next tile's queries while this one computes
-    if (tile + 4 < n_tiles) load_q_tile<D, G>(a, qoff_s, n_pairs, tile + 4, ma, jg, qn);
+    // queries two tiles ahead in flight while this one computes
+    if (tile + 8 < n_tiles) load_q_tile<D, G>(a, qoff_s, n_pairs, tile + 8, ma, jg, qn2);
     float qss = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) qss = sumsq8(__builtin_bit_cast(uint4, qa[t]), qss);
@@ -505,7 +507,10 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
       if (nt % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // two output tiles in flight
     }
 #pragma unroll
-    for (int t = 0; t < KSTEP; ++t) qa[t] = qn[t];
+    for (int t = 0; t < KSTEP; ++t) {
+      qa[t] = qn[t];
+      qn[t] = qn2[t];
+    }
   }
 }
 
