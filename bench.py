@@ -659,16 +659,23 @@ def oracle_baseline(cfg, inp, budget_s=20.0):
 
 def pmc_mean_kib(csv_path, counter, match):
     """Mean per-dispatch value of `counter` over dispatches whose kernel name
-    contains `match`, from a rocprofv3 --pmc counter_collection.csv."""
+    contains `match`, from a rocprofv3 --pmc counter_collection.csv.  The
+    dispatches must share one grid size: a run over several workloads that use
+    the same kernel (different grids) would be averaged across them, so it is
+    refused (profile such workloads in runs of their own)."""
     import csv
-    vals = {}
+    vals, grids = {}, set()
     with open(csv_path, newline="") as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") == counter and match in row.get("Kernel_Name", ""):
                 d = row.get("Dispatch_Id") or row.get("Correlation_Id")
                 vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
+                grids.add(row.get("Grid_Size"))
     if not vals:
         raise SystemExit("no %s dispatch of a kernel matching %r in %s" % (counter, match, csv_path))
+    if len(grids) > 1:
+        raise SystemExit("dispatches of %r in %s have several grid sizes %s: one workload per counter run"
+                         % (match, csv_path, sorted(grids)))
     return float(np.mean(list(vals.values()))), len(vals)
 
 
@@ -706,15 +713,20 @@ def pmc_summary(fetch_csv, write_csv, workload, kernel, command):
 
 def pmc_dispatch_values(csv_path, counter, match):
     """Per-dispatch values of `counter` for kernels whose name contains `match`,
-    with each dispatch's duration in microseconds."""
+    with each dispatch's duration in microseconds (one grid size required, as
+    in pmc_mean_kib)."""
     import csv
-    vals, dur = {}, {}
+    vals, dur, grids = {}, {}, set()
     with open(csv_path, newline="") as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") == counter and match in row.get("Kernel_Name", ""):
                 d = row.get("Dispatch_Id") or row.get("Correlation_Id")
                 vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
                 dur[d] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                grids.add(row.get("Grid_Size"))
+    if len(grids) > 1:
+        raise SystemExit("dispatches of %r in %s have several grid sizes %s: one workload per counter run"
+                         % (match, csv_path, sorted(grids)))
     return vals, dur
 
 
