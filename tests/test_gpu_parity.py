@@ -616,6 +616,16 @@ def test_global_hsa_small_groups_appended_rows(hsa, G, Hkv):
     global_parity(hsa, W.generate(cfg), K=100, rows=sample_rows(cfg, 240, seed=G))
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_global_hsa_without_qk_norm(hsa, d):
+    """Without query-key normalisation the global kernel stages the keys as
+    given (no normalisation pass) and subtracts each chunk's maximum logit
+    (the logits are then unbounded); appended rows, two kv heads."""
+    cfg = small(n_q_heads=8, n_kv_heads=2, head_dim=d, q_len=1500, q_pos0=500, kv_len=2000, top_k=8,
+                qk_norm=False, seed=70 + d)
+    global_parity(hsa, W.generate(cfg), K=100, rows=sample_rows(cfg, 240, seed=d))
+
+
 def test_global_hsa_uniform_scores_equal_chunk_mean(hsa):
     """q_ret = 0: every score equal, so the output is the mean of the per-chunk
     attentions (the pages' K >= #chunks invariant), through the dense path."""
