@@ -95,3 +95,20 @@ def test_mfma_summary_busy_fraction(tmp_path):
     assert float(vals["mfma_busy_percent"]) == pytest.approx(25.0)
     assert float(vals["mfma_bf16_flop_per_dispatch"]) == pytest.approx(512e9)
     assert float(vals["mfma_bf16_tflops_counted"]) == pytest.approx(512e9 / 1e-3 / 1e12)
+
+
+def test_counter_summary_refuses_a_run_mixing_workloads(tmp_path):
+    """Two workloads that share a kernel (different grid sizes) in one counter
+    run would be averaged together: the summary refuses such a CSV."""
+    path = tmp_path / "f.csv"
+    name = "void hsa::(anonymous namespace)::chunk_attend_kernel<128, 8>(hsa::ChunkArgs)"
+    with open(path, "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value",
+                     "Start_Timestamp", "End_Timestamp"])
+        wr.writerow([1, 1310720, name, "FETCH_SIZE", 100.0, 0, 10])
+        wr.writerow([2, 21102592, name, "FETCH_SIZE", 900.0, 0, 10])
+    with pytest.raises(SystemExit, match="grid sizes"):
+        bench.pmc_mean_kib(str(path), "FETCH_SIZE", "chunk_attend_kernel")
+    with pytest.raises(SystemExit, match="grid sizes"):
+        bench.pmc_dispatch_values(str(path), "FETCH_SIZE", "chunk_attend_kernel")
