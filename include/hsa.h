@@ -89,7 +89,7 @@ typedef struct {
   int32_t n_q_heads;   /* Hq */
   int32_t n_kv_heads;  /* Hkv; G = Hq/Hkv must be 1, 2, 4, 8 or 16 */
   int32_t head_dim;    /* d: 64 or 128 */
-  int32_t top_k;       /* K: 1 .. 64 */
+  int32_t top_k;       /* K: 1 .. 64; larger only as described at hsa_forward and hsa_backward */
   float ret_scale;     /* Step 2 scale; <= 0 means 1/sqrt(d) */
   float attn_scale;    /* Step 3 scale; <= 0 means 1/sqrt(d) */
   uint32_t flags;      /* HSA_FLAG_* */
@@ -126,7 +126,14 @@ hsa_status_t hsa_chunk_attend_blend(const hsa_shape_t* shape, const void* q_attn
                                     void* stream);
 
 /* Steps 1-4.  topk_idx / topk_score may be NULL (the selection then stays in
- * the workspace) or receive the selection as hsa_retrieve_topk writes it. */
+ * the workspace) or receive the selection as hsa_retrieve_topk writes it.
+ * A top_k above 64 is accepted when it covers every row's eligible chunks
+ * (top_k >= min(floor((q_pos0 + Lq - 1)/64), Nc)): every eligible chunk is
+ * then selected, the warm-up stage's global HSA ("Every Token Counts",
+ * agent-atlas explainer, "Build Your Own" step 5).  bf16 only, and
+ * topk_idx / topk_score must be NULL (HSA_ERR_UNSUPPORTED otherwise); with
+ * HSA_FLAG_QK_L2NORM its workspace also holds the normalised keys of the
+ * complete chunks (B * Hkv * Nc * 64 * d * 2 bytes). */
 hsa_status_t hsa_forward(const hsa_shape_t* shape, const void* q_ret, const void* landmarks,
                          const void* q_attn, const void* k, const void* v, void* out,
                          int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
