@@ -6,7 +6,9 @@
 // the append completed get their landmark.
 //
 // One wave per chunk: every lane issues all of its 16-byte loads of the
-// chunk's keys at once (the chunk is one contiguous 64 x d block), adds its
+// chunk's keys at once (the chunk is one contiguous 64 x d block; streaming
+// loads, since every key is read once: 6.26 against 5.9 TB/s with cached
+// loads over the 16M history), adds its
 // rows in fp32, the lanes holding the same columns are combined with xor
 // shuffles, and the lanes of the first row store the mean in the input dtype.
 // HBM-bound: 64 * d * e bytes read and d * e written per chunk.
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(256) void chunk_landmark_kernel(LandmarkArgs a) {
   for (int i0 = 0; i0 < ITER; i0 += BATCH) {
     uint4 x[BATCH];
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) x[i] = *reinterpret_cast<const uint4*>(base + (r0 + RPI * (i0 + i)) * D);
+    for (int i = 0; i < BATCH; ++i) x[i] = load_stream(reinterpret_cast<const uint4*>(base + (r0 + RPI * (i0 + i)) * D));
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       const uint32_t wd[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
