@@ -107,11 +107,16 @@ __global__ __launch_bounds__(256) void chunk_scatter_pairs_kernel(ChunkArgs a) {
 }
 
 // --- bucketing through a workgroup histogram in LDS --------------------------
-// A workgroup takes kBucketRows query rows of one (batch, kv head), counts its
+// A workgroup takes bucket_rows query rows of one (batch, kv head), counts its
 // pairs per chunk in LDS and adds each nonzero count to the global bin once, so
 // global atomics drop from one per pair to one per (workgroup, chunk).  Used
-// when the chunks of one (batch, kv head) fit the LDS histogram.
+// when the chunks of one (batch, kv head) fit the LDS histogram.  bucket_rows
+// is kBucketRows, halved (down to kBucketRowsMin) while the grid would have
+// fewer than kBucketGrid workgroups: each workgroup's passes are a chain of
+// dependent loads, so a small grid leaves the chip idle.
 constexpr int kBucketRows = 1024;
+constexpr int kBucketRowsMin = 64;
+constexpr int kBucketGrid = 512;
 constexpr int kBandRows = 16384;         // forward bins; a multiple of kBucketRows
 constexpr int kHistMax = 16384;
 constexpr int kBucketBatch = 4;          // row passes whose loads are issued together
@@ -122,10 +127,10 @@ struct BucketRange {
 };
 __device__ __forceinline__ BucketRange bucket_range(const ChunkArgs& a) {
   BucketRange br;
-  const int64_t rbk = (a.Lq + kBucketRows - 1) / kBucketRows;
+  const int64_t rbk = (a.Lq + a.bucket_rows - 1) / a.bucket_rows;
   br.bg = (int64_t)blockIdx.x / rbk;
-  br.r0 = ((int64_t)blockIdx.x % rbk) * kBucketRows;
-  br.r1 = min(br.r0 + kBucketRows, a.Lq);
+  br.r0 = ((int64_t)blockIdx.x % rbk) * a.bucket_rows;
+  br.r1 = min(br.r0 + a.bucket_rows, a.Lq);
   br.b = (int)(br.bg / a.Hkv);
   br.g = (int)(br.bg % a.Hkv);
   return br;
@@ -197,11 +202,14 @@ __global__ __launch_bounds__(256) void chunk_scatter_lds_kernel(ChunkArgs a) {
 }
 
 // --- scan: bin offsets, scatter cursors, work items ------------------------
-// Two kernels over segments of Nc bins (one segment per (batch, kv head,
-// band)): the first scans each segment locally and records its totals; the
-// second adds the totals of all earlier segments, writes the bin offsets, the
-// scatter cursors and the work items, and clears the counts for the next call.
+// An exclusive scan of (pairs, items) over all bins in two kernels over tiles
+// of kScanTile bins (kScanPer consecutive bins per thread): the first records
+// each tile's totals; the second adds the totals of all earlier tiles, scans
+// its tile, writes the bin offsets, the scatter cursors and the work items,
+// and clears the counts for the next call.
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 2;
+constexpr int64_t kScanTile = (int64_t)kScanThreads * kScanPer;
 
 __device__ __forceinline__ void block_exclusive_scan2(uint32_t& a, uint32_t& b, uint32_t* sa, uint32_t* sb,
                                                       uint32_t& tot_a, uint32_t& tot_b) {
@@ -223,89 +231,83 @@ __device__ __forceinline__ void block_exclusive_scan2(uint32_t& a, uint32_t& b, 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kScanThreads) void chunk_seg_scan_kernel(ChunkArgs a) {
+__device__ __forceinline__ uint32_t items_of(uint32_t pairs, uint32_t ppi) { return (pairs + ppi - 1) / ppi; }
+
+__global__ __launch_bounds__(kScanThreads) void chunk_tile_sum_kernel(ChunkArgs a) {
   const uint32_t ppi = (uint32_t)a.pairs_per_item;
-  __shared__ uint32_t sp[kScanThreads], si[kScanThreads];
-  const int t = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * a.Nc, n = a.Nc;
-  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = min(n, t * per), hi = min(n, lo + per);
+  __shared__ uint32_t sp[kScanThreads / kWave], si[kScanThreads / kWave];
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  const int64_t i0 = (int64_t)blockIdx.x * kScanTile + (int64_t)t * kScanPer;
   uint32_t tp = 0, ti = 0;
-  for (int64_t i0 = lo; i0 < hi; i0 += 16) {
-    uint32_t c[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[base + i0 + u] : 0u;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      tp += c[u];
-      ti += (c[u] + ppi - 1) / ppi;
-    }
+  for (int u = 0; u < kScanPer; ++u) {
+    const uint32_t c = i0 + u < a.n_bins ? a.counts[i0 + u] : 0u;
+    tp += c;
+    ti += items_of(c, ppi);
   }
-  uint32_t rp = tp, ri = ti, tot_p, tot_i;
-  block_exclusive_scan2(rp, ri, sp, si, tot_p, tot_i);
-  // local prefixes: pairs into offsets, items into cursor (fixed up next)
-  for (int64_t i0 = lo; i0 < hi; i0 += 16) {
-    uint32_t c[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) c[u] = i0 + u < hi ? a.counts[base + i0 + u] : 0u;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (i0 + u < hi) {
-        a.offsets[base + i0 + u] = rp;
-        a.cursor[base + i0 + u] = ri;
-        rp += c[u];
-        ri += (c[u] + ppi - 1) / ppi;
-      }
-    }
+  for (int o = 32; o >= 1; o >>= 1) {
+    tp += __shfl_xor(tp, o, kWave);
+    ti += __shfl_xor(ti, o, kWave);
   }
+  if (lane == 0) {
+    sp[w] = tp;
+    si[w] = ti;
+  }
+  __syncthreads();
   if (t == 0) {
-    a.seg_tot[2 * blockIdx.x] = tot_p;
-    a.seg_tot[2 * blockIdx.x + 1] = tot_i;
+    uint32_t p = 0, it = 0;
+    for (int x = 0; x < kScanThreads / kWave; ++x) {
+      p += sp[x];
+      it += si[x];
+    }
+    a.seg_tot[2 * blockIdx.x] = p;
+    a.seg_tot[2 * blockIdx.x + 1] = it;
   }
 }
 
-__global__ __launch_bounds__(kScanThreads) void chunk_seg_fix_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kScanThreads) void chunk_tile_fix_kernel(ChunkArgs a) {
   const uint32_t ppi = (uint32_t)a.pairs_per_item;
   __shared__ uint32_t sp[kScanThreads], si[kScanThreads];
   const int t = threadIdx.x;
-  const int64_t seg = blockIdx.x;
-  uint32_t pb = 0, ib = 0;                       // totals of the earlier segments
-  for (int64_t s = t; s < seg; s += kScanThreads) {
-    pb += a.seg_tot[2 * s];
-    ib += a.seg_tot[2 * s + 1];
+  const int64_t tile = blockIdx.x;
+  uint32_t pb = 0, ib = 0;                       // totals of the earlier tiles
+  for (int64_t x = t; x < tile; x += kScanThreads) {
+    pb += a.seg_tot[2 * x];
+    ib += a.seg_tot[2 * x + 1];
   }
   uint32_t tot_p, tot_i;
   block_exclusive_scan2(pb, ib, sp, si, tot_p, tot_i);
-  pb = tot_p;
-  ib = tot_i;
-  const int64_t base = seg * a.Nc, n = a.Nc;
-  const int64_t per = (n + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = min(n, t * per), hi = min(n, lo + per);
-  for (int64_t i0 = lo; i0 < hi; i0 += 16) {
-    uint32_t c[16], lp[16], li[16];
+  const uint32_t base_p = tot_p, base_i = tot_i;
+  // this thread's bins, then the tile's exclusive scan over threads
+  const int64_t i0 = tile * kScanTile + (int64_t)t * kScanPer;
+  uint32_t c[kScanPer];
+  uint32_t lp = 0, li = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const bool in = i0 + u < hi;
-      c[u] = in ? a.counts[base + i0 + u] : 0u;
-      lp[u] = in ? a.offsets[base + i0 + u] : 0u;
-      li[u] = in ? a.cursor[base + i0 + u] : 0u;
-    }
+  for (int u = 0; u < kScanPer; ++u) {
+    c[u] = i0 + u < a.n_bins ? a.counts[i0 + u] : 0u;
+    lp += c[u];
+    li += items_of(c[u], ppi);
+  }
+  uint32_t tile_p, tile_i;
+  block_exclusive_scan2(lp, li, sp, si, tile_p, tile_i);
+  uint32_t op = base_p + lp, oi = base_i + li;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int64_t i = base + i0 + u;
-      if (i0 + u < hi) {
-        a.offsets[i] = pb + lp[u];
-        a.cursor[i] = pb + lp[u];
-        a.counts[i] = 0u;                        // ready for the next call
-        if (a.item_start != nullptr) a.item_start[i] = ib + li[u];
-        const uint32_t ni = (c[u] + ppi - 1) / ppi;
-        for (uint32_t jb = 0; jb < ni; ++jb) a.items[ib + li[u] + jb] = (uint64_t)i | ((uint64_t)jb << 32);
-      }
+  for (int u = 0; u < kScanPer; ++u) {
+    const int64_t i = i0 + u;
+    if (i < a.n_bins) {
+      a.offsets[i] = op;
+      a.cursor[i] = op;
+      a.counts[i] = 0u;                          // ready for the next call
+      if (a.item_start != nullptr) a.item_start[i] = oi;
+      const uint32_t ni = items_of(c[u], ppi);
+      for (uint32_t jb = 0; jb < ni; ++jb) a.items[oi + jb] = (uint64_t)i | ((uint64_t)jb << 32);
+      op += c[u];
+      oi += ni;
     }
   }
-  if (seg == (int64_t)gridDim.x - 1 && t == 0) {
-    a.offsets[a.n_bins] = pb + a.seg_tot[2 * seg];
-    *a.n_items = ib + a.seg_tot[2 * seg + 1];
+  if (tile == (int64_t)gridDim.x - 1 && t == 0) {
+    a.offsets[a.n_bins] = base_p + tile_p;
+    *a.n_items = base_i + tile_i;
   }
 }
 
@@ -576,8 +578,16 @@ hipError_t launch_dg(const ChunkArgs& a, hipStream_t st, const Marks& mk) {
 int64_t chunk_pairs_per_item() { return kFwdPairs; }
 int64_t chunk_band_rows() { return kBandRows; }
 
-hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st) {
+int64_t chunk_scan_tiles(int64_t n_bins) { return (n_bins + kScanTile - 1) / kScanTile; }
+
+hipError_t launch_bucket(const ChunkArgs& args, hipStream_t st) {
   hipError_t e;
+  ChunkArgs a = args;
+  const int64_t ranges = a.Lq > 0 ? a.rows / a.Lq : 0;   // (batch, kv head) pairs
+  a.bucket_rows = kBucketRows;
+  while (a.bucket_rows > kBucketRowsMin && (a.Lq + a.bucket_rows - 1) / a.bucket_rows * ranges < kBucketGrid)
+    a.bucket_rows /= 2;
+  if (a.band_rows % a.bucket_rows != 0) return hipErrorInvalidValue;   // a range lies in one band
   if ((e = launch_fill_u32(a.counts, a.n_bins, 0u, st)) != hipSuccess) return e;
   const bool wide = a.K > kWave;                 // more slots than lanes in a wave
   const bool lds = !wide && a.Nc <= kHistMax;
@@ -589,17 +599,18 @@ hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st) {
   // rows per 256-thread block of the one-lane-per-slot kernels (K <= 64 there)
   const int64_t seg = wide ? 64 : (a.K <= 1 ? 1 : (int64_t)1 << (32 - __builtin_clz((unsigned)a.K - 1)));
   const unsigned row_blocks = (unsigned)((a.rows + 256 / seg - 1) / (256 / seg));
-  const unsigned range_blocks = (unsigned)((a.Lq + kBucketRows - 1) / kBucketRows * (a.rows / a.Lq));
+  const unsigned range_blocks = (unsigned)((a.Lq + a.bucket_rows - 1) / a.bucket_rows * ranges);
   const size_t hist_bytes = (size_t)a.Nc * 4;
   if (wide) hipLaunchKernelGGL(chunk_count_pairs_kernel, dim3(pair_blocks), dim3(256), 0, st, a);
   else if (lds) hipLaunchKernelGGL(chunk_count_lds_kernel, dim3(range_blocks), dim3(256), hist_bytes, st, a);
   else hipLaunchKernelGGL(chunk_count_kernel, dim3(row_blocks), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned n_seg = (unsigned)(a.n_bins / (a.Nc > 0 ? a.Nc : 1));
-  if (n_seg > 0 && a.Nc > 0) {
-    hipLaunchKernelGGL(chunk_seg_scan_kernel, dim3(n_seg), dim3(kScanThreads), 0, st, a);
+  const int64_t n_tiles = chunk_scan_tiles(a.n_bins);
+  if (n_tiles > INT32_MAX) return hipErrorInvalidValue;
+  if (n_tiles > 0) {
+    hipLaunchKernelGGL(chunk_tile_sum_kernel, dim3((unsigned)n_tiles), dim3(kScanThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_seg_fix_kernel, dim3(n_seg), dim3(kScanThreads), 0, st, a);
+    hipLaunchKernelGGL(chunk_tile_fix_kernel, dim3((unsigned)n_tiles), dim3(kScanThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else if ((e = launch_fill_u32(a.n_items, 1, 0u, st)) != hipSuccess) {   // no bins: no work items
     return e;

@@ -115,7 +115,6 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
   constexpr int KROW = D + 16;              // K, V rows (bf16; 32-byte pad: no bank conflicts)
   constexpr int PT = 16 / G;                // pairs per 16-head-row tile
   constexpr int KSTEP = D / 32, NT = D / 16;
-  constexpr int HR = 32;                    // head-rows staged per phase B round (2 tiles)
   // about 67 KiB of LDS: two workgroups per CU.  ks holds the normalised keys
   // khat (k itself without query-key normalisation).
   __shared__ __align__(16) uint16_t ks[kChunk * KROW];
@@ -597,40 +596,45 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a, uint32_t n_attn)
   *reinterpret_cast<float4*>(a.dq_ret + row * D + x4) = acc;
 }
 
-// --- per chunk: dlandmark -------------------------------------------------------
-// D / 8 threads per pair, each owning 8 dims; 256 / (D / 8) groups take the
-// chunk's pairs round robin, then the groups' sums are added in group order.
+// --- dlandmark ------------------------------------------------------------------
+// dlandmarks = sum over the pairs that chose a chunk of draw(pair) * q_ret(row),
+// in two passes so that no workgroup walks the pairs of a whole chunk (early
+// chunks are chosen by many more rows than late ones).  First, per work item
+// (at most kBP pairs of one bin): each of NG lane groups adds its pairs in
+// order, then the groups are added in order; the item's D sums go to the first
+// D floats of its item_part slot, which bwd_chunk_kernel has finished reading.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_landmark_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_lm_item_kernel(BwdArgs a) {
   const ChunkArgs& c = a.c;
   constexpr int TPP = D / 8, NG = 256 / TPP;
   __shared__ float red[NG][D + 4];
-  const int64_t bg = blockIdx.x / c.Nc, chunk = blockIdx.x % c.Nc;
+  const uint32_t item_i = blockIdx.x;
+  if (item_i >= *c.n_items) return;
+  const uint64_t item = c.items[item_i];
+  const int64_t bin = (int64_t)(item & 0xFFFFFFFFull);
+  const uint32_t p0 = c.offsets[bin] + (uint32_t)(item >> 32) * kBP;
+  const uint32_t p1 = min(p0 + (uint32_t)kBP, c.offsets[bin + 1]);
   const int tid = threadIdx.x, grp = tid / TPP, x8 = 8 * (tid % TPP);
   const uint16_t* qr = reinterpret_cast<const uint16_t*>(a.q_ret) + x8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t band = 0; band < c.n_bands; ++band) {
-    const int64_t bin = (bg * c.n_bands + band) * c.Nc + chunk;
-    const uint32_t p0 = c.offsets[bin], p1 = c.offsets[bin + 1];
-    for (uint32_t p = p0 + grp; p < p1; p += 4 * NG) {   // four pairs in flight, in order
-      uint32_t pid[4];
-      float dr[4];
-      uint4 q[4];
+  for (uint32_t p = p0 + grp; p < p1; p += 4 * NG) {   // four pairs in flight, in order
+    uint32_t pid[4];
+    float dr[4];
+    uint4 q[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pid[u] = c.pairs[min(p + u * NG, p1 - 1)];
+    for (int u = 0; u < 4; ++u) pid[u] = c.pairs[min(p + u * NG, p1 - 1)];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        dr[u] = p + u * NG < p1 ? a.draw[pid[u]] : 0.f;
-        q[u] = *reinterpret_cast<const uint4*>(qr + (int64_t)(pid[u] / (uint32_t)c.K) * D);
-      }
+    for (int u = 0; u < 4; ++u) {
+      dr[u] = p + u * NG < p1 ? a.draw[pid[u]] : 0.f;
+      q[u] = *reinterpret_cast<const uint4*>(qr + (int64_t)(pid[u] / (uint32_t)c.K) * D);
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t wq[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t wq[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += dr[u] * __uint_as_float(wq[e] << 16);
-          acc[2 * e + 1] += dr[u] * __uint_as_float(wq[e] & 0xFFFF0000u);
-        }
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += dr[u] * __uint_as_float(wq[e] << 16);
+        acc[2 * e + 1] += dr[u] * __uint_as_float(wq[e] & 0xFFFF0000u);
       }
     }
   }
@@ -638,10 +642,34 @@ __global__ __launch_bounds__(256) void bwd_landmark_kernel(BwdArgs a) {
   for (int x = 0; x < 8; ++x) red[grp][x8 + x] = acc[x];
   __syncthreads();
   if (tid < D) {
-    float s = 0.f;
-    for (int gi = 0; gi < NG; ++gi) s += red[gi][tid];
-    a.dlandmarks[(bg * c.Nc + chunk) * D + tid] = s;
+    float sum = 0.f;
+    for (int gi = 0; gi < NG; ++gi) sum += red[gi][tid];
+    a.item_part[(int64_t)item_i * 2 * kChunk * D + tid] = sum;
   }
+}
+
+// Second pass: per (batch, kv head, chunk), the item sums of the chunk's bins
+// (band by band, item by item) added in that order; thread t owns dim t.
+template <int D>
+__global__ __launch_bounds__(D) void bwd_landmark_kernel(BwdArgs a) {
+  const ChunkArgs& c = a.c;
+  const int64_t bg = blockIdx.x / c.Nc, chunk = blockIdx.x % c.Nc;
+  const int x = threadIdx.x;
+  float sum = 0.f;
+  for (int64_t band = 0; band < c.n_bands; ++band) {
+    const int64_t bin = (bg * c.n_bands + band) * c.Nc + chunk;
+    const uint32_t n = c.offsets[bin + 1] - c.offsets[bin];
+    const uint32_t i0 = c.item_start[bin], i1 = i0 + (n + kBP - 1) / kBP;
+    for (uint32_t it = i0; it < i1; it += 4) {     // 4 items in flight, added in item order
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = a.item_part[(int64_t)min(it + u, i1 - 1) * 2 * kChunk * D + x];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (it + u < i1) sum += v[u];
+    }
+  }
+  a.dlandmarks[(bg * c.Nc + chunk) * D + x] = sum;
 }
 
 }  // namespace
@@ -681,7 +709,12 @@ hipError_t launch_bwd_dg(const BwdArgs& a, hipStream_t st, const Marks& mk) {
     constexpr int64_t BPC = kChunk / (256 / (D / 4));
     hipLaunchKernelGGL((bwd_chunk_kernel<D>), dim3((unsigned)(n_bg * a.c.Nc * BPC)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_landmark_kernel<D>), dim3((unsigned)(n_bg * a.c.Nc)), dim3(256), 0, st, a);
+    // after bwd_chunk_kernel: the landmark item sums reuse the item partials' memory
+    if (a.c.max_items > 0) {
+      hipLaunchKernelGGL((bwd_lm_item_kernel<D>), dim3((unsigned)a.c.max_items), dim3(256), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_landmark_kernel<D>), dim3((unsigned)(n_bg * a.c.Nc)), dim3(D), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.c.Lkv > a.c.Nc * kChunk) {

@@ -177,7 +177,7 @@ hsa_status_t make_plan(const hsa_shape_t* s, Plan* p, bool check_positions, bool
     p->off_ccursor = off; off = align_up(off + nb * 4, 256);
     p->off_citems = off; off = align_up(off + (size_t)p->max_items * 8, 256);
     p->off_cnitems = off; off = align_up(off + 4, 256);
-    p->off_cseg = off; off = align_up(off + (Nc > 0 ? nb / (size_t)Nc : 0) * 8, 256);
+    p->off_cseg = off; off = align_up(off + (size_t)chunk_scan_tiles(p->n_bins) * 8, 256);
     p->off_cpairs = off; off = align_up(off + np * 4, 256);
     p->off_cwts = off; off = align_up(off + np * 4, 256);
     p->off_cparts = off; off = align_up(off + np * G * p->D * 2, 256);
@@ -465,7 +465,7 @@ hsa_status_t make_bwd_plan(const hsa_shape_t* s, BwdPlan* b) {
   b->off_cursor = off; off = align_up(off + nb * 4, 256);
   b->off_items = off; off = align_up(off + (size_t)p.max_items * 8, 256);
   b->off_nitems = off; off = align_up(off + 4, 256);
-  b->off_seg = off; off = align_up(off + (p.Nc > 0 ? nb / (size_t)p.Nc : 0) * 8, 256);
+  b->off_seg = off; off = align_up(off + (size_t)chunk_scan_tiles(p.n_bins) * 8, 256);
   b->off_istart = off; off = align_up(off + nb * 4, 256);
   b->off_pairs = off; off = align_up(off + np * 4, 256);
   b->off_wts = off; off = align_up(off + np * 4, 256);
@@ -629,8 +629,9 @@ HSA_EXPORT hsa_status_t hsa_forward_noalloc(const hsa_shape_t* shape, const void
   if ((st = hsa::static_scratch(s, &ws)) != HSA_OK) return st;
   st = hsa::forward_impl(shape, q_ret, landmarks, q_attn, k, v, out, topk_idx, topk_score, ws,
                          hsa::kStaticScratchBytes, stream, hsa::Marks{});
-  if (st == HSA_ERR_DEVICE)   // a partly launched call may have left counters non-zero
-    hsa::launch_fill_u32(static_cast<uint32_t*>(ws), (int64_t)(hsa::kCounterBytes / 4), 0u, s);
+  if (st == HSA_ERR_DEVICE)   // a partly launched call may have left counters non-zero (best effort:
+                              // the call's own error is what is reported)
+    (void)hsa::launch_fill_u32(static_cast<uint32_t*>(ws), (int64_t)(hsa::kCounterBytes / 4), 0u, s);
   return st;
 }
 

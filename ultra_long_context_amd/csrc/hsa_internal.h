@@ -98,7 +98,7 @@ struct ChunkArgs {
   uint32_t* cursor;       // [n_bins]      scatter positions
   uint64_t* items;        // [max_items]   bin | block << 32
   uint32_t* n_items;      // number of valid items
-  uint32_t* seg_tot;      // [2 * n_bins / Nc] pairs and items per segment of Nc bins
+  uint32_t* seg_tot;      // [2 * chunk_scan_tiles(n_bins)] pairs and items per scan tile of bins
   uint32_t* item_start;   // [n_bins] first work item of each bin, or nullptr
   uint32_t* pairs;        // [rows * K]    pair ids (row * K + slot), grouped by bin
   float* wts;             // [rows * K]    blend weights
@@ -106,6 +106,7 @@ struct ChunkArgs {
   int64_t rows, Lq, Lkv, Nc, n_bins, max_items;
   int64_t band_rows, n_bands;   // bins split the query rows of a (batch, kv head) into bands
   int32_t pairs_per_item;       // work item size, at most 128 pairs
+  int32_t bucket_rows;          // query rows per bucketing workgroup (set by launch_bucket)
   int32_t Hq, Hkv, K;
   float attn_scale;
   int32_t qk_norm;
@@ -174,6 +175,7 @@ hipError_t launch_attend_chunk(const ChunkArgs& a, int D, int G, hipStream_t st,
 hipError_t launch_bucket(const ChunkArgs& a, hipStream_t st);
 int64_t chunk_pairs_per_item();   // forward work items of large problems (else 64)
 int64_t chunk_band_rows();        // forward bins
+int64_t chunk_scan_tiles(int64_t n_bins);   // tiles of the bin scan (entries of seg_tot / 2)
 int64_t bwd_band_rows();          // backward bins (each bin sortable in LDS)
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 
