@@ -176,6 +176,18 @@ def test_chunked_prefill_shape_cut(hsa):
     parity(hsa, inp, rows=sample_rows(cfg, 300))
 
 
+@pytest.mark.parametrize("Hkv,Nc", [(1, 2047), (1, 2049), (2, 1025)])
+def test_bin_scan_tile_edges(hsa, Hkv, Nc):
+    """The many-row path's bin offsets and work items come from a scan over
+    tiles of 2,048 (batch, kv head, band, chunk) bins: bin counts just below and
+    past a tile, and a tile that holds the end of one kv head's bins and the
+    start of the next."""
+    L = Nc * 64
+    cfg = small(q_len=1024, kv_len=L, q_pos0=L - 1024, n_q_heads=8 * Hkv, n_kv_heads=Hkv)
+    inp = W.generate(cfg)
+    parity(hsa, inp, rows=sample_rows(cfg, 300))
+
+
 # ----------------------------------------------------------------------------
 # edge cases
 # ----------------------------------------------------------------------------

@@ -608,8 +608,10 @@ hipError_t launch_bucket(const ChunkArgs& args, hipStream_t st) {
   const int64_t n_tiles = chunk_scan_tiles(a.n_bins);
   if (n_tiles > INT32_MAX) return hipErrorInvalidValue;
   if (n_tiles > 0) {
-    hipLaunchKernelGGL(chunk_tile_sum_kernel, dim3((unsigned)n_tiles), dim3(kScanThreads), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (n_tiles > 1) {   // one tile has no earlier tiles whose totals it needs
+      hipLaunchKernelGGL(chunk_tile_sum_kernel, dim3((unsigned)n_tiles), dim3(kScanThreads), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(chunk_tile_fix_kernel, dim3((unsigned)n_tiles), dim3(kScanThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else if ((e = launch_fill_u32(a.n_items, 1, 0u, st)) != hipSuccess) {   // no bins: no work items
