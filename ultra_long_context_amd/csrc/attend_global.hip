@@ -65,9 +65,10 @@ __global__ __launch_bounds__(256) void key_norm_kernel(GlobalArgs a, int64_t n_p
 
 // TW: 16-head-row tiles per wave.  The workgroup always holds 256 head-rows
 // (16 / TW waves); with TW = 2 every K and V^T operand read from LDS feeds two
-// MFMAs, halving the LDS operand traffic per chunk.  Measured on the 32K
-// window (G = 8): TW = 2 2.90 ms against TW = 1 2.72 ms (the loop is bound by
-// instruction issue, not by LDS operand reads), so the launches use TW = 1.
+// MFMAs, halving the LDS operand traffic per chunk, but leaves two waves per
+// SIMD instead of four.  Measured on the 32K window (G = 8): TW = 2 2.28 ms
+// against TW = 1 2.22 ms (d = 64: 0.44 against 0.40 ms), so the launches use
+// TW = 1.
 template <int D, int G, int TW>
 __global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs a) {
   constexpr int NW = 16 / TW;                  // waves per workgroup
