@@ -712,7 +712,7 @@ __device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // one from the reads of the other): tile t + 1 streams into the idle buffer
 // while tile t is scored.  fn(sub-tile scores, sub-tile, first chunk, whole
 // sub-tile eligible for every row of the wave).
-template <int D, int TILE, bool kUnrollSub, class F>
+template <int D, int TILE, class F>
 __device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int n_tiles, int w_stop,
                                             int w_min, uint16_t* lmA, uint16_t* lmB,
                                             const QOperand<true, D>& q, int w, int lane, int qrow, int j,
@@ -734,18 +734,14 @@ __device__ __forceinline__ void block_sweep(const uint16_t* lm, int c_stop, int 
       }
       fn(acc, vbase + sub, cs, cs + 16 <= w_min);
     };
-    if constexpr (kUnrollSub) {          // fn indexes registers by sub-tile
+    // unrolled: fn indexes registers by sub-tile, and the sub-tiles' load ->
+    // MFMA -> compare chains overlap (a rolled loop that kept one copy of pass
+    // 2's step ran each chain in turn: the 1M chunked prefill's scan 0.75
+    // against 0.69 ms)
 #pragma unroll
-      for (int sub = 0; sub < TILE / 16; ++sub) {
-        if (t * TILE + 16 * sub >= w_stop) break;
-        sub_tile(sub);
-      }
-    } else {                             // fn is large: one copy of it
-#pragma unroll 1
-      for (int sub = 0; sub < TILE / 16; ++sub) {
-        if (t * TILE + 16 * sub >= w_stop) break;
-        sub_tile(sub);
-      }
+    for (int sub = 0; sub < TILE / 16; ++sub) {
+      if (t * TILE + 16 * sub >= w_stop) break;
+      sub_tile(sub);
     }
   };
   tile_to_lds<D, TILE>(lm, 0, c_stop, lmA, w, lane);
@@ -800,21 +796,24 @@ __global__ __launch_bounds__(256, TILE == 32 ? 3 : 2) void scan_block_kernel(Sca
   const int n_tiles = (c_stop + TILE - 1) / TILE;
   const int K = a.K;
 
-  auto sweep1 = [&](auto&& fn) __attribute__((always_inline)) {
-    block_sweep<D, TILE, true>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
-  };
-  auto sweep2 = [&](auto&& fn) __attribute__((always_inline)) {
-    block_sweep<D, TILE, false>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
+  auto sweep = [&](auto&& fn) __attribute__((always_inline)) {
+    block_sweep<D, TILE>(lm, c_stop, n_tiles, w_stop, w_min, lmA, lmB, q, wu, lane, qrow, j, fn);
   };
 
   // --- pass 1: group maxima, then a lower bound of each row's K-th key -------
   float gm[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) gm[x] = -INFINITY;
-  sweep1([&](const floatx4& acc, int sub, int cs, bool all) __attribute__((always_inline)) {
+  sweep([&](const floatx4& acc, int sub, int cs, bool all) __attribute__((always_inline)) {
+    floatx4 v = acc;
+    if (!all) {                         // a sub-tile past some row's last eligible chunk
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (all || cs + 4 * j + i < lim) gm[4 * sub + i] = fmaxf(gm[4 * sub + i], acc[i]);
+      for (int i = 0; i < 4; ++i)
+        if (cs + 4 * j + i >= lim) v[i] = -INFINITY;
+    }
+    // max(a, b) as the median of (a, b, +inf): one instruction, scores are finite
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gm[4 * sub + i] = __builtin_amdgcn_fmed3f(gm[4 * sub + i], v[i], INFINITY);
   });
   uint32_t t16 = 0;
   {
@@ -843,8 +842,24 @@ __global__ __launch_bounds__(256, TILE == 32 ? 3 : 2) void scan_block_kernel(Sca
 #pragma unroll
   for (int s = 0; s < 16; ++s) qrowbuf[jq + 4 * s] = kEmpty;
   int m = 0, cj = 0;     // kept entries of the row; this lane's appends after them
-  sweep2([&](const floatx4& acc, int sub, int cs, bool all) __attribute__((always_inline)) {
-    if (__any(m + j + 4 * cj + 12 >= kBlkCap)) {
+  sweep([&](const floatx4& acc, int sub, int cs, bool all) __attribute__((always_inline)) {
+    // this lane's eligible scores at or above the bound, as a 4-bit mask; the
+    // rest of the step runs only when some lane of the wave has one
+    unsigned vm = 0xFu;
+    if (!all) {
+      vm = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vm |= (unsigned)(cs + 4 * j + i < lim) << i;
+    }
+    auto reach = [&]() __attribute__((always_inline)) {
+      unsigned qm = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qm |= (unsigned)(acc[i] >= lo) << i;
+      return qm & vm;
+    };
+    unsigned qm = reach();
+    if (!__any(qm != 0u)) return;
+    if (__any(m + j + 4 * cj + 12 >= kBlkCap)) {   // room for four more appends per lane
       uint64_t kth;
       const int mq = block_cut(qrowbuf, K, jq, kth, false);
       // later chunks lose ties with the row's K-th: the bound becomes strict
@@ -852,12 +867,12 @@ __global__ __launch_bounds__(256, TILE == 32 ? 3 : 2) void scan_block_kernel(Sca
       m = __shfl(mq, 4 * qrow, kWave);
       lo = fmaxf(lo, __shfl(loq, 4 * qrow, kWave));
       cj = 0;
+      qm = reach();
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = cs + 4 * j + i;
-      if ((all || c < lim) && acc[i] >= lo) {
-        mrowbuf[m + j + 4 * cj] = make_slot(acc[i], (uint32_t)c);
+      if ((qm >> i) & 1u) {
+        mrowbuf[m + j + 4 * cj] = make_slot(acc[i], (uint32_t)(cs + 4 * j + i));
         ++cj;
       }
     }
