@@ -442,8 +442,7 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
     float qss = 0.f;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t) qss = sumsq8(__builtin_bit_cast(uint4, qa[t]), qss);
-    qss += __shfl_xor(qss, 16, kWave);
-    qss += __shfl_xor(qss, 32, kWave);
+    qss = xrow_sum(qss);
     const float rq = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
     // S^T = K Q^T on MFMA: A = keys from LDS, B = the tile's queries
     floatx4 s[4];
@@ -467,8 +466,7 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
         s[nt][i] = s[nt][i] * rq * rkl[nt][i];
         mx = fmaxf(mx, s[nt][i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = xrow_max(mx);
     float sum = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -477,8 +475,7 @@ __global__ __launch_bounds__(256, 4) void chunk_attend_kernel(ChunkArgs a) {
         s[nt][i] = __builtin_amdgcn_exp2f(s[nt][i] - mx);   // logits are in base 2
         sum += s[nt][i];
       }
-    sum += __shfl_xor(sum, 16, kWave);
-    sum += __shfl_xor(sum, 32, kWave);
+    sum = xrow_sum(sum);
     const int pm = tile * PT + ma / G;
     const float scale = (pm < n_pairs ? w_s[pm] : 0.f) * __builtin_amdgcn_rcpf(sum);
     // P^T as the B operand of O^T = V^T P^T: step st takes keys of nt = 2st, 2st + 1

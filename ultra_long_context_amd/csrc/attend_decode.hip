@@ -414,12 +414,10 @@ __global__ __launch_bounds__(kThreads) void attend_decode_kernel(DecodeArgs a) {
         }
       }
     }
-    qss += __shfl_xor(qss, 16, kWave);
-    qss += __shfl_xor(qss, 32, kWave);
+    qss = xrow_sum(qss);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      kss[nt] += __shfl_xor(kss[nt], 16, kWave);
-      kss[nt] += __shfl_xor(kss[nt], 32, kWave);
+      kss[nt] = xrow_sum(kss[nt]);
     }
     const float rq_mine = a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f;
     float rk[4];

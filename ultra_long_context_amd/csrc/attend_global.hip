@@ -128,8 +128,7 @@ __global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs 
         qss = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, qss, false);
       }
     }
-    qss += __shfl_xor(qss, 16, kWave);
-    qss += __shfl_xor(qss, 32, kWave);
+    qss = xrow_sum(qss);
     const float rq = (a.qk_norm ? 1.0f / fmaxf(sqrtf(qss), 1e-6f) : 1.0f) * a.attn_scale * kLog2eG;
 #pragma unroll
     for (int t = 0; t < KSTEP; ++t)
@@ -244,26 +243,29 @@ __global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs 
     float al[TW];
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      float mx = 0.f;
-      if (!bounded) {
-        mx = -INFINITY;
+      if (bounded) {                           // uniform branch: no maximum to subtract
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[u][nt][i] = __builtin_amdgcn_exp2f(s4[u][nt][i]);
+      } else {
+        float mx = -INFINITY;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s4[u][nt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = xrow_max(mx);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[u][nt][i] = __builtin_amdgcn_exp2f(s4[u][nt][i] - mx);
       }
       float sum = 0.f;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s4[u][nt][i] = __builtin_amdgcn_exp2f(s4[u][nt][i] - mx);
-          sum += s4[u][nt][i];
-        }
-      sum += __shfl_xor(sum, 16, kWave);
-      sum += __shfl_xor(sum, 32, kWave);
+        for (int i = 0; i < 4; ++i) sum += s4[u][nt][i];
+      sum = xrow_sum(sum);
       // --- online blend over chunks (Step 4) ---------------------------------
       const float sr = sc[rloc[u]][c % kGTile];
       float f = 0.f;                           // this chunk's factor on O_c

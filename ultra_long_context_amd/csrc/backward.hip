@@ -260,8 +260,7 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
         yr[t] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.dout) + off + 8 * jg + 32 * t);
       }
     }
-    qss += __shfl_xor(qss, 16, kWave);
-    qss += __shfl_xor(qss, 32, kWave);
+    qss = xrow_sum(qss);
     const float rq = c.qk_norm ? inv_norm(qss) : 1.0f;
     // S^T = khat Q^T and dP'^T = V dout^T: lane holds keys 16*nt + 4*jg + i of head-row ma
     floatx4 sv[4], dp[4];
@@ -286,8 +285,7 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[nt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = xrow_max(mx);
     const float mxs = mx * cs;
     float sum = 0.f, edp = 0.f;
 #pragma unroll
@@ -298,10 +296,8 @@ __global__ __launch_bounds__(256, 2) void bwd_item_kernel(BwdArgs a) {
         sum += sv[nt][i];
         edp = fmaf(sv[nt][i], dp[nt][i], edp);
       }
-    sum += __shfl_xor(sum, 16, kWave);
-    sum += __shfl_xor(sum, 32, kWave);
-    edp += __shfl_xor(edp, 16, kWave);
-    edp += __shfl_xor(edp, 32, kWave);
+    sum = xrow_sum(sum);
+    edp = xrow_sum(edp);
     const float inv = __builtin_amdgcn_rcpf(sum);
     const float pdp = edp * inv;                            // sum_j P dP' = dout . O
     {  // w dw of the pair: its G head-rows are lanes ma with equal ma / G

@@ -122,6 +122,25 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
          (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
+// Sum / maximum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48),
+// result in every lane, with gfx950's row-swap permutes: a VALU op per step
+// instead of an LDS crossbar round trip.  permlane16_swap(v, v) leaves rows
+// (0, 0, 2, 2) in its first result and (1, 1, 3, 3) in its second, so their
+// sum is v[l] + v[l ^ 16] in every lane; permlane32_swap(v, v) does the same
+// for the two halves (v[l] + v[l ^ 32]).  Each step adds the same two values
+// as x + shfl_xor(x, 16 or 32) does, so the results are identical.
+__device__ __forceinline__ float xrow_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float xrow_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 // number of lanes whose predicate holds
 __device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
