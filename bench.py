@@ -72,7 +72,7 @@ KERNELS = {
     ("decode_16M", "scan"): "scan_wide_kernel<true, 128>",
     ("decode_16M", "attend"): "attend_decode_kernel<128, 8>",
     ("decode_16M", "landmarks"): "chunk_landmark_kernel<true, 128>",
-    ("global_32K", "attend"): "attend_global_kernel<128, 8, 1>",
+    ("global_32K", "attend"): "attend_global_kernel<128, 8, 2>",
     ("chunked_1M", "scan"): "scan_block_kernel<128, 64>",
     ("chunked_1M", "bucket"): "chunk_count/scan/scatter kernels",
     ("chunked_1M", "attend"): "chunk_attend_kernel<128, 8>",

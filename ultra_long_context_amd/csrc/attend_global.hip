@@ -66,9 +66,11 @@ __global__ __launch_bounds__(256) void key_norm_kernel(GlobalArgs a, int64_t n_p
 // TW: 16-head-row tiles per wave.  The workgroup always holds 256 head-rows
 // (16 / TW waves); with TW = 2 every K and V^T operand read from LDS feeds two
 // MFMAs, halving the LDS operand traffic per chunk, but leaves two waves per
-// SIMD instead of four.  Measured on the 32K window (G = 8): TW = 2 2.28 ms
-// against TW = 1 2.22 ms (d = 64: 0.44 against 0.40 ms), so the launches use
-// TW = 1.
+// SIMD instead of four.  Measured on the 32K window (G = 8), with the row
+// reductions on the row-swap permutes: TW = 2 1.3-1.5 % faster than TW = 1 in
+// three interleaved rounds (2.35-2.38 against 2.39-2.41 ms per call); with the
+// LDS-shuffle reductions they were equal at d = 128, and at d = 64 TW = 2 ran
+// 0.44 against 0.40 ms.  So d = 128 launches TW = 2, d = 64 TW = 1.
 template <int D, int G, int TW>
 __global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs a) {
   constexpr int NW = 16 / TW;                  // waves per workgroup
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(64 * 16 / TW) void attend_global_kernel(GlobalArgs 
 int global_rows_per_block(int G) { return 256 / G; }
 
 // Tiles per wave (measured: see the kernel's comment).
-template <int D> constexpr int global_tw() { return 1; }
+template <int D> constexpr int global_tw() { return D == 128 ? 2 : 1; }
 
 hipError_t launch_attend_global(const GlobalArgs& a, int64_t B, int D, int G, hipStream_t st) {
   const int64_t R = 256 / G;
