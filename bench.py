@@ -855,11 +855,15 @@ def main():
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-workload kernel statistics of a rocprofv3 --kernel-trace CSV of a run "
                          "over --workloads")
+    ap.add_argument("--trace-gap", type=float, default=0.15,
+                    help="host gap (s) that separates workloads in --trace-summary (the crossover draws its "
+                         "inputs on the GPU: a run of it alone is one group at a gap of a few seconds)")
     args = ap.parse_args()
     if args.trace_summary:
-        order = ["decode_16M", "prefill_32K", "chunked_1M", "global_32K", "backward_32K", "prefill_128K"]
+        order = ["crossover", "decode_16M", "prefill_32K", "chunked_1M", "global_32K", "backward_32K",
+                 "prefill_128K"]
         wl = [w for w in order if w in args.workloads.split(",")]
-        sys.stdout.write(trace_summary(args.trace_summary, wl, args.command))
+        sys.stdout.write(trace_summary(args.trace_summary, wl, args.command, gap_s=args.trace_gap))
         return
     if args.mfma_summary:
         wl, stage = args.kernel_of.split(":")
