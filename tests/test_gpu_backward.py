@@ -201,6 +201,13 @@ def test_backward_without_complete_chunks(hsa):
         assert np.all(g == 0), name
 
 
+def test_backward_global_histogram_bucketing(hsa):
+    """A history of more than 16,384 chunks: the backward's bucketing counts
+    pairs with global atomics whose return values place them in their bins."""
+    full_parity(hsa, small(q_len=600, q_pos0=1048700, kv_len=1048700 + 600 + 37, n_q_heads=2, n_kv_heads=1,
+                           head_dim=64, top_k=8, n_needles=16))
+
+
 def test_backward_duplicate_slots(hsa):
     """A given selection may name one chunk in two slots of a row: two pairs,
     as in the oracle."""

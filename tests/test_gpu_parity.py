@@ -468,6 +468,16 @@ def test_chunk_major_attend_group_sizes(hsa, G, d):
     parity(hsa, W.generate(cfg), rows=sample_rows(cfg, 400))
 
 
+def test_chunk_major_global_histogram_bucketing(hsa):
+    """More than 16,384 chunks per kv head (past the LDS histogram): pairs are
+    counted into their bins with global atomics whose return values place them,
+    and the scatter adds each pair's rank to its bin's first slot.  Ragged
+    rows and history, two kv heads, needles for popular bins."""
+    cfg = small(batch=1, n_kv_heads=2, n_q_heads=16, q_len=1500, q_pos0=1048700, kv_len=1048700 + 1500 + 37,
+                top_k=16, n_needles=32)
+    parity(hsa, W.generate(cfg), rows=sample_rows(cfg, 300, seed=11))
+
+
 def test_chunk_major_given_selection_with_gaps(hsa):
     """hsa_chunk_attend_blend in the chunk-major mode with -1 and out-of-range slots."""
     import torch

@@ -42,6 +42,9 @@ __device__ __forceinline__ int64_t bin_of(int64_t row, int32_t c, const ChunkArg
 __device__ __forceinline__ int seg_lanes(int K) { return K <= 1 ? 1 : 1 << (32 - __clz(K - 1)); }
 
 // --- count: blend weights and pairs per bin (one lane per slot) ------------
+// The count's returning atomic gives each pair its place in its bin, kept in
+// the partial-output region (free until the attend writes it) so that the
+// scatter needs no atomics: place = the bin's first slot + that rank.
 __global__ __launch_bounds__(256) void chunk_count_kernel(ChunkArgs a) {
   const int K = a.K, S = seg_lanes(K);
   const int64_t row = (int64_t)blockIdx.x * (256 / S) + threadIdx.x / S;
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(256) void chunk_count_kernel(ChunkArgs a) {
   float den = ex;
   for (int o = 1; o < S; o <<= 1) den += __shfl_xor(den, o, kWave);
   if (active) a.wts[row * K + k] = valid ? ex / den : 0.f;
-  if (valid) atomicAdd(&a.counts[bin_of(row, c, a)], 1u);
+  if (valid) reinterpret_cast<uint32_t*>(a.partials)[row * K + k] = atomicAdd(&a.counts[bin_of(row, c, a)], 1u);
 }
 
 // --- more than 64 slots per row (a selection of every eligible chunk) ---------
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(256) void chunk_scatter_kernel(ChunkArgs a) {
   if (row >= a.rows || k >= K) return;
   const int32_t c = a.idx[row * K + k];
   if (c >= 0 && (int64_t)c < a.Nc) {
-    const uint32_t pos = atomicAdd(&a.cursor[bin_of(row, c, a)], 1u);
+    const uint32_t pos = a.cursor[bin_of(row, c, a)] + reinterpret_cast<const uint32_t*>(a.partials)[row * K + k];
     a.pairs[pos] = (uint32_t)(row * K + k);
   }
 }
@@ -588,6 +591,9 @@ hipError_t launch_bucket(const ChunkArgs& args, hipStream_t st) {
   if ((e = launch_fill_u32(a.counts, a.n_bins, 0u, st)) != hipSuccess) return e;
   const bool wide = a.K > kWave;                 // more slots than lanes in a wave
   const bool lds = !wide && a.Nc <= kHistMax;
+  // the global-histogram count keeps each pair's rank in its bin in the
+  // partial-output region (4 bytes per pair) until the scatter reads it
+  if (!wide && !lds && a.partials == nullptr) return hipErrorInvalidValue;
   const unsigned pair_blocks = (unsigned)((a.rows * a.K + 255) / 256);
   if (wide) {
     hipLaunchKernelGGL(chunk_wts_wide_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);

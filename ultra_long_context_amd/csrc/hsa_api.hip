@@ -527,7 +527,9 @@ hsa_status_t backward_impl(const hsa_shape_t* shape, const void* q_ret, const vo
   c.item_start = reinterpret_cast<uint32_t*>(w + b.off_istart);
   c.pairs = reinterpret_cast<uint32_t*>(w + b.off_pairs);
   c.wts = reinterpret_cast<float*>(w + b.off_wts);
-  c.partials = nullptr;
+  // bucketing scratch (each pair's rank in its bin, 4 bytes per pair): the dq^
+  // partial region, which the item kernel only writes after the bucketing
+  c.partials = reinterpret_cast<uint16_t*>(w + b.off_dqp);
   c.rows = p.rows; c.Lq = p.Lq; c.Lkv = p.Lkv; c.Nc = p.Nc; c.n_bins = p.n_bins;
   c.max_items = p.max_items; c.Hq = p.Hq; c.Hkv = p.Hkv; c.K = p.K;
   c.band_rows = hsa::bwd_band_rows(); c.n_bands = p.n_bands;
