@@ -411,25 +411,6 @@ __device__ __forceinline__ void collect_quarter(const uint32_t (&v)[4], ChunkOf 
   rc.n = off;
 }
 
-// Rank of e among the values v of the first n lanes (n wave-uniform): the
-// number of them above e.  Each value reaches every lane as a scalar operand
-// (v_readlane), so the rank costs VALU issue instead of LDS broadcasts, which
-// the 16 waves of a workgroup ranking at once would otherwise queue on.
-__device__ __forceinline__ int lane_rank(uint64_t v, int n, uint64_t e) {
-  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
-  int rank = 0;
-  for (int i0 = 0; i0 < n; i0 += 4) {      // four independent compares per step
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u < n ? i0 + u : n - 1;
-      const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, i) << 32) |
-                         (uint32_t)__builtin_amdgcn_readlane(lo, i);
-      rank += (i0 + u < n && x > e) ? 1 : 0;
-    }
-  }
-  return rank;
-}
-
 // Exact top K of the row's candidates, sorted best first into L; returns m.
 __device__ __forceinline__ int finish_cands(RowCands& rc, uint64_t* T, uint64_t* L, int K, int lane) {
   const int n = filter_cands(T, rc.n, rc.tau, rc.thr, lane);
@@ -437,7 +418,7 @@ __device__ __forceinline__ int finish_cands(RowCands& rc, uint64_t* T, uint64_t*
     const uint64_t a = lane < n ? T[lane] : 0ull;
     const uint64_t b = lane + kWave < n ? T[lane + kWave] : 0ull;
     int ra = 0, rb = 0;
-    if (n <= kWave) ra = lane_rank(a, n, a);
+    if (n <= kWave) ra = lds_rank(T, n, a);
     else lds_rank2(T, n, a, b, ra, rb);
     if (lane < n && ra < K) L[ra] = a;
     if (lane + kWave < n && rb < K) L[rb] = b;
