@@ -8,10 +8,10 @@
 // weighted by softmax_c(s_c) over all of them (Step 4).  No top-K is needed;
 // the blend runs as an online softmax over the chunks:
 //   m' = max(m, s_c),  l' = l 2^(m-m') + 2^(s_c-m'),  acc' = acc 2^(m-m') + 2^(s_c-m') O_c,
-// out = acc / l (scores in base 2).  A workgroup of 16 waves owns 256/G
-// consecutive query rows of one (batch, kv head) (16 head-rows per wave: 16/G
-// rows of G heads) and
-// streams their eligible chunks: each chunk's K (normalised once per call by
+// out = acc / l (scores in base 2).  A workgroup owns 256/G consecutive query
+// rows of one (batch, kv head), 256 head-rows in tiles of 16 (16/G rows of G
+// heads), one tile per wave over 16 waves or two per wave over 8 (TW below),
+// and streams their eligible chunks: each chunk's K (normalised once per call by
 // key_norm_kernel when query-key normalisation is on) and V (row-major) are
 // staged in LDS once for all 256 head-rows, double-buffered so the next chunk's loads are
 // in flight during the current one; S^T = K Q^T and O^T += V^T P^T run on
