@@ -112,3 +112,40 @@ def test_counter_summary_refuses_a_run_mixing_workloads(tmp_path):
         bench.pmc_mean_kib(str(path), "FETCH_SIZE", "chunk_attend_kernel")
     with pytest.raises(SystemExit, match="grid sizes"):
         bench.pmc_dispatch_values(str(path), "FETCH_SIZE", "chunk_attend_kernel")
+
+
+def _trace_csv(path, spans):
+    """A rocprofv3 kernel-trace CSV with one row per (start_ns, end_ns, name, grid)."""
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Workgroup_Size_X",
+                    "Grid_Size_Y"])
+        for st, en, name, grid in spans:
+            w.writerow([name, st, en, grid, 256, 1])
+
+
+def test_trace_summary_groups_workloads_at_host_gaps(tmp_path):
+    """Dispatches separated by more than the gap form one workload each; the
+    groups before the named workloads are setup; kernels are keyed by name and
+    workgroup count."""
+    ms = 1_000_000
+    spans = [(0, 1 * ms, "void hsa::(anonymous namespace)::fill_u32_kernel(unsigned int*)", 256),
+             # workload A after a 1 s gap: two grid sizes of one kernel
+             (1000 * ms, 1002 * ms, "void hsa::(anonymous namespace)::chunk_attend_kernel<128, 8>(hsa::ChunkArgs)", 2560),
+             (1003 * ms, 1004 * ms, "void hsa::(anonymous namespace)::chunk_attend_kernel<128, 8>(hsa::ChunkArgs)", 5120),
+             # workload B after another 1 s gap
+             (2000 * ms, 2003 * ms, "void hsa::(anonymous namespace)::scan_wide_kernel<true, 128>(hsa::ScanArgs)", 65536),
+             (2003 * ms, 2004 * ms, "void hsa::(anonymous namespace)::scan_wide_kernel<true, 128>(hsa::ScanArgs)", 65536)]
+    p = tmp_path / "kt.csv"
+    _trace_csv(p, spans)
+    text = bench.trace_summary(str(p), ["A", "B"], "cmd")
+    sections = text.split("\n## ")[1:]
+    assert [s.splitlines()[0] for s in sections] == ["setup 0", "A", "B"]
+    a_rows = [l.split() for l in sections[1].splitlines()[2:]]
+    assert sorted((r[0] + r[1], int(r[2]), int(r[3])) for r in a_rows) == [
+        ("chunk_attend_kernel<128,8>", 10, 1), ("chunk_attend_kernel<128,8>", 20, 1)]
+    b_row = sections[2].splitlines()[2].split()
+    assert b_row[2] == "256" and b_row[3] == "2" and float(b_row[4]) == pytest.approx(2000.0)
+    # with a gap longer than both host gaps everything is one workload
+    one = bench.trace_summary(str(p), ["all"], "cmd", gap_s=5.0)
+    assert [s.splitlines()[0] for s in one.split("\n## ")[1:]] == ["all"]
